@@ -1,0 +1,249 @@
+"""CPU oracle for forward 2-D convolution -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library never imports, links
+or calls it, and it shares no code with the GPU path: the arithmetic lives in
+``oracle.c`` (plain C, fp64 / int64 loop nest, OpenMP over output planes),
+compiled on its own with gcc.  This module only marshals numpy arrays.
+
+What is computed and why is documented in ``oracle.c``: the plain
+cross-correlation of the naive loop nest in the blog post "卷积总结"
+(section "最原始的卷积实现"), generalised with batch, stride, zero padding,
+dilation and groups, plus the int8 requantisation reading
+``clamp(rne(fp32(acc) * scale[k]), -127, 127)``.
+
+Layouts: the oracle works on logical NCHW only.  Packing to and from NCHWx is
+plain numpy marshalling in ``cnn_convolution_fwd_amd/workloads.py``
+(pinned by ``tests/test_layout_np.py``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC",
+           "-shared", "-std=c99", "-Wall", "-Wextra", "-Werror"]
+
+def build(force: bool = False, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile ``oracle.c`` (or a copy of it) into a shared library with gcc."""
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(src):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, src, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
+
+
+def _pair(v):
+    if isinstance(v, (tuple, list)):
+        assert len(v) == 2
+        return int(v[0]), int(v[1])
+    return int(v), int(v)
+
+
+class Oracle:
+    """numpy front end over one build of ``oracle.c``."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        i32p = ctypes.POINTER(ctypes.c_int)
+        vp = ctypes.c_void_p
+        lib.oracle_output_size.argtypes = [ctypes.c_int] * 5
+        lib.oracle_output_size.restype = ctypes.c_int
+        lib.oracle_check.argtypes = [i32p]
+        lib.oracle_check.restype = ctypes.c_int
+        lib.oracle_max_threads.argtypes = []
+        lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_conv2d_f64.argtypes = [vp, vp, i32p, vp, vp]
+        lib.oracle_conv2d_f64.restype = ctypes.c_int
+        lib.oracle_conv2d_i8.argtypes = [vp, vp, i32p, vp]
+        lib.oracle_conv2d_i8.restype = ctypes.c_int
+        lib.oracle_requant_one.argtypes = [ctypes.c_int64, ctypes.c_float]
+        lib.oracle_requant_one.restype = ctypes.c_int8
+        lib.oracle_requant_i8.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_long, vp]
+        lib.oracle_requant_i8.restype = ctypes.c_int
+        lib.oracle_conv2d_f64_points.argtypes = [vp, vp, i32p, ctypes.c_long, vp, vp, vp]
+        lib.oracle_conv2d_f64_points.restype = ctypes.c_int
+        lib.oracle_conv2d_i8_points.argtypes = [vp, vp, i32p, ctypes.c_long, vp, vp]
+        lib.oracle_conv2d_i8_points.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def _params(self, x_shape, w_shape, stride, padding, dilation, groups):
+        N, C, H, W = (int(d) for d in x_shape)
+        K, Cg, R, S = (int(d) for d in w_shape)
+        sh, sw = _pair(stride)
+        ph, pw = _pair(padding)
+        dh, dw = _pair(dilation)
+        G = int(groups)
+        if G <= 0 or C % G or Cg * G != C:
+            raise ValueError("weight shape %s does not match C=%d, groups=%d" % (w_shape, C, G))
+        p = (ctypes.c_int * 14)(N, C, H, W, K, R, S, sh, sw, ph, pw, dh, dw, G)
+        if self.lib.oracle_check(p) != 0:
+            raise ValueError("invalid convolution problem %s" % (list(p),))
+        OH = self.output_size(H, R, sh, ph, dh)
+        OW = self.output_size(W, S, sw, pw, dw)
+        return p, (N, K, OH, OW)
+
+    def output_size(self, n_in: int, k: int, stride: int = 1, pad: int = 0, dil: int = 1) -> int:
+        """floor((in + 2 pad - dil (k - 1) - 1) / stride) + 1, or 0 if it does not fit."""
+        return int(self.lib.oracle_output_size(int(n_in), int(k), int(stride), int(pad), int(dil)))
+
+    def max_threads(self) -> int:
+        """OpenMP threads the oracle will use (OMP_NUM_THREADS, else all cores)."""
+        return int(self.lib.oracle_max_threads())
+
+    def conv2d(self, x, w, stride=1, padding=0, dilation=1, groups=1):
+        """fp64 convolution of NCHW ``x`` with KCRS ``w``.
+
+        Inputs of any real float dtype are widened exactly to float64.
+        Returns ``(y, den)``, both float64 [N, K, OH, OW], where ``den`` is the
+        sum of |x * w| over each output's terms.
+        """
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        p, oshape = self._params(x.shape, w.shape, stride, padding, dilation, groups)
+        y = np.empty(oshape, dtype=np.float64)
+        den = np.empty(oshape, dtype=np.float64)
+        if self.lib.oracle_conv2d_f64(x.ctypes.data, w.ctypes.data, p, y.ctypes.data, den.ctypes.data):
+            raise RuntimeError("oracle_conv2d_f64 failed")
+        return y, den
+
+    def conv2d_int8(self, x, w, stride=1, padding=0, dilation=1, groups=1):
+        """Exact int64 accumulators of the int8 convolution (NCHW ``x``, KCRS ``w``)."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w)
+        if x.dtype != np.int8 or w.dtype != np.int8:
+            raise TypeError("conv2d_int8 takes int8 arrays")
+        p, oshape = self._params(x.shape, w.shape, stride, padding, dilation, groups)
+        acc = np.empty(oshape, dtype=np.int64)
+        if self.lib.oracle_conv2d_i8(x.ctypes.data, w.ctypes.data, p, acc.ctypes.data):
+            raise RuntimeError("oracle_conv2d_i8 failed")
+        return acc
+
+    def requant(self, acc, scale):
+        """int8 outputs clamp(rne(fp32(acc) * scale[k]), -127, 127) of [N, K, ...] accumulators."""
+        acc = np.ascontiguousarray(acc, dtype=np.int64)
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        N, K = acc.shape[0], acc.shape[1]
+        if scale.shape != (K,):
+            raise ValueError("scale must have shape [K]")
+        hw = int(np.prod(acc.shape[2:], dtype=np.int64)) if acc.ndim > 2 else 1
+        y = np.empty(acc.shape, dtype=np.int8)
+        if self.lib.oracle_requant_i8(acc.ctypes.data, scale.ctypes.data, N, K, hw, y.ctypes.data):
+            raise OverflowError("an accumulator does not fit in int32")
+        return y
+
+    def requant_one(self, acc: int, scale: float) -> int:
+        """The requantisation rule for a single accumulator value (int32 range)."""
+        if not (-2**31 <= int(acc) < 2**31):
+            raise OverflowError("accumulator outside int32")
+        return int(self.lib.oracle_requant_one(int(acc), float(np.float32(scale))))
+
+    def conv2d_int8_requant(self, x, w, scale, stride=1, padding=0, dilation=1, groups=1):
+        """int8 convolution followed by the requantisation rule; returns (y_int8, acc_int64)."""
+        acc = self.conv2d_int8(x, w, stride, padding, dilation, groups)
+        return self.requant(acc, scale), acc
+
+    @staticmethod
+    def _points_idx(idx):
+        idx = np.ascontiguousarray(idx, dtype=np.int64)
+        if idx.ndim != 2 or idx.shape[1] != 4:
+            raise ValueError("idx must be [npts, 4] of (n, k, oh, ow)")
+        return idx
+
+    def conv2d_points(self, x, w, idx, stride=1, padding=0, dilation=1, groups=1):
+        """fp64 values (y, den) of selected outputs idx[:, (n, k, oh, ow)]."""
+        x = np.ascontiguousarray(x, dtype=np.float64)
+        w = np.ascontiguousarray(w, dtype=np.float64)
+        idx = self._points_idx(idx)
+        p, _ = self._params(x.shape, w.shape, stride, padding, dilation, groups)
+        y = np.empty(len(idx), dtype=np.float64)
+        den = np.empty(len(idx), dtype=np.float64)
+        if self.lib.oracle_conv2d_f64_points(x.ctypes.data, w.ctypes.data, p, len(idx),
+                                             idx.ctypes.data, y.ctypes.data, den.ctypes.data):
+            raise ValueError("oracle_conv2d_f64_points: index out of range")
+        return y, den
+
+    def conv2d_int8_points(self, x, w, idx, stride=1, padding=0, dilation=1, groups=1):
+        """Exact int64 accumulators of selected outputs idx[:, (n, k, oh, ow)]."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w)
+        if x.dtype != np.int8 or w.dtype != np.int8:
+            raise TypeError("conv2d_int8_points takes int8 arrays")
+        idx = self._points_idx(idx)
+        p, _ = self._params(x.shape, w.shape, stride, padding, dilation, groups)
+        acc = np.empty(len(idx), dtype=np.int64)
+        if self.lib.oracle_conv2d_i8_points(x.ctypes.data, w.ctypes.data, p, len(idx),
+                                            idx.ctypes.data, acc.ctypes.data):
+            raise ValueError("oracle_conv2d_i8_points: index out of range")
+        return acc
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from ``oracle.c`` in this directory (built on first use)."""
+    global _default
+    if _default is None:
+        _default = Oracle(build())
+    return _default
+
+
+def output_size(*a, **k):
+    return default().output_size(*a, **k)
+
+
+def max_threads():
+    return default().max_threads()
+
+
+def conv2d(*a, **k):
+    return default().conv2d(*a, **k)
+
+
+def conv2d_int8(*a, **k):
+    return default().conv2d_int8(*a, **k)
+
+
+def requant(*a, **k):
+    return default().requant(*a, **k)
+
+
+def requant_one(*a, **k):
+    return default().requant_one(*a, **k)
+
+
+def conv2d_int8_requant(*a, **k):
+    return default().conv2d_int8_requant(*a, **k)
+
+
+def conv2d_points(*a, **k):
+    return default().conv2d_points(*a, **k)
+
+
+def conv2d_int8_points(*a, **k):
+    return default().conv2d_int8_points(*a, **k)
+
+
+def normalised_error(y_hat, y, den):
+    """max_i |y_hat_i - y_i| / den_i; where den_i == 0, y_hat_i must be exactly 0.
+
+    Returns +inf when an output with den == 0 is not exactly zero.
+    """
+    y_hat = np.asarray(y_hat, dtype=np.float64)
+    y = np.asarray(y, dtype=np.float64)
+    den = np.asarray(den, dtype=np.float64)
+    zero = den == 0
+    if np.any(y_hat[zero] != 0):
+        return float("inf")
+    if np.all(zero):
+        return 0.0
+    nz = ~zero
+    return float(np.max(np.abs(y_hat[nz] - y[nz]) / den[nz]))

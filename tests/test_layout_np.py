@@ -1,0 +1,36 @@
+"""NCHWx packing used to feed the GPU library (CPU only).
+
+The MegEngine inference article, section "NCHWX", defines the layout as
+[Batch, Channels/X, Height, Width, X] with X = 4 or 8.  Element (n, c, h, w)
+lives at [n][c // X][h][w][c % X]; channels past C are zero.
+"""
+import numpy as np
+import pytest
+
+from cnn_convolution_fwd_amd.workloads import (bf16_bits, bf16_to_f32, pack_nchwx, round_to_bf16,
+                                                unpack_nchwx)
+
+
+@pytest.mark.parametrize("C,xb", [(3, 4), (4, 4), (16, 4), (5, 8), (32, 8)])
+def test_pack_index_formula_and_roundtrip(C, xb):
+    rng = np.random.default_rng(C * xb)
+    x = rng.integers(-127, 128, size=(2, C, 3, 5)).astype(np.int8)
+    p = pack_nchwx(x, xb)
+    assert p.shape == (2, -(-C // xb), 3, 5, xb)
+    for n in range(2):
+        for c in range(-(-C // xb) * xb):
+            for h in range(3):
+                for w in range(5):
+                    expect = x[n, c, h, w] if c < C else 0
+                    assert p[n, c // xb, h, w, c % xb] == expect
+    np.testing.assert_array_equal(unpack_nchwx(p, C), x)
+
+
+def test_bf16_rounding_is_rne():
+    # 1 + 2^-8 is halfway between bf16 neighbours 1 and 1 + 2^-7: ties to even -> 1
+    vals = np.array([1.0 + 2**-8, 1.0 + 3 * 2**-8, -1.0 - 2**-8, 1.0 + 2**-8 + 2**-20], dtype=np.float32)
+    out = round_to_bf16(vals)
+    np.testing.assert_array_equal(out, np.array([1.0, 1.0 + 2**-6, -1.0, 1.0 + 2**-7], dtype=np.float32))
+    bits = bf16_bits(np.array([1.0, -2.0], dtype=np.float32))
+    assert bits.tolist() == [0x3F80, 0xC000]
+    np.testing.assert_array_equal(bf16_to_f32(bits), [1.0, -2.0])

@@ -1,0 +1,68 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a temporary copy of oracle.c (a flipped kernel,
+a dropped term, a wrong stride / padding / dilation / group index, a
+transposed weight index, a wrong error normaliser, a different rounding or
+clamp), builds it with the oracle's own flags and runs the pins of
+test_oracle_pins.py against it: at least one pin must fail.  The committed
+oracle itself is never modified.
+"""
+import os
+import shutil
+
+import pytest
+
+import oracle
+import tests.test_oracle_pins as pins
+
+MUTATIONS = {
+    "kernel_flip": ("+ s * dw", "+ (S - 1 - s) * dw"),
+    "stride_ignored": ("oh * sh - ph", "oh - ph"),
+    "dilation_is_stride": ("r * dh", "r * sh"),
+    "padding_sign": ("- ph +", "+ ph +"),
+    "dropped_last_tap": ("for (int s = 0; s < S; ++s)", "for (int s = 0; s + 1 < S; ++s)"),
+    "group_offset_dropped": ("const int c = g * Cg + cc;", "const int c = cc + 0 * g;"),
+    "weight_index_transposed": ("* R + r) * S + s]", "* R + s) * S + r]"),
+    "den_not_absolute": ("+= fabs(prod);", "+= prod;"),
+    "round_half_away": ("rintf(prod)", "roundf(prod)"),
+    "asymmetric_clamp": ("if (q < -127.0f)\n        return -127;", "if (q < -128.0f)\n        return -128;"),
+    "exact_product": ("const float prod = a * scale;", "const float prod = (float)((double)acc * (double)scale); (void)a;"),
+}
+
+
+def pin_checks():
+    yield "worked_example", pins.test_worked_example_stride2
+    yield "no_flip", pins.test_no_kernel_flip
+    for i, case in enumerate(pins.cases(12, 1234)):
+        yield "im2col_%d" % i, (lambda c=case: pins.test_vs_im2col_bruteforce(c))
+    yield "groups", pins.test_groups_are_concatenated_convolutions
+    yield "depthwise", pins.test_depthwise_is_per_channel_correlation
+    yield "scipy", pins.test_single_channel_is_scipy_correlate2d
+    yield "den", pins.test_den_properties
+    yield "ties", pins.test_requant_ties_to_even
+    yield "saturate", pins.test_requant_saturates_symmetrically
+    yield "fp32_first", pins.test_requant_converts_acc_to_fp32_first
+    yield "delta", lambda: pins.test_delta_kernel_is_identity(3, 3)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    assert old in src, "mutation pattern %r no longer matches oracle.c" % old
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = oracle.build(force=True, src=str(mutated), out=str(tmp_path / "liboracle_mut.so"))
+    saved = oracle._default
+    oracle._default = oracle.Oracle(lib)
+    failed = []
+    try:
+        for label, check in pin_checks():
+            try:
+                check()
+            except (AssertionError, ValueError, OverflowError):
+                failed.append(label)
+    finally:
+        oracle._default = saved
+        shutil.rmtree(tmp_path, ignore_errors=True)
+    assert failed, "planted mistake %r was not caught by any pin" % name
