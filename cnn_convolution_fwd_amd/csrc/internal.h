@@ -1,0 +1,145 @@
+// Internal declarations of the cfwd GPU library (gfx950).  Not installed and
+// not part of the C ABI: the public surface is include/cfwd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "cfwd.h"
+
+namespace cfwd {
+
+// ------------------------------------------------------------------ problem
+
+// A validated problem, with derived sizes.  Activation element (n, c, h, w) is
+// at  n*x_img + c*H*W + h*W + w                      (NCHW, xb == 1)
+//     n*x_img + (c/xb)*H*W*xb + (h*W + w)*xb + c%xb  (NCHWX)
+struct Prob {
+    int n, c, h, w, k, r, s;
+    int sh, sw, ph, pw, dh, dw, g;
+    int oh, ow, cg, kg;
+    int layout;  // cfwd_layout
+    int xb;      // channel block: 1 for NCHW, 4 or 8 for NCHWX
+    int dtype;   // cfwd_dtype
+    int esize;   // bytes per element
+    long long x_img, y_img;  // elements per image of x and y (incl. channel padding)
+    bool depthwise() const { return g == c && g == k && cg == 1; }
+    bool pointwise() const { return r == 1 && s == 1 && ph == 0 && pw == 0; }
+};
+
+// Fills *p from a descriptor; returns CFWD_OK or INVALID_ARG/UNSUPPORTED and a
+// reason in *why.
+cfwd_status make_prob(const cfwd_conv_desc* d, Prob* p, std::string* why);
+
+// ------------------------------------------------------------ error plumbing
+
+cfwd_status set_error(cfwd_status st, const std::string& msg);
+cfwd_status check_hip(hipError_t e, const char* what);
+
+// ------------------------------------------------------------ kernel families
+// Each family answers: can it run (problem, config)?  How many bytes of
+// prepared filter / workspace?  And launches on a stream.  Launchers assume the
+// problem is valid and the pointers checked; they return CFWD_ERR_HIP if a
+// launch fails.
+
+// Direct summation (generic fallback; depthwise specialisation inside).
+int direct_num_configs();
+bool direct_supported(const Prob& p, int cfg, std::string* why);
+cfwd_status direct_launch(const Prob& p, int cfg, const void* x, const void* w,
+                          const float* scale, void* y, hipStream_t st);
+
+// Implicit GEMM on the matrix cores.
+int igemm_num_configs();
+bool igemm_supported(const Prob& p, int cfg, std::string* why);
+size_t igemm_filter_bytes(const Prob& p, int cfg);
+cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
+cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp,
+                         const float* scale, void* y, hipStream_t st);
+int igemm_default_config(const Prob& p);
+
+// Pointwise (1x1) path.
+int pointwise_num_configs();
+bool pointwise_supported(const Prob& p, int cfg, std::string* why);
+size_t pointwise_filter_bytes(const Prob& p, int cfg);
+cfwd_status pointwise_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
+cfwd_status pointwise_launch(const Prob& p, int cfg, const void* x, const void* wp,
+                             const float* scale, void* y, hipStream_t st);
+
+// Winograd F(m x m, 3 x 3), m = 2 or 6.
+int winograd_num_configs(int m);
+bool winograd_supported(const Prob& p, int m, int cfg, std::string* why);
+size_t winograd_filter_bytes(const Prob& p, int m, int cfg);
+cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st);
+cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp,
+                            void* y, hipStream_t st);
+
+// Writes 0 to the NCHWX output channels past K (no-op unless K % xb != 0).
+cfwd_status zero_output_channel_padding(const Prob& p, void* y, hipStream_t st);
+
+// Fast-Run accuracy gate helpers (k_util.hip).
+cfwd_status abs_copy(const Prob& p, const void* src, void* dst, long long count, hipStream_t st);
+// stats[0] = bit pattern of max |cand - ref| / den (float dtypes), stats[1] =
+// count of outputs that fail outright (int8: any difference; float: NaN, or
+// den == 0 with cand != 0).
+cfwd_status gate_compare(const Prob& p, const void* cand, const void* ref, const void* den, unsigned* stats,
+                         hipStream_t st);
+
+// ------------------------------------------------------------ device helpers
+
+#if defined(__HIPCC__)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 storage type: raw 16-bit pattern.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_to_float(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t float_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// int32 accumulator -> int8: clamp(rne(fp32(acc) * scale), -127, 127).
+// __fmul_rn keeps the multiply a separate IEEE operation; rintf rounds to
+// nearest even.
+__device__ __forceinline__ int8_t requant_i8(int acc, float scale) {
+    float q = rintf(__fmul_rn(static_cast<float>(acc), scale));
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return static_cast<int8_t>(static_cast<int>(q));
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float to_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+    static __device__ __forceinline__ float to_f(bf16_t v) { return bf16_to_float(v.bits); }
+};
+template <> struct Elem<int8_t> {
+    static __device__ __forceinline__ int to_f(int8_t v) { return v; }
+};
+
+// Offset of activation element (c, h, w) inside one image.
+template <int XB>
+__device__ __forceinline__ long long act_off(int c, int h, int w, int H, int W) {
+    if (XB == 1)
+        return (static_cast<long long>(c) * H + h) * W + w;
+    return ((static_cast<long long>(c / XB) * H + h) * W + w) * XB + (c % XB);
+}
+#endif
+
+}  // namespace cfwd

@@ -1,0 +1,15 @@
+// Implicit-GEMM instantiations for one dtype (bf16_t); the kernel is in igemm_impl.h.
+#include "igemm_impl.h"
+
+namespace cfwd {
+
+cfwd_status igemm_launch_bf16(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
+                             const float* scale, void* y, hipStream_t st) {
+    return ig::launch_dtype<bf16_t>(cfg, p, g, x, wp, scale, y, st);
+}
+
+cfwd_status igemm_prepare_bf16(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st) {
+    return ig::prepare_dtype<bf16_t>(cfg, p, g, w, wp, st);
+}
+
+}  // namespace cfwd

@@ -1,0 +1,196 @@
+/*
+ * cfwd.h -- forward 2-D convolution for CNN inference on one AMD Instinct
+ * MI355X (gfx950).  Plain C ABI: no C++ types, no exceptions, no torch types.
+ *
+ * What is computed (every entry point that writes y):
+ *   The forward convolution of CNN inference as the naive loop nest of the
+ *   blog post "卷积总结" (convolution summary), section "最原始的卷积实现",
+ *   defines it -- a cross-correlation, output[k, oh, ow] = sum over c, r, s of
+ *   w[k, c, r, s] * x[c, oh*stride + r*dil - pad, ow*stride + s*dil - pad],
+ *   with a batch loop, symmetric zero padding, stride, dilation and groups
+ *   (output channel k reads input channels of group k / (K/G) only), and
+ *   OH = floor((H + 2*pad_h - dil_h*(R-1) - 1) / stride_h) + 1 (OW likewise).
+ *
+ * Algorithms (MegEngine inference article, sections "Im2col+MatMul",
+ * "Winograd" and "Fast-Run"; Momenta talk "Paper Reading | 讓深度學習更高效運行
+ * 的兩個視角", section "優化2：Depthwise卷積" for the depthwise / 1x1 layers):
+ *   IMPLICIT_GEMM   im2col x matmul without materialising im2col: input patches
+ *                   are staged in LDS and multiplied on the matrix cores.
+ *   WINOGRAD_F2X2_3X3 / WINOGRAD_F6X6_3X3
+ *                   F(m x m, 3 x 3) minimal filtering for 3x3, stride 1,
+ *                   dilation 1, groups 1, float dtypes only.
+ *   DIRECT          direct summation; the depthwise (G = C = K) path.
+ *   POINTWISE       1x1 convolution as a low-K matrix product.
+ *   AUTO            resolved per problem: a Fast-Run map entry if one exists,
+ *                   else (or a search with CFWD_FASTRUN_MODE=search) a fixed
+ *                   preference: depthwise -> DIRECT, 1x1 -> POINTWISE, else
+ *                   IMPLICIT_GEMM.  Winograd is never chosen without timing.
+ *
+ * Tensors (all device memory, owned by the caller, 16-byte aligned, dense):
+ *   x  activations  NCHW  [N][C][H][W]
+ *                   NCHWX [N][ceil(C/x)][H][W][x], x = 4 or 8 (MegEngine
+ *                   inference article, section "NCHWX"); channels past C are
+ *                   ignored on input.
+ *   w  weights      KCRS  [K][C/G][R][S] in every layout, activation dtype.
+ *   y  output       same layout and dtype as x, with K channels; in NCHWX the
+ *                   channels past K are written as 0.
+ *   requant_scale   int8 only: fp32 [K] on the device; the int32 accumulator
+ *                   becomes int8 as clamp(rne(fp32(acc) * scale[k]), -127, 127)
+ *                   (round to nearest even, symmetric clamp, zero point 0).
+ * Dtypes: fp32 (fp32 accumulate), bf16 (fp32 accumulate, output rounded to
+ * nearest even), int8 (int32 accumulate, requantised output).
+ *
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream).  Calls that only enqueue work return without waiting.
+ *
+ * Errors: every call returns a cfwd_status; on failure nothing has been
+ * enqueued and cfwd_last_error() (per thread) describes why.  Validation
+ * failures never touch y.  No call allocates device memory.
+ */
+#ifndef CFWD_H
+#define CFWD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CFWD_OK = 0,
+    CFWD_ERR_INVALID_ARG = 1,  /* bad descriptor, NULL or misaligned pointer */
+    CFWD_ERR_UNSUPPORTED = 2,  /* valid problem this algorithm cannot run   */
+    CFWD_ERR_WORKSPACE = 3,    /* workspace / prepared buffer too small      */
+    CFWD_ERR_NO_CANDIDATE = 4, /* Fast-Run found no candidate passing its gate */
+    CFWD_ERR_HIP = 5,          /* a HIP runtime call failed (message kept)   */
+    CFWD_ERR_CACHE_IO = 6      /* Fast-Run map file could not be written    */
+} cfwd_status;
+
+typedef enum { CFWD_LAYOUT_NCHW = 0, CFWD_LAYOUT_NCHWX = 1 } cfwd_layout;
+
+typedef enum { CFWD_F32 = 0, CFWD_BF16 = 1, CFWD_I8 = 2 } cfwd_dtype;
+
+typedef enum {
+    CFWD_ALGO_AUTO = 0,
+    CFWD_ALGO_IMPLICIT_GEMM = 1,
+    CFWD_ALGO_WINOGRAD_F2X2_3X3 = 2,
+    CFWD_ALGO_WINOGRAD_F6X6_3X3 = 3,
+    CFWD_ALGO_DIRECT = 4,
+    CFWD_ALGO_POINTWISE = 5
+} cfwd_algo_kind;
+
+/* One convolution problem.  pad_* >= 0; every other integer >= 1;
+ * C and K divisible by groups; x is 4 or 8 when layout is NCHWX (ignored for
+ * NCHW).  Each of x and y must hold fewer than 2^31 elements per image. */
+typedef struct {
+    int n, c, h, w, k, r, s;
+    int stride_h, stride_w, pad_h, pad_w, dil_h, dil_w, groups;
+    cfwd_layout layout;
+    int x;
+    cfwd_dtype dtype;
+} cfwd_conv_desc;
+
+/* An algorithm choice: family, tile configuration within the family
+ * (-1 = the family's default for the problem), and the median time Fast-Run
+ * measured for it in milliseconds (0 when not measured). */
+typedef struct {
+    cfwd_algo_kind kind;
+    int config_id;
+    float median_ms;
+} cfwd_algo;
+
+/* Library version string, e.g. "cfwd 0.1.0 gfx950". */
+const char *cfwd_version(void);
+
+/* OH, OW of the problem (the floor formula above).  INVALID_ARG if the
+ * descriptor is invalid or the window does not fit. */
+cfwd_status cfwd_output_dims(const cfwd_conv_desc *desc, int *oh, int *ow);
+
+/* Resolve `algo` (AUTO, or a family with config_id -1) to the concrete
+ * (kind, config_id) conv2d_fwd would run.  UNSUPPORTED if the family cannot
+ * run this problem. */
+cfwd_status cfwd_resolve_algo(const cfwd_conv_desc *desc, cfwd_algo algo, cfwd_algo *resolved);
+
+/* Every (kind, config_id) that can run the problem, in Fast-Run's fixed
+ * candidate order (IMPLICIT_GEMM < POINTWISE < DIRECT < WINOGRAD_F2 <
+ * WINOGRAD_F6, then config id).  Writes at most `cap` entries to out (out may
+ * be NULL when cap is 0) and the total count to *count. */
+cfwd_status cfwd_list_candidates(const cfwd_conv_desc *desc, cfwd_algo *out, int cap, int *count);
+
+/* Bytes of the prepared (re-laid-out or transformed) filter the algorithm
+ * reads; 0 means it reads the KCRS weights directly. */
+cfwd_status cfwd_filter_size(const cfwd_conv_desc *desc, cfwd_algo algo, size_t *bytes);
+
+/* Build the prepared filter of `algo` from KCRS weights into w_prepared
+ * (`bytes` >= cfwd_filter_size).  Enqueued on `stream`.  Winograd: the
+ * G g G^T filter transform (MegEngine inference article, section "Winograd",
+ * step one); implicit GEMM: the weight tile order its matrix-core loop reads
+ * (the pack step the article's "融合 PACK" section folds away on the
+ * activation side). */
+cfwd_status cfwd_prepare_filter(const cfwd_conv_desc *desc, cfwd_algo algo, const void *w_kcrs,
+                                void *w_prepared, size_t bytes, void *stream);
+
+/* Workspace bytes conv2d_fwd needs for `algo` when it is given no prepared
+ * filter (it then prepares one into the workspace first).  0 when none. */
+cfwd_status cfwd_workspace_size(const cfwd_conv_desc *desc, cfwd_algo algo, size_t *bytes);
+
+/* y = conv(x, w).  w_kcrs is required.  w_prepared may be NULL; when it is
+ * not, it must hold cfwd_prepare_filter's output for the same descriptor and
+ * resolved algorithm, and the filter is not re-prepared.  requant_scale is
+ * required for int8 and must be NULL otherwise.  Enqueued on `stream`. */
+cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc *desc, cfwd_algo algo, const void *x,
+                            const void *w_kcrs, const void *w_prepared,
+                            const float *requant_scale, void *y, void *workspace,
+                            size_t ws_bytes, void *stream);
+
+/* Fast-Run selection phase (MegEngine inference article, section "Fast-Run"):
+ * time every candidate of cfwd_list_candidates on this device with these
+ * buffers (median of >= 5 runs after 2 warm-ups), reject any whose output
+ * fails the accuracy gate against the IMPLICIT_GEMM or DIRECT result on the
+ * same data (bit-identical for int8; normalised error <= 1e-5 fp32 direct
+ * families, 1e-3 fp32 Winograd, 1e-2 bf16), keep the fastest (times within 1%
+ * count as equal and the earlier candidate wins), record it in the map and
+ * return it in *best.  Synchronises `stream`; overwrites y.  workspace must
+ * hold cfwd_fastrun_workspace_size bytes. */
+cfwd_status cfwd_fastrun_select(const cfwd_conv_desc *desc, const void *x, const void *w_kcrs,
+                                const float *requant_scale, void *y, void *workspace,
+                                size_t ws_bytes, void *stream, cfwd_algo *best);
+
+/* Workspace for cfwd_fastrun_select: the largest candidate workspace plus a
+ * reference output copy. */
+cfwd_status cfwd_fastrun_workspace_size(const cfwd_conv_desc *desc, size_t *bytes);
+
+/* Fast-Run execution-phase map (host memory, process-wide, thread-safe).
+ * lookup: CFWD_OK and *algo when the problem has an entry on this device,
+ * UNSUPPORTED otherwise.  load: merge a map file (one record per line); a
+ * missing, corrupt or other-device file is ignored with CFWD_OK.
+ * save: write the whole map (CACHE_IO on failure).  clear: empty it. */
+cfwd_status cfwd_fastrun_lookup(const cfwd_conv_desc *desc, cfwd_algo *algo);
+cfwd_status cfwd_fastrun_load(const char *path);
+cfwd_status cfwd_fastrun_save(const char *path);
+cfwd_status cfwd_fastrun_clear(void);
+
+/* The host-side part of Fast-Run's choice, for callers that time candidates
+ * themselves (and for testing the rule without a GPU): cands[n] in Fast-Run
+ * order, times[n * reps] row-major in ms, gate_ok[n] nonzero when the
+ * candidate passed the accuracy gate.  *chosen = index of the candidate with
+ * the smallest median time, where a later candidate wins only if its median is
+ * more than 1% below the current best's; -1 if none passed. */
+cfwd_status cfwd_fastrun_choose(const cfwd_algo *cands, const float *times, int n, int reps,
+                                const int *gate_ok, int *chosen);
+
+/* Static description of a status code. */
+const char *cfwd_status_string(cfwd_status status);
+
+/* Detail of this thread's most recent failure ("" if none). */
+const char *cfwd_last_error(void);
+
+/* Name of an algorithm, e.g. "implicit_gemm/3". */
+const char *cfwd_algo_name(cfwd_algo algo);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CFWD_H */

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Floating point: max over outputs of |y_gpu - y| / sum|x*w| must stay within
+1e-5 (fp32 implicit GEMM / direct), 1e-3 (fp32 Winograd) or 1e-2 (bf16).
+int8: outputs bit-identical to the oracle's int64 accumulation followed by
+clamp(rne(fp32(acc) * scale[k]), -127, 127).
+
+Small shapes are compared element by element over every candidate algorithm
+the library lists; full-size benchmark layers are compared on sampled outputs
+the oracle computes one by one.
+"""
+import sys
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from cnn_convolution_fwd_amd import binding as B
+from cnn_convolution_fwd_amd.workloads import (CONFIGS, Layer, float_problem, int8_problem, random_float_problem,
+                                                random_int8_problem)
+from tests.gpu_util import TOL, TOL_WINOGRAD, candidates_for, run_conv, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # name, N, C, H, W, K, R, S, stride, pad, dil, groups
+    ("3x3_s1_ragged", 2, 20, 13, 17, 24, 3, 3, 1, 1, 1, 1),
+    ("3x3_s2", 1, 35, 9, 30, 70, 3, 3, 2, 1, 1, 1),
+    ("1x1", 3, 16, 8, 8, 16, 1, 1, 1, 0, 1, 1),
+    ("1x1_s2", 2, 40, 14, 14, 72, 1, 1, 2, 0, 1, 1),
+    ("5x5_d2", 1, 12, 15, 14, 20, 5, 5, 1, 4, 2, 1),
+    ("grouped", 2, 12, 10, 11, 18, 3, 3, 1, 1, 1, 3),
+    ("depthwise", 2, 16, 12, 16, 16, 3, 3, 1, 1, 1, 16),
+    ("stem7x7s2", 2, 3, 20, 22, 8, 7, 7, 2, 3, 1, 1),
+    ("tiny", 1, 1, 1, 1, 1, 1, 1, 1, 0, 1, 1),
+    ("asym", 1, 9, 7, 33, 130, 3, 1, (2, 1), (0, 1), 1, 1),
+    ("multi_tile_k", 1, 70, 6, 6, 200, 3, 3, 1, 1, 1, 1),
+    ("wide_row", 1, 8, 3, 300, 16, 3, 3, 1, 1, 1, 1),
+]
+
+LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
+
+
+def tol_for(dtype, algo):
+    return (TOL_WINOGRAD if algo.startswith("winograd") else TOL)[dtype]
+
+
+def check_float(name, y, ref, den, dtype, algo):
+    assert y.shape == ref.shape, (name, y.shape, ref.shape)
+    err = oracle.normalised_error(y, ref, den)
+    assert err <= tol_for(dtype, algo), "%s: normalised error %.3g > %.1g" % (name, err, tol_for(dtype, algo))
+    return err
+
+
+@pytest.mark.parametrize("layout,xb", LAYOUTS, ids=["nchw", "nchw4", "nchw8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i8"])
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_small_shapes_all_candidates(case, dtype, layout, xb):
+    torch_cuda()
+    name, N, C, H, W, K, R, S, st, pd, dl, G = case
+    L = Layer(name, C, K, H, W, R, S, 1, 0, 1, G)
+    seed = zlib.crc32((name + dtype).encode())
+    cands = candidates_for((N, C, H, W, K, R, S), dtype, st, pd, dl, G, layout, xb)
+    assert cands, "no candidate for %s" % name
+    failures = []
+    if dtype == "i8":
+        pr = random_int8_problem(L, N, seed)
+        yref, _ = oracle.conv2d_int8_requant(pr.x, pr.w, pr.scale, st, pd, dl, G)
+        for algo, cfg in cands:
+            say("case", name, dtype, layout, xb, algo, cfg)
+            y = run_conv(pr.x, pr.w, dtype, st, pd, dl, G, layout, xb, algo, cfg, scale=pr.scale)
+            if not np.array_equal(y, yref):
+                failures.append("%s/%d: %d of %d int8 outputs differ" % (algo, cfg, int((y != yref).sum()), y.size))
+    else:
+        pr = random_float_problem(L, N, dtype, seed)
+        yref, den = oracle.conv2d(pr.x, pr.w, st, pd, dl, G)
+        for algo, cfg in cands:
+            say("case", name, dtype, layout, xb, algo, cfg)
+            y = run_conv(pr.x, pr.w, dtype, st, pd, dl, G, layout, xb, algo, cfg)
+            err = oracle.normalised_error(y, yref, den)
+            if not err <= tol_for(dtype, algo):
+                failures.append("%s/%d: error %.3g" % (algo, cfg, err))
+    assert not failures, "; ".join(failures)
+
+
+def test_prepared_filter_path_matches():
+    torch_cuda()
+    L = Layer("p", 24, 40, 10, 12, 3, 3, 1, 1)
+    pr = random_float_problem(L, 2, "bf16", 5)
+    a = run_conv(pr.x, pr.w, "bf16", 1, 1, algo="implicit_gemm", config_id=0)
+    b = run_conv(pr.x, pr.w, "bf16", 1, 1, algo="implicit_gemm", config_id=0, prepared=True)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_config1_full():
+    """Single 3x3 conv 16->32 at 32x32, fp32, every candidate, full tensor."""
+    torch_cuda()
+    pr = float_problem(1)
+    L = pr.layer
+    yref, den = oracle.conv2d(pr.x, pr.w, L.stride, L.pad, L.dil, L.groups)
+    for algo, cfg in candidates_for((1, 16, 32, 32, 32, 3, 3), "f32", 1, 1):
+        say("config1", algo, cfg)
+        y = run_conv(pr.x, pr.w, "f32", 1, 1, algo=algo, config_id=cfg)
+        check_float("config1 %s/%d" % (algo, cfg), y, yref, den, "f32", algo)
+
+
+def sample_points(shape, n, seed):
+    """n random output positions plus the four corners of every (n, k) edge case."""
+    N, K, OH, OW = shape
+    rng = np.random.default_rng(seed)
+    pts = np.stack([rng.integers(0, N, n), rng.integers(0, K, n), rng.integers(0, OH, n), rng.integers(0, OW, n)], 1)
+    corners = np.array([[nn, kk, oh, ow] for nn in (0, N - 1) for kk in (0, K - 1) for oh in (0, OH - 1)
+                        for ow in (0, OW - 1)])
+    return np.concatenate([pts, corners]).astype(np.int64)
+
+
+def check_points_float(name, y, pr, dtype, algo, n=3000):
+    L = pr.layer
+    idx = sample_points(y.shape, n, 1)
+    ref, den = oracle.conv2d_points(pr.x, pr.w, idx, L.stride, L.pad, L.dil, L.groups)
+    got = y[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]]
+    err = oracle.normalised_error(got, ref, den)
+    assert err <= tol_for(dtype, algo), "%s: sampled normalised error %.3g" % (name, err)
+    return err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_config3_full_size_sampled(dtype):
+    """ResNet 3x3 256->256 at 56x56, N=32: every IG config on sampled outputs."""
+    torch_cuda()
+    pr = float_problem(3, dtype=dtype)
+    for algo, cfg in candidates_for((32, 256, 56, 56, 256, 3, 3), dtype, 1, 1):
+        if algo == "direct":
+            continue  # generic direct at this size is slow and covered on small shapes
+        say("config3", dtype, algo, cfg)
+        y = run_conv(pr.x, pr.w, dtype, 1, 1, algo=algo, config_id=cfg)
+        check_points_float("config3 %s %s/%d" % (dtype, algo, cfg), y, pr, dtype, algo)
+
+
+def test_config3_deterministic():
+    torch_cuda()
+    pr = float_problem(3, dtype="bf16")
+    a = run_conv(pr.x, pr.w, "bf16", 1, 1, algo="implicit_gemm")
+    b = run_conv(pr.x, pr.w, "bf16", 1, 1, algo="implicit_gemm")
+    np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layer_idx", [0, 1, 2])
+def test_config2_layers_n64_sampled(dtype, layer_idx):
+    """MobileNet-style stem / depthwise / pointwise at N=64, default algorithm."""
+    torch_cuda()
+    pr = float_problem(2, layer_idx, dtype=dtype)
+    L = pr.layer
+    say("config2", L.name, dtype)
+    y = run_conv(pr.x, pr.w, dtype, L.stride, L.pad, L.dil, L.groups)
+    check_points_float("config2 %s %s" % (L.name, dtype), y, pr, dtype, "auto")
+
+
+@pytest.mark.parametrize("layer_idx", [0, 1, 2, 3])
+def test_config4_layers_sampled(layer_idx):
+    torch_cuda()
+    pr = float_problem(4, layer_idx, dtype="bf16")
+    L = pr.layer
+    say("config4", L.name)
+    y = run_conv(pr.x, pr.w, "bf16", L.stride, L.pad, L.dil, L.groups)
+    check_points_float("config4 %s" % L.name, y, pr, "bf16", "auto")
+
+
+@pytest.mark.parametrize("layer_idx", range(20))
+def test_config5_int8_layer_exact(layer_idx):
+    """int8 ResNet-18 layer, NCHW4: full tensor at N=2 and sampled at N=64, bit-exact."""
+    torch_cuda()
+    L = CONFIGS[5].layers[layer_idx]
+    small = int8_problem(5, layer_idx, n=2)
+    yref, _ = oracle.conv2d_int8_requant(small.x, small.w, small.scale, L.stride, L.pad, L.dil, L.groups)
+    say("config5 full N=2", L.name)
+    y = run_conv(small.x, small.w, "i8", L.stride, L.pad, L.dil, L.groups, "NCHWX", 4, scale=small.scale)
+    assert np.array_equal(y, yref), "%s N=2: %d outputs differ" % (L.name, int((y != yref).sum()))
+    big = int8_problem(5, layer_idx)
+    say("config5 N=64", L.name)
+    y = run_conv(big.x, big.w, "i8", L.stride, L.pad, L.dil, L.groups, "NCHWX", 4, scale=big.scale)
+    idx = sample_points(y.shape, 2000, 2)
+    acc = oracle.conv2d_int8_points(big.x, big.w, idx, L.stride, L.pad, L.dil, L.groups)
+    ref = np.array([oracle.requant_one(int(a), float(big.scale[k])) for a, k in zip(acc, idx[:, 1])], dtype=np.int8)
+    got = y[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]]
+    assert np.array_equal(got, ref), "%s N=64: %d sampled outputs differ" % (L.name, int((got != ref).sum()))
+
+
+def test_fastrun_select_and_dispatch(tmp_path):
+    torch = torch_cuda()
+    B.fastrun_clear()
+    pr = float_problem(1)
+    from tests.gpu_util import to_device, from_device
+    xd, wd = to_device(pr.x, "f32"), to_device(pr.w, "f32")
+    say("fastrun config1")
+    best, y = B.fastrun_select(xd, wd, 1, 1)
+    yref, den = oracle.conv2d(pr.x, pr.w, 1, 1)
+    check_float("fastrun output", from_device(y, "f32"), yref, den, "f32", B.algo_name(best))
+    desc = B.desc_for(xd, wd, 1, 1)
+    hit = B.fastrun_lookup(desc)
+    assert hit is not None and hit.key() == best.key()
+    assert B.resolve_algo(desc, B.algo()).key() == best.key()
+    path = str(tmp_path / "fr.txt")
+    B.fastrun_save(path)
+    B.fastrun_clear()
+    assert B.fastrun_lookup(desc) is None
+    B.fastrun_load(path)
+    assert B.fastrun_lookup(desc).key() == best.key()
+    B.fastrun_clear()
+    torch.cuda.synchronize()
+
+
+def test_fastrun_int8_layer_bit_exact():
+    torch = torch_cuda()
+    B.fastrun_clear()
+    L = CONFIGS[5].layers[6]
+    pr = int8_problem(5, 6, n=4)
+    from tests.gpu_util import to_device, from_device
+    from cnn_convolution_fwd_amd.workloads import pack_nchwx, unpack_nchwx
+    xd = to_device(pack_nchwx(pr.x, 4), "i8")
+    wd = to_device(pr.w, "i8")
+    sd = torch.from_numpy(pr.scale).cuda()
+    say("fastrun int8", L.name)
+    best, y = B.fastrun_select(xd, wd, L.stride, L.pad, L.dil, L.groups, "NCHWX", channels=L.c, requant_scale=sd)
+    yref, _ = oracle.conv2d_int8_requant(pr.x, pr.w, pr.scale, L.stride, L.pad, L.dil, L.groups)
+    got = unpack_nchwx(from_device(y, "i8"), L.k)
+    assert np.array_equal(got, yref)
+    B.fastrun_clear()
