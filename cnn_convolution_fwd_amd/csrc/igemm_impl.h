@@ -49,7 +49,7 @@ struct Args {
     int N, C, H, W, K, OH, OW, Cg, Kg, R, S, sh, sw, ph, pw, dh, dw;
     long long x_img, y_img;
     int TN, TH, TW, PH, PW, npix;  // output tile and its input patch
-    int tiles_w, tiles_h;
+    int tiles_w, tiles_h, tiles_n;
     int nchunks, ntk;              // channel chunks, output-channel tiles
 };
 
@@ -77,6 +77,58 @@ template <> struct Mma<float> {
         c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
     }
 };
+
+// 32x32 output fragments: one lane holds output column (lane % 32) and, for
+// accumulator element v, row 8*(v/4) + 4*(lane/32) + v%4.  Per 64-byte K
+// chunk a lane feeds two 16-byte pieces (P0, P1) of its A row / B column:
+//   bf16: piece i -> one v_mfma_f32_32x32x16_bf16 (K = 16 each)
+//   int8: piece i -> one v_mfma_i32_32x32x32_i8   (K = 32 each)
+//   fp32: eight v_mfma_f32_32x32x2_f32, MFMA m taking element m%4 of piece m/4.
+// Which channel slots the pieces are is fixed by piece_slot().
+template <typename T> struct Mma32;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+template <> struct Mma32<bf16_t> {
+    using acc_t = f32x16;
+    static __device__ __forceinline__ void run(acc_t& c, const uint4& a0, const uint4& a1, const uint4& b0,
+                                               const uint4& b1) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b0), c,
+                                                    0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1), __builtin_bit_cast(bf16x8, b1), c,
+                                                    0, 0, 0);
+    }
+};
+template <> struct Mma32<int8_t> {
+    using acc_t = i32x16;
+    static __device__ __forceinline__ void run(acc_t& c, const uint4& a0, const uint4& a1, const uint4& b0,
+                                               const uint4& b1) {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a0), __builtin_bit_cast(i32x4, b0), c, 0,
+                                                  0, 0);
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a1), __builtin_bit_cast(i32x4, b1), c, 0,
+                                                  0, 0);
+    }
+};
+template <> struct Mma32<float> {
+    using acc_t = f32x16;
+    static __device__ __forceinline__ void run(acc_t& c, const uint4& a0, const uint4& a1, const uint4& b0,
+                                               const uint4& b1) {
+        const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const uint32_t bv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(av[m]), __uint_as_float(bv[m]), c, 0, 0, 0);
+    }
+};
+
+// 16-byte channel slot (0..3 of a 64-byte chunk) that piece i of a lane in
+// half h (= lane / 32) holds, for 32x32 fragments.  bf16 / int8: each MFMA
+// takes 16 (bf16) or 32 (int8) consecutive K, split over the two halves, so
+// piece i is slot 2i + h.  fp32: MFMA m takes K = 2, one value per half, and
+// lane half h supplies channels 8h .. 8h+7 over m = 0..7: slots 2h, 2h + 1.
+template <typename T>
+__device__ __host__ __forceinline__ int piece_slot(int i, int h) {
+    return (sizeof(T) == 4) ? 2 * h + i : 2 * i + h;
+}
 
 // Raw storage element of each dtype.
 template <typename T> struct Raw;
@@ -153,6 +205,24 @@ template <> __device__ __forceinline__ void store_out<int8_t>(int8_t* y, long lo
     y[off] = requant_i8(acc[v], scale);
 }
 
+// Four consecutive output pixels of one channel (NCHW, 4-aligned).
+template <typename T> __device__ __forceinline__ void store_out4(T* y, long long off, typename Mma<T>::acc_t acc,
+                                                                float scale);
+template <> __device__ __forceinline__ void store_out4<float>(float* y, long long off, f32x4 acc, float) {
+    *reinterpret_cast<float4*>(y + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+}
+template <> __device__ __forceinline__ void store_out4<bf16_t>(bf16_t* y, long long off, f32x4 acc, float) {
+    const uint32_t lo = static_cast<uint32_t>(float_to_bf16(acc[0])) | (static_cast<uint32_t>(float_to_bf16(acc[1])) << 16);
+    const uint32_t hi = static_cast<uint32_t>(float_to_bf16(acc[2])) | (static_cast<uint32_t>(float_to_bf16(acc[3])) << 16);
+    *reinterpret_cast<uint2*>(y + off) = make_uint2(lo, hi);
+}
+template <> __device__ __forceinline__ void store_out4<int8_t>(int8_t* y, long long off, i32x4 acc, float scale) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v |= static_cast<uint32_t>(static_cast<uint8_t>(requant_i8(acc[i], scale))) << (8 * i);
+    *reinterpret_cast<uint32_t*>(y + off) = v;
+}
+
 constexpr int kMaxUnitsPerThread = 8;
 
 // LDS byte offset of 16-byte slot j of patch pixel q.  The XOR with bits 1..2
@@ -160,14 +230,71 @@ constexpr int kMaxUnitsPerThread = 8;
 // same j) over all 32 banks.
 __device__ __forceinline__ int lds_slot(int q, int j) { return q * 64 + ((j ^ ((q >> 1) & 3)) << 4); }
 
-template <typename T, int XB, int WM, int WN, int FM, int FN>
+// ---- wide staging ("row blocks")
+// One 16-byte global load along W holds PP pixels of SZ bytes each: one
+// channel (NCHW, SZ = element size) or one channel block (NCHWX, SZ = x *
+// element size).  PP such loads cover PP pixels x 16 bytes of channels, which
+// is a PP x PP transpose of SZ-byte sub-elements into PP LDS slots.
+template <typename T, int XB> struct Wide {
+    static constexpr int ESZ = static_cast<int>(sizeof(T));
+    static constexpr int SZ = (XB == 1) ? ESZ : XB * ESZ;
+    static constexpr int PP = 16 / SZ;
+    static constexpr bool ok = (SZ == 2 || SZ == 4 || SZ == 8);
+    // units each thread may own: keeps the in-flight registers at 32 VGPRs
+    static constexpr int MAXU = ok ? (32 / (4 * PP) > 0 ? 32 / (4 * PP) : 1) : 1;
+};
+
+// Slot p of the transpose: 16 bytes = sub-element p of each of the PP loads.
+template <int SZ>
+__device__ __forceinline__ uint4 wide_pick(const uint4* ld, int p);
+template <>
+__device__ __forceinline__ uint4 wide_pick<2>(const uint4* ld, int p) {
+    // 8 loads x 8 16-bit pixels -> pixel p: 8 channels, 2 per dword
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 a = ld[2 * i], b = ld[2 * i + 1];
+        const uint32_t wa = (p >> 1) == 0 ? a.x : (p >> 1) == 1 ? a.y : (p >> 1) == 2 ? a.z : a.w;
+        const uint32_t wb = (p >> 1) == 0 ? b.x : (p >> 1) == 1 ? b.y : (p >> 1) == 2 ? b.z : b.w;
+        w[i] = (p & 1) ? ((wa >> 16) | (wb & 0xffff0000u)) : ((wa & 0xffffu) | (wb << 16));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+__device__ __forceinline__ uint4 wide_pick<4>(const uint4* ld, int p) {
+    auto word = [](const uint4& v, int i) { return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w; };
+    return make_uint4(word(ld[0], p), word(ld[1], p), word(ld[2], p), word(ld[3], p));
+}
+template <>
+__device__ __forceinline__ uint4 wide_pick<8>(const uint4* ld, int p) {
+    return p == 0 ? make_uint4(ld[0].x, ld[0].y, ld[1].x, ld[1].y) : make_uint4(ld[0].z, ld[0].w, ld[1].z, ld[1].w);
+}
+
+// Accumulator and operand types for one fragment size.
+template <typename T, int FR> struct Frag;
+template <typename T> struct Frag<T, 16> {
+    using acc_t = typename Mma<T>::acc_t;
+    static constexpr int NPIECE = 1;  // 16-byte pieces per lane per 64-byte chunk
+    static constexpr int NACC = 4;
+};
+template <typename T> struct Frag<T, 32> {
+    using acc_t = typename Mma32<T>::acc_t;
+    static constexpr int NPIECE = 2;
+    static constexpr int NACC = 16;
+};
+
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR>
 __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
-    constexpr int NT = WN * FN * 16;
+    constexpr int NT = WN * FN * FR;
     constexpr int E16 = 16 / static_cast<int>(sizeof(T));
     constexpr int CK = 4 * E16;
-    constexpr int MAXU = kMaxUnitsPerThread;
-    using acc_t = typename Mma<T>::acc_t;
+    using FT = Frag<T, FR>;
+    using acc_t = typename FT::acc_t;
+    constexpr int NP = FT::NPIECE;
+    using WD = Wide<T, XB>;
+    constexpr int MAXU = (STG == 1) ? WD::MAXU : kMaxUnitsPerThread;
+    constexpr int PP = (STG == 1) ? WD::PP : 1;
 
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
@@ -176,9 +303,27 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int wave = tid >> 6;
     const int wm = wave % WM;
     const int wn = wave / WM;
-    const int jl = lane >> 4;
+    const int lrow = lane % FR;  // A row / B column this lane feeds
+    const int lgrp = lane / FR;  // K group (FR=16: slot 0..3; FR=32: half 0..1)
 
-    int mt = blockIdx.x;
+    // ---- XCD-aware work order.  Workgroups are dispatched round-robin over
+    // the 8 XCDs; give each XCD a contiguous range of the linear tile order,
+    // in which the output-channel tiles of one pixel tile are adjacent (they
+    // share the input patch in that XCD's L2) and consecutive pixel tiles are
+    // spatial neighbours (they share halo rows).
+    int lin;
+    {
+        const int total = static_cast<int>(gridDim.x);
+        const int bid = static_cast<int>(blockIdx.x);
+        const int xcd = bid & 7, local = bid >> 3;
+        const int per = total >> 3, rem = total & 7;
+        lin = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+    }
+    const int kt = lin % a.ntk;
+    lin /= a.ntk;
+    const int ntm = a.tiles_w * a.tiles_h * a.tiles_n;
+    const int g = lin / ntm;
+    int mt = lin - g * ntm;
     const int tw_i = mt % a.tiles_w;
     mt /= a.tiles_w;
     const int th_i = mt % a.tiles_h;
@@ -186,8 +331,6 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int n0 = mt * a.TN;
     const int oh0 = th_i * a.TH;
     const int ow0 = tw_i * a.TW;
-    const int kt = blockIdx.y;
-    const int g = blockIdx.z;
     const int RS = a.R * a.S;
     const int PHW = a.PH * a.PW;
     const int thw = a.TH * a.TW;
@@ -198,29 +341,53 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const T* __restrict__ x = static_cast<const T*>(a.x);
 
     // ---- staging units owned by this thread (chunk-invariant parts)
-    const int nunits = 4 * a.npix;
-    int u_lds[MAXU];     // LDS byte offset (swizzled), -1 if no unit
-    int u_j[MAXU];       // 16-byte slot within the 64-byte channel chunk
-    int u_sp[MAXU];      // spatial offset ih*W+iw, -1 if outside the image
-    int u_n[MAXU];       // image
+    // STG 0: unit = one pixel x 16 bytes of channels (element gathers).
+    // STG 1: unit = PP pixels (one aligned column block) x 16 bytes of channels.
+    int u_q[MAXU];   // patch pixel of the unit's first pixel
+    int u_j[MAXU];   // 16-byte slot within the 64-byte channel chunk (-1: no unit)
+    int u_sp[MAXU];  // spatial offset ih*W + iw of the first pixel, -1 if outside
+    int u_n[MAXU];   // image
+    int u_pc[MAXU];  // patch column of the unit's first pixel (STG 1; may be < 0)
+    int ncb = 1, cb0 = 0;
+    if (STG == 1) {
+        cb0 = (iw0 >= 0) ? iw0 / PP : -((-iw0 + PP - 1) / PP);
+        const int last = iw0 + a.PW - 1;
+        const int cb1 = (last >= 0) ? last / PP : -((-last + PP - 1) / PP);
+        ncb = cb1 - cb0 + 1;
+    }
+    const int nrows = a.TN * a.PH;
+    const int nunits = (STG == 1) ? 4 * nrows * ncb : 4 * a.npix;
 #pragma unroll
     for (int i = 0; i < MAXU; ++i) {
         const int u = tid + i * NTHR;
-        u_lds[i] = -1;
-        u_j[i] = 0;
+        u_q[i] = 0;
+        u_j[i] = -1;
         u_sp[i] = -1;
         u_n[i] = 0;
+        u_pc[i] = 0;
         if (u < nunits) {
-            const int j = u / a.npix;
-            const int q = u - j * a.npix;
-            const int tn = q / PHW;
-            const int rem = q - tn * PHW;
-            const int prow = rem / a.PW;
-            const int pcol = rem - prow * a.PW;
+            int j, tn, prow, pcol;
+            if (STG == 1) {
+                const int cb = u % ncb;
+                const int t = u / ncb;
+                const int row = t % nrows;
+                j = t / nrows;
+                tn = row / a.PH;
+                prow = row - tn * a.PH;
+                pcol = (cb0 + cb) * PP - iw0;
+            } else {
+                j = u / a.npix;
+                const int q = u - j * a.npix;
+                tn = q / PHW;
+                const int rem = q - tn * PHW;
+                prow = rem / a.PW;
+                pcol = rem - prow * a.PW;
+            }
             const int n = n0 + tn;
             const int ih = ih0 + prow;
             const int iw = iw0 + pcol;
-            u_lds[i] = lds_slot(q, j);
+            u_q[i] = (tn * a.PH + prow) * a.PW + pcol;
+            u_pc[i] = pcol;
             u_j[i] = j;
             u_n[i] = n;
             if (n < a.N && static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) &&
@@ -229,32 +396,60 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         }
     }
 
-    uint4 stg[MAXU];
+    uint4 stg[MAXU][PP];
     auto stage_load = [&](int chunk) {
 #pragma unroll
         for (int i = 0; i < MAXU; ++i) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (u_sp[i] >= 0) {
-                const int cl = chunk * CK + u_j[i] * E16;
-                const int nval = a.Cg - cl;
-                if (nval > 0)
-                    v = load_unit<T, XB>(x + u_n[i] * a.x_img, a.H, a.W, g * a.Cg + cl, nval, u_sp[i]);
+#pragma unroll
+            for (int l = 0; l < PP; ++l) stg[i][l] = make_uint4(0, 0, 0, 0);
+            if (u_sp[i] < 0) continue;
+            const int cl = chunk * CK + u_j[i] * E16;
+            const int nval = a.Cg - cl;
+            if (nval <= 0) continue;
+            const int c0 = g * a.Cg + cl;
+            const T* xn = x + u_n[i] * a.x_img;
+            if (STG == 1) {
+                using R = typename Raw<T>::type;
+                const R* xr = reinterpret_cast<const R*>(xn);
+                const long long HW = static_cast<long long>(a.H) * a.W;
+#pragma unroll
+                for (int l = 0; l < PP; ++l) {
+                    if (XB == 1) {
+                        if (l < nval)
+                            stg[i][l] = *reinterpret_cast<const uint4*>(xr + (c0 + l) * HW + u_sp[i]);
+                    } else {
+                        if (l * XB < nval)
+                            stg[i][l] = *reinterpret_cast<const uint4*>(xr + ((c0 / XB + l) * HW + u_sp[i]) * XB);
+                    }
+                }
+            } else {
+                stg[i][0] = load_unit<T, XB>(xn, a.H, a.W, c0, nval, u_sp[i]);
             }
-            stg[i] = v;
         }
     };
     auto stage_store = [&](int buf) {
         uint8_t* base = lds + buf * patch_bytes;
 #pragma unroll
-        for (int i = 0; i < MAXU; ++i)
-            if (u_lds[i] >= 0) *reinterpret_cast<uint4*>(base + u_lds[i]) = stg[i];
+        for (int i = 0; i < MAXU; ++i) {
+            if (u_j[i] < 0) continue;
+            if (STG == 1) {
+#pragma unroll
+                for (int p = 0; p < PP; ++p) {
+                    const int col = u_pc[i] + p;
+                    if (col < 0 || col >= a.PW) continue;  // outside this patch row
+                    *reinterpret_cast<uint4*>(base + lds_slot(u_q[i] + p, u_j[i])) = wide_pick<WD::SZ>(stg[i], p);
+                }
+            } else {
+                *reinterpret_cast<uint4*>(base + lds_slot(u_q[i], u_j[i])) = stg[i][0];
+            }
+        }
     };
 
     // ---- per-lane A fragment bases (pixel index inside the patch)
     int qbase[FM];
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-        const int p = (wm * FM + f) * 16 + (lane & 15);
+        const int p = (wm * FM + f) * FR + lrow;
         int qb = 0;
         if (p < tile_pix) {
             const int tn = p / thw;
@@ -265,85 +460,204 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         }
         qbase[f] = qb;
     }
-
-    // ---- B (prepared weights) addressing
-    const uint8_t* __restrict__ wtile =
-        static_cast<const uint8_t*>(a.wp) +
-        static_cast<long long>(g * a.ntk + kt) * a.nchunks * RS * NT * 64 +
-        static_cast<long long>(wn * FN * 16 + (lane & 15)) * 64 + jl * 16;
-    auto load_b = [&](uint4* b, int it) {
-        const uint8_t* p = wtile + static_cast<long long>(it) * NT * 64;
+    // 16-byte slots this lane reads for its pieces
+    int pslot[NP];
 #pragma unroll
-        for (int nf = 0; nf < FN; ++nf) b[nf] = *reinterpret_cast<const uint4*>(p + nf * 16 * 64);
+    for (int i = 0; i < NP; ++i) pslot[i] = (FR == 16) ? lgrp : piece_slot<T>(i, lgrp);
+
+    // ---- B (prepared weights).  One tap of one output-channel tile is NT rows
+    // of 64 bytes, laid out so that each fragment piece is 1 KB contiguous:
+    // FR=16: [NT][64 B] (lane reads row lrow, slot lgrp);
+    // FR=32: [NT/32][piece][32 rows][half][16 B].
+    const uint8_t* __restrict__ wtile =
+        static_cast<const uint8_t*>(a.wp) + static_cast<long long>(g * a.ntk + kt) * a.nchunks * RS * NT * 64;
+    const int boff = (FR == 16) ? (wn * FN * 16 + lrow) * 64 + lgrp * 16 : (wn * FN * 2 * 32 + lrow) * 32 + lgrp * 16;
+    auto load_b = [&](uint4 (*b)[NP], int it) {
+        const uint8_t* p = wtile + static_cast<long long>(it) * NT * 64 + boff;
+#pragma unroll
+        for (int nf = 0; nf < FN; ++nf)
+#pragma unroll
+            for (int i = 0; i < NP; ++i)
+                b[nf][i] = *reinterpret_cast<const uint4*>(p + (FR == 16 ? nf * 1024 : (nf * 2 + i) * 1024));
+    };
+    auto load_a = [&](uint4 (*af)[NP], const uint8_t* pb, int toff) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            const int q = qbase[f] + toff;
+#pragma unroll
+            for (int i = 0; i < NP; ++i) af[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, pslot[i]));
+        }
     };
 
     acc_t acc[FM][FN];
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
-        for (int nf = 0; nf < FN; ++nf) acc[f][nf] = acc_t{0, 0, 0, 0};
+        for (int nf = 0; nf < FN; ++nf) acc[f][nf] = acc_t{};
 
+    auto mma = [&](uint4 (*af)[NP], uint4 (*bf)[NP]) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int nf = 0; nf < FN; ++nf) {
+                if constexpr (FR == 16)
+                    Mma<T>::run(acc[f][nf], af[f][0], bf[nf][0]);
+                else
+                    Mma32<T>::run(acc[f][nf], af[f][0], af[f][1], bf[nf][0], bf[nf][1]);
+            }
+    };
+
+    uint4 bcur[FN][NP], bnxt[FN][NP];
+    load_b(bcur, 0);
     stage_load(0);
     stage_store(0);
     __syncthreads();
 
-    uint4 bcur[FN], bnxt[FN];
-    load_b(bcur, 0);
     const int total_it = a.nchunks * RS;
     int it = 0;
-    for (int chunk = 0; chunk < a.nchunks; ++chunk) {
-        const int buf = chunk & 1;
-        const bool more = chunk + 1 < a.nchunks;
-        if (more) stage_load(chunk + 1);
-        const uint8_t* pb = lds + buf * patch_bytes;
-        int r = 0, s = 0;
-        for (int rs = 0; rs < RS; ++rs, ++it) {
-            if (it + 1 < total_it) load_b(bnxt, it + 1);
-            const int toff = r * a.dh * a.PW + s * a.dw;
-            uint4 afr[FM];
+    if constexpr (FR == 32) {
+        // 32x32 fragments run one wave per SIMD and are software-pipelined
+        // by hand, with a branch-free tap body:
+        //  * A is a rolling single buffer: once fragment f's MFMAs of this
+        //    tap are issued, its registers are refilled from LDS with
+        //    fragment f of the next tap (at a chunk's last tap, the same tap
+        //    again: harmless), which then has FM-1 fragments of MFMAs to land;
+        //  * B (weights, from L2) is prefetched two taps ahead, so the next
+        //    chunk's staging loads -- issued at the chunk start, behind the
+        //    weights of its first two taps -- are not waited for until the
+        //    third tap.
+        uint4 ra[FM][NP];
+        uint4 b2[FN][NP];
+        auto read_a = [&](const uint8_t* pb, int toff) {
 #pragma unroll
             for (int f = 0; f < FM; ++f) {
                 const int q = qbase[f] + toff;
-                afr[f] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, jl));
+#pragma unroll
+                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, pslot[i]));
             }
+        };
+        load_b(bnxt, total_it > 1 ? 1 : 0);
+        read_a(lds, 0);
+        const int last_it = total_it - 1;
+        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+            const int buf = chunk & 1;
+            const bool more = chunk + 1 < a.nchunks;
+            const uint8_t* pb = lds + buf * patch_bytes;
+            if (more) stage_load(chunk + 1);
+            int r = 0, s = 0;
+            for (int rs = 0; rs < RS; ++rs, ++it) {
+                load_b(b2, min(it + 2, last_it));
+                // offset of the next tap within this chunk (this tap at the end)
+                int rn = r, sn = s + 1;
+                if (sn == a.S) {
+                    sn = 0;
+                    ++rn;
+                }
+                const bool has_next = rs + 1 < RS;
+                const int toff_next = has_next ? rn * a.dh * a.PW + sn * a.dw : r * a.dh * a.PW + s * a.dw;
 #pragma unroll
-            for (int f = 0; f < FM; ++f)
+                for (int f = 0; f < FM; ++f) {
 #pragma unroll
-                for (int nf = 0; nf < FN; ++nf) Mma<T>::run(acc[f][nf], afr[f], bcur[nf]);
+                    for (int nf = 0; nf < FN; ++nf)
+                        Mma32<T>::run(acc[f][nf], ra[f][0], ra[f][1], bcur[nf][0], bcur[nf][1]);
+                    const int q = qbase[f] + toff_next;
 #pragma unroll
-            for (int nf = 0; nf < FN; ++nf) bcur[nf] = bnxt[nf];
-            if (++s == a.S) {
-                s = 0;
-                ++r;
+                    for (int i = 0; i < NP; ++i)
+                        ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, pslot[i]));
+                }
+#pragma unroll
+                for (int nf = 0; nf < FN; ++nf)
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) {
+                        bcur[nf][i] = bnxt[nf][i];
+                        bnxt[nf][i] = b2[nf][i];
+                    }
+                if (has_next) {
+                    r = rn;
+                    s = sn;
+                }
             }
+            if (more) stage_store(buf ^ 1);
+            __syncthreads();
+            if (more) read_a(lds + (buf ^ 1) * patch_bytes, 0);
         }
-        if (more) stage_store(buf ^ 1);
-        __syncthreads();
+    } else {
+        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+            const int buf = chunk & 1;
+            const bool more = chunk + 1 < a.nchunks;
+            const uint8_t* pb = lds + buf * patch_bytes;
+            if (more) stage_load(chunk + 1);
+            int r = 0, s = 0;
+            for (int rs = 0; rs < RS; ++rs, ++it) {
+                if (it + 1 < total_it) load_b(bnxt, it + 1);
+                uint4 afr[FM][NP];
+                load_a(afr, pb, r * a.dh * a.PW + s * a.dw);
+                mma(afr, bcur);
+#pragma unroll
+                for (int nf = 0; nf < FN; ++nf) bcur[nf][0] = bnxt[nf][0];
+                if (++s == a.S) {
+                    s = 0;
+                    ++r;
+                }
+            }
+            if (more) stage_store(buf ^ 1);
+            __syncthreads();
+        }
     }
 
-    // ---- epilogue: convert and store in the caller's layout
+    // ---- epilogue: convert and store in the caller's layout.  The patch
+    // buffers are free now (the last chunk ended with a barrier); they hold a
+    // table of each tile pixel's output offset (without the channel term),
+    // -1 for pixels outside the output, so the per-element index arithmetic
+    // is one LDS read and an add.
+    long long* otab = reinterpret_cast<long long*>(lds);
+    constexpr int TP = WM * FM * FR;  // pixel rows of the register tiles
+    for (int p = tid; p < TP; p += NTHR) {
+        long long o = -1;
+        if (p < tile_pix) {
+            const int tn = p / thw;
+            const int rem = p - tn * thw;
+            const int ohl = rem / a.TW;
+            const int owl = rem - ohl * a.TW;
+            const int n = n0 + tn;
+            const int oh = oh0 + ohl;
+            const int ow = ow0 + owl;
+            if (n < a.N && oh < a.OH && ow < a.OW)
+                o = n * a.y_img + static_cast<long long>(oh * a.OW + ow) * XB;
+        }
+        otab[p] = o;
+    }
+    __syncthreads();
     T* __restrict__ y = static_cast<T*>(a.y);
+    const bool vec4 = (XB == 1) && (a.TW % 4 == 0) && (a.OW % 4 == 0);
+    const long long OHW = static_cast<long long>(a.OH) * a.OW;
+    constexpr int NG = FT::NACC / 4;  // groups of 4 consecutive rows per accumulator
 #pragma unroll
     for (int nf = 0; nf < FN; ++nf) {
-        const int kl = kt * NT + (wn * FN + nf) * 16 + (lane & 15);
+        const int kl = kt * NT + (wn * FN + nf) * FR + lrow;
         if (kl >= a.Kg) continue;
         const int k = g * a.Kg + kl;
         const float sc = (a.scale != nullptr) ? a.scale[k] : 1.0f;
+        const long long coff = (XB == 1) ? k * OHW : (k / XB) * OHW * XB + (k % XB);
 #pragma unroll
         for (int f = 0; f < FM; ++f) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int p = (wm * FM + f) * 16 + 4 * jl + v;
-                if (p >= tile_pix) continue;
-                const int tn = p / thw;
-                const int rem = p - tn * thw;
-                const int ohl = rem / a.TW;
-                const int owl = rem - ohl * a.TW;
-                const int n = n0 + tn;
-                const int oh = oh0 + ohl;
-                const int ow = ow0 + owl;
-                if (n >= a.N || oh >= a.OH || ow >= a.OW) continue;
-                store_out<T>(y, n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW), acc[f][nf], v, sc);
+            for (int grp = 0; grp < NG; ++grp) {
+                // rows of this group: FR=16: 4*lgrp + v; FR=32: 8*grp + 4*lgrp + v
+                const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
+                typename Mma<T>::acc_t quad;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) quad[v] = acc[f][nf][grp * 4 + v];
+                if (vec4) {
+                    const long long o = otab[p0];
+                    if (o >= 0) store_out4<T>(y, o + coff, quad, sc);
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const long long o = otab[p0 + v];
+                        if (o >= 0) store_out<T>(y, o + coff, quad, v, sc);
+                    }
+                }
             }
         }
     }
@@ -374,31 +688,75 @@ __global__ __launch_bounds__(256) void igemm_prepare_kernel(const T* __restrict_
     }
 }
 
+// Weight preparation for 32x32 fragments: per tap of one output-channel tile,
+// [NT/32][piece][32 rows][half][16 B], piece/half content = slot
+// piece_slot(piece, half) of the row's 64-byte channel chunk, zero padded.
+template <typename T, int NT>
+__global__ __launch_bounds__(256) void igemm_prepare32_kernel(const T* __restrict__ w, T* __restrict__ wp, int G,
+                                                              int Kg, int Cg, int RS, int ntk, int nchunks) {
+    constexpr int E16 = 16 / static_cast<int>(sizeof(T));
+    constexpr int CK = 4 * E16;
+    using R = typename Raw<T>::type;
+    const long long total = static_cast<long long>(G) * ntk * nchunks * RS * NT * CK;
+    const R* wr = reinterpret_cast<const R*>(w);
+    R* out = reinterpret_cast<R*>(wp);
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < total; i += static_cast<long long>(gridDim.x) * 256) {
+        long long t = i;
+        const int e = static_cast<int>(t % E16); t /= E16;
+        const int half = static_cast<int>(t % 2); t /= 2;
+        const int row = static_cast<int>(t % 32); t /= 32;
+        const int piece = static_cast<int>(t % 2); t /= 2;
+        const int nfr = static_cast<int>(t % (NT / 32)); t /= (NT / 32);
+        const int rs = static_cast<int>(t % RS); t /= RS;
+        const int chunk = static_cast<int>(t % nchunks); t /= nchunks;
+        const int kt = static_cast<int>(t % ntk); t /= ntk;
+        const int g = static_cast<int>(t);
+        const int kl = kt * NT + nfr * 32 + row;
+        const int cl = chunk * CK + piece_slot<T>(piece, half) * E16 + e;
+        R v = 0;
+        if (kl < Kg && cl < Cg) v = wr[(static_cast<long long>(g * Kg + kl) * Cg + cl) * RS + rs];
+        out[i] = v;
+    }
+}
+
 // ---------------------------------------------------------------- host side
 
 struct Cfg {
-    int wm, wn, fm, fn;
+    int wm, wn, fm, fn, fr;
     int threads() const { return wm * wn * 64; }
-    int pixels() const { return wm * fm * 16; }
-    int nt() const { return wn * fn * 16; }
+    int pixels() const { return wm * fm * fr; }
+    int nt() const { return wn * fn * fr; }
 };
 
 // Tile configurations, in config-id order.
+// fr = 16: 16x16 fragments, two or more waves per SIMD.
+// fr = 32: 32x32 fragments, big per-wave register tiles, one wave per SIMD.
 constexpr Cfg kCfgs[] = {
-    {2, 2, 4, 4},  // 0: 128 px x 128 ch
-    {2, 2, 7, 4},  // 1: 224 px x 128 ch
-    {2, 2, 4, 2},  // 2: 128 px x  64 ch
-    {2, 2, 2, 2},  // 3:  64 px x  64 ch
-    {4, 1, 2, 4},  // 4: 128 px x  64 ch
-    {2, 2, 7, 2},  // 5: 224 px x  64 ch
-    {2, 2, 2, 4},  // 6:  64 px x 128 ch
+    {2, 2, 4, 4, 16},  // 0: 128 px x 128 ch
+    {2, 2, 7, 4, 16},  // 1: 224 px x 128 ch
+    {2, 2, 4, 2, 16},  // 2: 128 px x  64 ch
+    {2, 2, 2, 2, 16},  // 3:  64 px x  64 ch
+    {4, 1, 2, 4, 16},  // 4: 128 px x  64 ch
+    {2, 2, 7, 2, 16},  // 5: 224 px x  64 ch
+    {2, 2, 2, 4, 16},  // 6:  64 px x 128 ch
+    {1, 4, 7, 2, 32},  // 7: 224 px x 256 ch
+    {2, 2, 7, 2, 32},  // 8: 448 px x 128 ch
+    {1, 4, 4, 2, 32},  // 9: 128 px x 256 ch
+    {2, 2, 4, 2, 32},  // 10: 256 px x 128 ch
+    {2, 2, 2, 2, 32},  // 11: 128 px x 128 ch
+    {1, 4, 4, 1, 32},  // 12: 128 px x 128 ch
+    {2, 2, 4, 1, 32},  // 13: 256 px x  64 ch
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 struct Geo {
     int TN, TH, TW, PH, PW, npix, tiles_n, tiles_h, tiles_w, nchunks, ntk;
+    int stg;  // 0: per-pixel gathers, 1: wide row-block loads
     size_t lds_bytes;
 };
+
+// Bytes per pixel sub-element of one 16-byte load along W (see Wide<>).
+inline int wide_sz(const Prob& p) { return p.xb == 1 ? p.esize : p.xb * p.esize; }
 
 inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     const int P = c.pixels();
@@ -447,9 +805,22 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     g->tiles_w = (p.ow + g->TW - 1) / g->TW;
     g->nchunks = (p.cg + CK - 1) / CK;
     g->ntk = (p.kg + c.nt() - 1) / c.nt();
-    g->lds_bytes = 2 * static_cast<size_t>(g->npix) * 64;
-    if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w > 0x7fffffffLL || g->ntk > 65535 ||
-        p.g > 65535) {
+    // two patch buffers; the epilogue reuses them for an 8-byte offset per
+    // register-tile pixel row
+    g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * 64, static_cast<size_t>(c.pixels()) * 8);
+    g->stg = 0;
+    {
+        const int sz = wide_sz(p);
+        if (sz == 2 || sz == 4 || sz == 8) {
+            const int pp = 16 / sz;
+            const int maxu = std::max(1, 32 / (4 * pp));
+            const long long ncb = (g->PW + pp - 1) / pp + 1;
+            const long long units = 4LL * g->TN * g->PH * ncb;
+            const bool chan_ok = (p.xb == 1) || (p.cg % p.xb == 0);
+            if (p.w % pp == 0 && chan_ok && units <= static_cast<long long>(maxu) * c.threads()) g->stg = 1;
+        }
+    }
+    if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk * p.g > 0x7fffffffLL) {
         if (why) *why = "implicit GEMM: grid too large";
         return false;
     }
@@ -460,7 +831,7 @@ inline size_t filter_bytes(const Prob& p, const Cfg& c, const Geo& g) {
     return static_cast<size_t>(p.g) * g.ntk * g.nchunks * p.r * p.s * c.nt() * 64;
 }
 
-template <typename T, int XB, int WM, int WN, int FM, int FN>
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR>
 cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
                        hipStream_t st) {
     Args a;
@@ -473,9 +844,9 @@ cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* w
     a.sh = p.sh; a.sw = p.sw; a.ph = p.ph; a.pw = p.pw; a.dh = p.dh; a.dw = p.dw;
     a.x_img = p.x_img; a.y_img = p.y_img;
     a.TN = g.TN; a.TH = g.TH; a.TW = g.TW; a.PH = g.PH; a.PW = g.PW; a.npix = g.npix;
-    a.tiles_w = g.tiles_w; a.tiles_h = g.tiles_h;
+    a.tiles_w = g.tiles_w; a.tiles_h = g.tiles_h; a.tiles_n = g.tiles_n;
     a.nchunks = g.nchunks; a.ntk = g.ntk;
-    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN>;
+    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR>;
     static bool attr_done = false;
     if (g.lds_bytes > 65536 && !attr_done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -483,8 +854,7 @@ cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* w
         if (e != hipSuccess) return check_hip(e, "hipFuncSetAttribute(igemm)");
         attr_done = true;
     }
-    const dim3 grid(static_cast<unsigned>(g.tiles_n * g.tiles_h * g.tiles_w), static_cast<unsigned>(g.ntk),
-                    static_cast<unsigned>(p.g));
+    const dim3 grid(static_cast<unsigned>(static_cast<long long>(g.tiles_n) * g.tiles_h * g.tiles_w * g.ntk * p.g));
     kern<<<grid, WM * WN * 64, g.lds_bytes, st>>>(a);
     return check_hip(hipGetLastError(), "igemm_kernel launch");
 }
@@ -493,10 +863,14 @@ template <typename T, int XB>
 cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale,
                        void* y, hipStream_t st) {
     switch (cfg) {
-#define CFWD_IG_CFG(ID)                                                                                     \
-    case ID:                                                                                                \
-        return launch_one<T, XB, kCfgs[ID].wm, kCfgs[ID].wn, kCfgs[ID].fm, kCfgs[ID].fn>(p, g, x, wp, scale, y, \
-                                                                                          st);
+#define CFWD_IG_CFG(ID)                                                                                  \
+    case ID: {                                                                                           \
+        constexpr Cfg c = kCfgs[ID];                                                                     \
+        if constexpr (Wide<T, XB>::ok)                                                                   \
+            if (g.stg == 1)                                                                              \
+                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr>(p, g, x, wp, scale, y, st);    \
+        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr>(p, g, x, wp, scale, y, st);            \
+    }
         CFWD_IG_CFG(0)
         CFWD_IG_CFG(1)
         CFWD_IG_CFG(2)
@@ -504,6 +878,13 @@ cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, cons
         CFWD_IG_CFG(4)
         CFWD_IG_CFG(5)
         CFWD_IG_CFG(6)
+        CFWD_IG_CFG(7)
+        CFWD_IG_CFG(8)
+        CFWD_IG_CFG(9)
+        CFWD_IG_CFG(10)
+        CFWD_IG_CFG(11)
+        CFWD_IG_CFG(12)
+        CFWD_IG_CFG(13)
 #undef CFWD_IG_CFG
         default:
             return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM: no such config");
@@ -528,14 +909,27 @@ cfwd_status prepare_dtype(int cfg, const Prob& p, const Geo& g, const void* w, v
     long long blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     const int nt = kCfgs[cfg].nt();
-    if (nt == 128)
-        igemm_prepare_kernel<T, 128><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
-            static_cast<const T*>(w), static_cast<T*>(wp), p.g, p.kg, p.cg, p.r * p.s, g.ntk, g.nchunks);
-    else if (nt == 64)
-        igemm_prepare_kernel<T, 64><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
-            static_cast<const T*>(w), static_cast<T*>(wp), p.g, p.kg, p.cg, p.r * p.s, g.ntk, g.nchunks);
-    else
-        return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM: unexpected N tile");
+    const unsigned nb = static_cast<unsigned>(blocks);
+    const T* wi = static_cast<const T*>(w);
+    T* wo = static_cast<T*>(wp);
+    const int rs = p.r * p.s;
+    if (kCfgs[cfg].fr == 16) {
+        if (nt == 128)
+            igemm_prepare_kernel<T, 128><<<nb, 256, 0, st>>>(wi, wo, p.g, p.kg, p.cg, rs, g.ntk, g.nchunks);
+        else if (nt == 64)
+            igemm_prepare_kernel<T, 64><<<nb, 256, 0, st>>>(wi, wo, p.g, p.kg, p.cg, rs, g.ntk, g.nchunks);
+        else
+            return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM: unexpected N tile");
+    } else {
+        if (nt == 256)
+            igemm_prepare32_kernel<T, 256><<<nb, 256, 0, st>>>(wi, wo, p.g, p.kg, p.cg, rs, g.ntk, g.nchunks);
+        else if (nt == 128)
+            igemm_prepare32_kernel<T, 128><<<nb, 256, 0, st>>>(wi, wo, p.g, p.kg, p.cg, rs, g.ntk, g.nchunks);
+        else if (nt == 64)
+            igemm_prepare32_kernel<T, 64><<<nb, 256, 0, st>>>(wi, wo, p.g, p.kg, p.cg, rs, g.ntk, g.nchunks);
+        else
+            return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM: unexpected N tile");
+    }
     return check_hip(hipGetLastError(), "igemm_prepare launch");
 }
 
