@@ -90,6 +90,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
 template <> struct Mma32<bf16_t> {
     using acc_t = f32x16;
+    static __device__ __forceinline__ void piece(acc_t& c, const uint4& a, const uint4& b, int) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                    0, 0);
+    }
     static __device__ __forceinline__ void run(acc_t& c, const uint4& a0, const uint4& a1, const uint4& b0,
                                                const uint4& b1) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a0), __builtin_bit_cast(bf16x8, b0), c,
@@ -100,6 +104,9 @@ template <> struct Mma32<bf16_t> {
 };
 template <> struct Mma32<int8_t> {
     using acc_t = i32x16;
+    static __device__ __forceinline__ void piece(acc_t& c, const uint4& a, const uint4& b, int) {
+        c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+    }
     static __device__ __forceinline__ void run(acc_t& c, const uint4& a0, const uint4& a1, const uint4& b0,
                                                const uint4& b1) {
         c = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a0), __builtin_bit_cast(i32x4, b0), c, 0,
@@ -110,6 +117,12 @@ template <> struct Mma32<int8_t> {
 };
 template <> struct Mma32<float> {
     using acc_t = f32x16;
+    static __device__ __forceinline__ void piece(acc_t& c, const uint4& a, const uint4& b, int) {
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    }
     static __device__ __forceinline__ void run(acc_t& c, const uint4& a0, const uint4& a1, const uint4& b0,
                                                const uint4& b1) {
         const uint32_t av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
@@ -225,10 +238,22 @@ template <> __device__ __forceinline__ void store_out4<int8_t>(int8_t* y, long l
 
 constexpr int kMaxUnitsPerThread = 8;
 
-// LDS byte offset of 16-byte slot j of patch pixel q.  The XOR with bits 1..2
-// of q spreads the 8 lanes of one ds_read_b128 phase (consecutive pixels,
-// same j) over all 32 banks.
-__device__ __forceinline__ int lds_slot(int q, int j) { return q * 64 + ((j ^ ((q >> 1) & 3)) << 4); }
+// LDS byte offset of 16-byte slot j of patch pixel q.  The slot is XORed with
+// two bits of q so that the lanes of one ds_read_b128 (consecutive pixels,
+// same slot) spread over all banks.  Which two bits depends on how many
+// consecutive pixels one read covers: measured on gfx950, bits 1..2 are
+// conflict-free for 16-pixel fragments and bits 2..3 for 32-pixel ones (the
+// q>>1 form costs about 30% of LDS throughput there).
+//
+// 32-pixel fragments instead pad each pixel to 80 bytes (also measured
+// conflict-free), which keeps the address linear in the pixel index: a filter
+// tap is then a uniform offset added to a per-fragment base.
+template <int FR> struct PatchStride { static constexpr int value = (FR == 32) ? 80 : 64; };
+template <int FR>
+__device__ __forceinline__ int lds_slot(int q, int j) {
+    if constexpr (FR == 32) return q * 80 + j * 16;
+    return q * 64 + ((j ^ ((q >> 1) & 3)) << 4);
+}
 
 // ---- wide staging ("row blocks")
 // One 16-byte global load along W holds PP pixels of SZ bytes each: one
@@ -283,7 +308,7 @@ template <typename T> struct Frag<T, 32> {
     static constexpr int NACC = 16;
 };
 
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR>
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV>
 __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
     constexpr int NT = WN * FN * FR;
@@ -335,7 +360,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int PHW = a.PH * a.PW;
     const int thw = a.TH * a.TW;
     const int tile_pix = a.TN * thw;
-    const int patch_bytes = a.npix * 64;
+    const int patch_bytes = a.npix * PatchStride<FR>::value;
     const int ih0 = oh0 * a.sh - a.ph;
     const int iw0 = ow0 * a.sw - a.pw;
     const T* __restrict__ x = static_cast<const T*>(a.x);
@@ -437,12 +462,30 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 for (int p = 0; p < PP; ++p) {
                     const int col = u_pc[i] + p;
                     if (col < 0 || col >= a.PW) continue;  // outside this patch row
-                    *reinterpret_cast<uint4*>(base + lds_slot(u_q[i] + p, u_j[i])) = wide_pick<WD::SZ>(stg[i], p);
+                    *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i] + p, u_j[i])) = wide_pick<WD::SZ>(stg[i], p);
                 }
             } else {
-                *reinterpret_cast<uint4*>(base + lds_slot(u_q[i], u_j[i])) = stg[i][0];
+                *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i], u_j[i])) = stg[i][0];
             }
         }
+    };
+
+    // Branch-free staging of one 16-byte load, index l = unit * PP + load,
+    // for chunk `chunk` (wide staging only).  Invalid pixels or channels load
+    // from the tensor base and are zeroed afterwards, so every call issues
+    // exactly one load and the compiler can count outstanding loads exactly.
+    auto stage_piece = [&](int chunk, int l) {
+        using R = typename Raw<T>::type;
+        const int i = l / PP, ld = l % PP;
+        const int cl = chunk * CK + (u_j[i] < 0 ? 0 : u_j[i]) * E16;
+        const int nval = a.Cg - cl;
+        const bool valid = (u_sp[i] >= 0) && (XB == 1 ? ld < nval : ld * XB < nval);
+        const int c0 = g * a.Cg + cl;
+        const long long HW = static_cast<long long>(a.H) * a.W;
+        const long long off = (XB == 1) ? (c0 + ld) * HW + u_sp[i] : ((c0 / XB + ld) * HW + u_sp[i]) * XB;
+        const R* src = reinterpret_cast<const R*>(x) + (valid ? u_n[i] * a.x_img + off : 0);
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        stg[i][ld] = valid ? v : make_uint4(0, 0, 0, 0);
     };
 
     // ---- per-lane A fragment bases (pixel index inside the patch)
@@ -485,7 +528,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         for (int f = 0; f < FM; ++f) {
             const int q = qbase[f] + toff;
 #pragma unroll
-            for (int i = 0; i < NP; ++i) af[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, pslot[i]));
+            for (int i = 0; i < NP; ++i) af[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot<FR>(q, pslot[i]));
         }
     };
 
@@ -508,14 +551,73 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     };
 
     uint4 bcur[FN][NP], bnxt[FN][NP];
-    load_b(bcur, 0);
+    if constexpr (RSV != 9) load_b(bcur, 0);
     stage_load(0);
     stage_store(0);
     __syncthreads();
 
     const int total_it = a.nchunks * RS;
     int it = 0;
-    if constexpr (FR == 32) {
+    if constexpr (RSV == 9) {
+        // 3x3 (nine-tap) filters, 32x32 fragments, wide staging: the nine taps
+        // of a chunk are unrolled so that every register buffer is addressed
+        // at compile time (a copy between prefetch buffers would make the
+        // compiler wait for the load behind it):
+        //  * weights: a ring of three tap buffers, tap t+2 requested at tap t;
+        //  * activations of the next chunk: the eight 16-byte loads of this
+        //    thread, one per tap, each issued after that tap's weight request,
+        //    so that no weight wait ever waits for an activation load;
+        //  * A: rolling single buffer refilled right after each use.
+        static_assert(FR == 32 && STG == 1 && MAXU * PP == 8, "nine-tap path needs 32x32 tiles and wide staging");
+        uint4 ring[3][FN][NP];
+        uint4 ra[FM][NP];
+        // byte offsets: tap (uniform) and fragment base (per lane); piece i of
+        // a fragment is a further i * PSTEP bytes (piece_slot is 2i + h for
+        // 16-bit / 8-bit types and 2h + i for fp32)
+        constexpr int PS = PatchStride<FR>::value;
+        constexpr int PSTEP = (sizeof(T) == 4) ? 16 : 32;
+        int toffs[9];
+#pragma unroll
+        for (int t = 0; t < 9; ++t) toffs[t] = ((t / a.S) * a.dh * a.PW + (t % a.S) * a.dw) * PS;
+        int abase[FM];
+#pragma unroll
+        for (int f = 0; f < FM; ++f) abase[f] = qbase[f] * PS + pslot[0] * 16;
+        const int last_it = total_it - 1;
+        load_b(ring[0], 0);
+        load_b(ring[1], min(1, last_it));
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(lds + abase[f] + i * PSTEP);
+        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+            const int buf = chunk & 1;
+            const uint8_t* pb = lds + buf * patch_bytes;
+            const int it0 = chunk * 9;
+#pragma unroll
+            for (int t = 0; t < 9; ++t) {
+                load_b(ring[(t + 2) % 3], min(it0 + t + 2, last_it));
+                if (t < 8) stage_piece(chunk + 1, t);
+                const uint8_t* pt = pb + toffs[t < 8 ? t + 1 : 8];
+#pragma unroll
+                for (int i = 0; i < NP; ++i) {
+#pragma unroll
+                    for (int f = 0; f < FM; ++f) {
+#pragma unroll
+                        for (int nf = 0; nf < FN; ++nf) Mma32<T>::piece(acc[f][nf], ra[f][i], ring[t % 3][nf][i], i);
+                        ra[f][i] = *reinterpret_cast<const uint4*>(pt + abase[f] + i * PSTEP);
+                    }
+                }
+            }
+            stage_store(buf ^ 1);
+            __syncthreads();
+            const uint8_t* pn = lds + (buf ^ 1) * patch_bytes;
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pn + abase[f] + i * PSTEP);
+        }
+        it = total_it;
+    } else if constexpr (FR == 32) {
         // 32x32 fragments run one wave per SIMD and are software-pipelined
         // by hand, with a branch-free tap body:
         //  * A is a rolling single buffer: once fragment f's MFMAs of this
@@ -533,7 +635,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             for (int f = 0; f < FM; ++f) {
                 const int q = qbase[f] + toff;
 #pragma unroll
-                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, pslot[i]));
+                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot<FR>(q, pslot[i]));
             }
         };
         load_b(bnxt, total_it > 1 ? 1 : 0);
@@ -555,15 +657,21 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 }
                 const bool has_next = rs + 1 < RS;
                 const int toff_next = has_next ? rn * a.dh * a.PW + sn * a.dw : r * a.dh * a.PW + s * a.dw;
+                // Piece-major issue order: every fragment's first K piece, then
+                // every fragment's second, so the two MFMAs accumulating into
+                // one register tile are FM*FN instructions apart (a dependent
+                // MFMA issued back to back waits for the previous result).
+                // Each piece's registers are refilled with the next tap right
+                // after their last use.
 #pragma unroll
-                for (int f = 0; f < FM; ++f) {
+                for (int i = 0; i < NP; ++i) {
 #pragma unroll
-                    for (int nf = 0; nf < FN; ++nf)
-                        Mma32<T>::run(acc[f][nf], ra[f][0], ra[f][1], bcur[nf][0], bcur[nf][1]);
-                    const int q = qbase[f] + toff_next;
+                    for (int f = 0; f < FM; ++f) {
 #pragma unroll
-                    for (int i = 0; i < NP; ++i)
-                        ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot(q, pslot[i]));
+                        for (int nf = 0; nf < FN; ++nf) Mma32<T>::piece(acc[f][nf], ra[f][i], bcur[nf][i], i);
+                        ra[f][i] = *reinterpret_cast<const uint4*>(
+                            pb + lds_slot<FR>(qbase[f] + toff_next, pslot[i]));
+                    }
                 }
 #pragma unroll
                 for (int nf = 0; nf < FN; ++nf)
@@ -807,7 +915,7 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     g->ntk = (p.kg + c.nt() - 1) / c.nt();
     // two patch buffers; the epilogue reuses them for an 8-byte offset per
     // register-tile pixel row
-    g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * 64, static_cast<size_t>(c.pixels()) * 8);
+    g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64), static_cast<size_t>(c.pixels()) * 8);
     g->stg = 0;
     {
         const int sz = wide_sz(p);
@@ -831,7 +939,7 @@ inline size_t filter_bytes(const Prob& p, const Cfg& c, const Geo& g) {
     return static_cast<size_t>(p.g) * g.ntk * g.nchunks * p.r * p.s * c.nt() * 64;
 }
 
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR>
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV>
 cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
                        hipStream_t st) {
     Args a;
@@ -846,7 +954,7 @@ cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* w
     a.TN = g.TN; a.TH = g.TH; a.TW = g.TW; a.PH = g.PH; a.PW = g.PW; a.npix = g.npix;
     a.tiles_w = g.tiles_w; a.tiles_h = g.tiles_h; a.tiles_n = g.tiles_n;
     a.nchunks = g.nchunks; a.ntk = g.ntk;
-    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR>;
+    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV>;
     static bool attr_done = false;
     if (g.lds_bytes > 65536 && !attr_done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -863,13 +971,18 @@ template <typename T, int XB>
 cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale,
                        void* y, hipStream_t st) {
     switch (cfg) {
-#define CFWD_IG_CFG(ID)                                                                                  \
-    case ID: {                                                                                           \
-        constexpr Cfg c = kCfgs[ID];                                                                     \
-        if constexpr (Wide<T, XB>::ok)                                                                   \
-            if (g.stg == 1)                                                                              \
-                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr>(p, g, x, wp, scale, y, st);    \
-        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr>(p, g, x, wp, scale, y, st);            \
+#define CFWD_IG_CFG(ID)                                                                                    \
+    case ID: {                                                                                             \
+        constexpr Cfg c = kCfgs[ID];                                                                       \
+        if constexpr (Wide<T, XB>::ok) {                                                                   \
+            if (g.stg == 1) {                                                                              \
+                if constexpr (c.fr == 32)                                                                  \
+                    if (p.r * p.s == 9)                                                                    \
+                        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9>(p, g, x, wp, scale, y, st); \
+                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 0>(p, g, x, wp, scale, y, st);   \
+            }                                                                                              \
+        }                                                                                                  \
+        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 0>(p, g, x, wp, scale, y, st);           \
     }
         CFWD_IG_CFG(0)
         CFWD_IG_CFG(1)
