@@ -95,12 +95,14 @@ def main():
         algo_arg = chosen
     wp = B.prepare_filter(w, desc, chosen)
     wp_ptr = wp.data_ptr() if wp is not None else 0
+    sbytes = B.scratch_size(desc, chosen)  # Winograd: transformed-input tiles
+    scratch = torch.empty(max(sbytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
     def step(i):
         st = B.conv2d_fwd_raw(desc, algo_arg, xs[i % nsets].data_ptr(), w.data_ptr(), wp_ptr, 0,
-                              ys[i % nsets].data_ptr(), 0, 0, sptr)
+                              ys[i % nsets].data_ptr(), scratch.data_ptr() if sbytes else 0, sbytes, sptr)
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
 

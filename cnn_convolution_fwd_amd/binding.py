@@ -27,7 +27,7 @@ ALGO_NAMES = {
 
 EXPORTED = [
     "cfwd_version", "cfwd_output_dims", "cfwd_resolve_algo", "cfwd_list_candidates", "cfwd_filter_size",
-    "cfwd_prepare_filter", "cfwd_workspace_size", "cfwd_conv2d_fwd", "cfwd_fastrun_select",
+    "cfwd_prepare_filter", "cfwd_workspace_size", "cfwd_scratch_size", "cfwd_conv2d_fwd", "cfwd_fastrun_select",
     "cfwd_fastrun_workspace_size", "cfwd_fastrun_lookup", "cfwd_fastrun_load", "cfwd_fastrun_save",
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
 ]
@@ -80,6 +80,7 @@ def _lib():
             "cfwd_filter_size": [dp, Algo, P(sz)],
             "cfwd_prepare_filter": [dp, Algo, vp, vp, sz, vp],
             "cfwd_workspace_size": [dp, Algo, P(sz)],
+            "cfwd_scratch_size": [dp, Algo, P(sz)],
             "cfwd_conv2d_fwd": [dp, Algo, vp, vp, vp, vp, vp, vp, sz, vp],
             "cfwd_fastrun_select": [dp, vp, vp, vp, vp, vp, sz, vp, P(Algo)],
             "cfwd_fastrun_workspace_size": [dp, P(sz)],
@@ -169,6 +170,12 @@ def filter_size(desc: ConvDesc, a: Algo) -> int:
 def workspace_size(desc: ConvDesc, a: Algo) -> int:
     b = ctypes.c_size_t()
     _check(_lib().cfwd_workspace_size(ctypes.byref(desc), a, ctypes.byref(b)))
+    return b.value
+
+
+def scratch_size(desc: ConvDesc, a: Algo) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib().cfwd_scratch_size(ctypes.byref(desc), a, ctypes.byref(b)))
     return b.value
 
 
@@ -307,11 +314,9 @@ def conv2d_fwd(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", c
     a = resolve_algo(desc, algo(algo_kind, config_id))
     if out is None:
         out = torch.empty(_out_shape(desc), dtype=x.dtype, device=x.device)
-    ws_bytes = 0
-    if w_prepared is None:
-        ws_bytes = workspace_size(desc, a)
-        if ws_bytes and workspace is None:
-            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
+    ws_bytes = workspace_size(desc, a) if w_prepared is None else scratch_size(desc, a)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
     st = conv2d_fwd_raw(desc, a, x.data_ptr(), w.data_ptr(), w_prepared.data_ptr() if w_prepared is not None else 0,

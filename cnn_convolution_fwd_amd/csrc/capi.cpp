@@ -194,6 +194,21 @@ size_t filter_bytes(const Prob& p, const cfwd_algo& a) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Device scratch an algorithm needs besides its prepared filter.
+size_t scratch_bytes(const Prob& p, const cfwd_algo& a) {
+    switch (a.kind) {
+        case CFWD_ALGO_WINOGRAD_F2X2_3X3: return winograd_scratch_bytes(p, 2, a.config_id);
+        case CFWD_ALGO_WINOGRAD_F6X6_3X3: return winograd_scratch_bytes(p, 6, a.config_id);
+        default: return 0;
+    }
+}
+
+// Workspace when no prepared filter is passed: [filter | scratch].
+size_t workspace_bytes(const Prob& p, const cfwd_algo& a) {
+    const size_t sb = scratch_bytes(p, a);
+    return sb ? round_up(filter_bytes(p, a), 256) + sb : filter_bytes(p, a);
+}
+
 // ------------------------------------------------------------- Fast-Run map
 
 struct DeviceId {
@@ -319,14 +334,14 @@ cfwd_status prepare(const Prob& p, const cfwd_algo& a, const void* w, void* wp, 
 }
 
 cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w, const void* wp,
-                const float* scale, void* y, hipStream_t st) {
+                const float* scale, void* y, void* scratch, hipStream_t st) {
     cfwd_status s;
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, st); break;
         case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, st); break;
         case CFWD_ALGO_DIRECT: s = direct_launch(p, a.config_id, x, w, scale, y, st); break;
-        case CFWD_ALGO_WINOGRAD_F2X2_3X3: s = winograd_launch(p, 2, a.config_id, x, wp, y, st); break;
-        case CFWD_ALGO_WINOGRAD_F6X6_3X3: s = winograd_launch(p, 6, a.config_id, x, wp, y, st); break;
+        case CFWD_ALGO_WINOGRAD_F2X2_3X3: s = winograd_launch(p, 2, a.config_id, x, wp, scratch, y, st); break;
+        case CFWD_ALGO_WINOGRAD_F6X6_3X3: s = winograd_launch(p, 6, a.config_id, x, wp, scratch, y, st); break;
         default: return set_error(CFWD_ERR_INVALID_ARG, "unknown algorithm kind");
     }
     if (s != CFWD_OK) return s;
@@ -344,15 +359,25 @@ cfwd_status conv_impl(const Prob& p, const cfwd_algo& a, const void* x, const vo
     if (p.dtype != CFWD_I8 && scale != nullptr)
         return set_error(CFWD_ERR_INVALID_ARG, "requant_scale is only for int8");
     const size_t fb = filter_bytes(p, a);
+    const size_t sb = scratch_bytes(p, a);
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    void* scratch = nullptr;
     if (fb > 0 && wp == nullptr) {
-        if (ws == nullptr || ws_bytes < fb)
-            return set_error(CFWD_ERR_WORKSPACE, "workspace of " + std::to_string(fb) +
+        const size_t need = workspace_bytes(p, a);
+        if (ws == nullptr || ws_bytes < need)
+            return set_error(CFWD_ERR_WORKSPACE, "workspace of " + std::to_string(need) +
                                                      " bytes needed to prepare the filter of " + cfwd_algo_name(a));
         cfwd_status s = prepare(p, a, w, ws, st);
         if (s != CFWD_OK) return s;
         wp = ws;
+        if (sb) scratch = wsb + round_up(fb, 256);
+    } else if (sb) {
+        if (ws == nullptr || ws_bytes < sb)
+            return set_error(CFWD_ERR_WORKSPACE, "workspace of " + std::to_string(sb) + " bytes needed by " +
+                                                     cfwd_algo_name(a));
+        scratch = ws;
     }
-    return run(p, a, x, w, wp, scale, y, st);
+    return run(p, a, x, w, wp, scale, y, scratch, st);
 }
 
 // ------------------------------------------------------------- Fast-Run selection
@@ -376,7 +401,7 @@ FrLayout fastrun_layout(const Prob& p, const std::vector<cfwd_algo>& cands) {
     const size_t xbytes = round_up(static_cast<size_t>(p.x_img) * p.n * p.esize, 256);
     const size_t wbytes = round_up(static_cast<size_t>(p.k) * p.cg * p.r * p.s * p.esize, 256);
     size_t cand = 0;
-    for (const auto& c : cands) cand = std::max(cand, filter_bytes(p, c));
+    for (const auto& c : cands) cand = std::max(cand, workspace_bytes(p, c));
     size_t off = 0;
     L.ref = off; off += ybytes;
     if (p.dtype == CFWD_I8) {
@@ -528,7 +553,29 @@ cfwd_status cfwd_prepare_filter(const cfwd_conv_desc* desc, cfwd_algo algo, cons
 }
 
 cfwd_status cfwd_workspace_size(const cfwd_conv_desc* desc, cfwd_algo algo, size_t* bytes) {
-    return cfwd_filter_size(desc, algo, bytes);
+    Prob p;
+    std::string why;
+    cfwd_status s = make_prob(desc, &p, &why);
+    if (s != CFWD_OK) return set_error(s, why);
+    if (!bytes) return set_error(CFWD_ERR_INVALID_ARG, "bytes must not be NULL");
+    cfwd_algo a;
+    s = resolve(p, algo, &a);
+    if (s != CFWD_OK) return s;
+    *bytes = workspace_bytes(p, a);
+    return CFWD_OK;
+}
+
+cfwd_status cfwd_scratch_size(const cfwd_conv_desc* desc, cfwd_algo algo, size_t* bytes) {
+    Prob p;
+    std::string why;
+    cfwd_status s = make_prob(desc, &p, &why);
+    if (s != CFWD_OK) return set_error(s, why);
+    if (!bytes) return set_error(CFWD_ERR_INVALID_ARG, "bytes must not be NULL");
+    cfwd_algo a;
+    s = resolve(p, algo, &a);
+    if (s != CFWD_OK) return s;
+    *bytes = scratch_bytes(p, a);
+    return CFWD_OK;
 }
 
 cfwd_status cfwd_fastrun_workspace_size(const cfwd_conv_desc* desc, size_t* bytes) {
@@ -598,10 +645,11 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
             if (s != CFWD_OK) break;
         }
         const void* wp = fb > 0 ? cand_ws : nullptr;
+        void* scr = scratch_bytes(p, a) ? static_cast<uint8_t*>(cand_ws) + round_up(fb, 256) : nullptr;
         std::vector<float> t;
         for (int rep = 0; rep < kWarmup + kReps && s == CFWD_OK; ++rep) {
             s = check_hip(hipEventRecord(e0, st), "hipEventRecord");
-            if (s == CFWD_OK) s = run(p, a, x, w_kcrs, wp, requant_scale, y, st);
+            if (s == CFWD_OK) s = run(p, a, x, w_kcrs, wp, requant_scale, y, scr, st);
             if (s == CFWD_OK) s = check_hip(hipEventRecord(e1, st), "hipEventRecord");
             if (s == CFWD_OK) s = check_hip(hipEventSynchronize(e1), "hipEventSynchronize");
             float ms = 0.0f;
@@ -634,7 +682,8 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
             s = prepare(p, chosen, w_kcrs, cand_ws, st);
             if (s != CFWD_OK) return s;
         }
-        s = run(p, chosen, x, w_kcrs, fb > 0 ? cand_ws : nullptr, requant_scale, y, st);
+        void* scr = scratch_bytes(p, chosen) ? static_cast<uint8_t*>(cand_ws) + round_up(fb, 256) : nullptr;
+        s = run(p, chosen, x, w_kcrs, fb > 0 ? cand_ws : nullptr, requant_scale, y, scr, st);
         if (s != CFWD_OK) return s;
         s = check_hip(hipStreamSynchronize(st), "hipStreamSynchronize");
         if (s != CFWD_OK) return s;

@@ -72,8 +72,9 @@ cfwd_status pointwise_launch(const Prob& p, int cfg, const void* x, const void* 
 int winograd_num_configs(int m);
 bool winograd_supported(const Prob& p, int m, int cfg, std::string* why);
 size_t winograd_filter_bytes(const Prob& p, int m, int cfg);
+size_t winograd_scratch_bytes(const Prob& p, int m, int cfg);  // transformed input U
 cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st);
-cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp,
+cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch,
                             void* y, hipStream_t st);
 
 // Writes 0 to the NCHWX output channels past K (no-op unless K % xb != 0).

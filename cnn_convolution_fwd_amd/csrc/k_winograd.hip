@@ -1,19 +1,650 @@
-// Winograd F(m x m, 3 x 3) family (not built yet).
-#include "internal.h"
+// Winograd minimal filtering F(m x m, 3 x 3), m = 2 or 6 (gfx950).
+//
+// MegEngine inference article, section "Winograd": F(2x2,3x3) and F(6x6,3x3)
+// trade multiplies for additions (2.25x and 5.06x fewer), in three steps --
+// transform the input tiles and the weights, multiply the transformed tiles as
+// a batched matrix product, transform the products back -- and its
+// engineering subsection blocks the tiles so one block's working set stays in
+// cache.  Momenta talk, section "優化3：FFT / Winograd的卷積演算法": accuracy
+// drops as the tile grows.
+//
+// Construction (written from the mathematics, here at compile time): with
+// alpha = m + 2 interpolation points (one may be "infinity", which evaluates a
+// polynomial to its leading coefficient), V_n evaluates an n-coefficient
+// polynomial at the points; linear convolution is V^-1 [(V_3 g) * (V_m u)] and
+// correlation is its transpose, so A^T = V_m^T, G = V_3, B^T = V^-T and
+//   Y = A^T [ (G g G^T) * (B^T d B) ] A   over alpha x alpha input tiles d.
+// Points: {0, 1, -1, inf} for m = 2; {0, +-1, +-2, +-1/2, inf} for m = 6.
+//
+// GPU structure (stride 1, dilation 1, groups 1, R = S = 3):
+//   prepare  V[xi][c][k] = (G g G^T)[xi] per (k, c), laid out like the
+//            implicit-GEMM B operand (32-column fragments, 64-byte K chunks);
+//   input    U[xi][chunk][tile][CK] = (B^T d B)[xi]: one thread per (tile,
+//            channel group), written channel-contiguous;
+//   gemm     per workgroup a block of TB tiles x KB output channels for all
+//            alpha^2 positions (split over the four waves), reduced over the
+//            input channels on the matrix cores; the alpha^2 products of each
+//            (tile, channel) are then exchanged through LDS in channel slices
+//            and transformed back, Y = A^T M A, straight into the output.
+// bf16 inputs use fp16 transformed operands (fp16 keeps 11 bits; the
+// transform entries reach 32, so bf16's 8 bits lose too much for F(6x6)); fp32
+// inputs keep fp32 operands on the fp32 matrix cores.  Accumulation is fp32.
+#include "igemm_impl.h"
 
 namespace cfwd {
+namespace wg {
 
-int winograd_num_configs(int) { return 0; }
-bool winograd_supported(const Prob&, int, int, std::string* why) {
-    if (why) *why = "winograd: not available in this build";
-    return false;
+using ig::f32x16;
+
+// ------------------------------------------------------------ matrices
+
+template <int M> struct Mats {
+    static constexpr int A = M + 2;
+    double at[M][A] = {};
+    double g[A][3] = {};
+    double bt[A][A] = {};
+};
+
+constexpr double kInf = 1e300;  // marks the point at infinity
+
+template <int M>
+constexpr Mats<M> build_mats() {
+    constexpr int A = M + 2;
+    double pts[A] = {};
+    if (M == 2) {
+        const double p[4] = {0.0, 1.0, -1.0, kInf};
+        for (int i = 0; i < 4; ++i) pts[i] = p[i];
+    } else {
+        const double p[8] = {0.0, 1.0, -1.0, 2.0, -2.0, 0.5, -0.5, kInf};
+        for (int i = 0; i < 8; ++i) pts[i] = p[i];
+    }
+    // evaluation matrices
+    double v[A][A] = {};
+    for (int i = 0; i < A; ++i)
+        for (int j = 0; j < A; ++j) {
+            if (pts[i] == kInf) {
+                v[i][j] = (j == A - 1) ? 1.0 : 0.0;
+            } else {
+                double x = 1.0;
+                for (int e = 0; e < j; ++e) x *= pts[i];
+                v[i][j] = x;
+            }
+        }
+    Mats<M> r{};
+    for (int i = 0; i < A; ++i) {
+        for (int j = 0; j < M; ++j) {
+            double x = 1.0;
+            if (pts[i] == kInf) {
+                x = (j == M - 1) ? 1.0 : 0.0;
+            } else {
+                for (int e = 0; e < j; ++e) x *= pts[i];
+            }
+            r.at[j][i] = x;  // A^T = V_m^T
+        }
+        for (int j = 0; j < 3; ++j) {
+            double x = 1.0;
+            if (pts[i] == kInf) {
+                x = (j == 2) ? 1.0 : 0.0;
+            } else {
+                for (int e = 0; e < j; ++e) x *= pts[i];
+            }
+            r.g[i][j] = x;  // G = V_3
+        }
+    }
+    // V^-1 by Gauss-Jordan with partial pivoting
+    double aug[A][2 * A] = {};
+    for (int i = 0; i < A; ++i)
+        for (int j = 0; j < A; ++j) {
+            aug[i][j] = v[i][j];
+            aug[i][A + j] = (i == j) ? 1.0 : 0.0;
+        }
+    for (int col = 0; col < A; ++col) {
+        int piv = col;
+        for (int rr = col + 1; rr < A; ++rr) {
+            const double a = aug[rr][col] < 0 ? -aug[rr][col] : aug[rr][col];
+            const double b = aug[piv][col] < 0 ? -aug[piv][col] : aug[piv][col];
+            if (a > b) piv = rr;
+        }
+        for (int j = 0; j < 2 * A; ++j) {
+            const double t = aug[col][j];
+            aug[col][j] = aug[piv][j];
+            aug[piv][j] = t;
+        }
+        const double inv = 1.0 / aug[col][col];
+        for (int j = 0; j < 2 * A; ++j) aug[col][j] *= inv;
+        for (int rr = 0; rr < A; ++rr) {
+            if (rr == col) continue;
+            const double f = aug[rr][col];
+            if (f == 0.0) continue;
+            for (int j = 0; j < 2 * A; ++j) aug[rr][j] -= f * aug[col][j];
+        }
+    }
+    for (int i = 0; i < A; ++i)
+        for (int j = 0; j < A; ++j) r.bt[i][j] = aug[j][A + i];  // B^T = (V^-1)^T
+    return r;
 }
-size_t winograd_filter_bytes(const Prob&, int, int) { return 0; }
-cfwd_status winograd_prepare(const Prob&, int, int, const void*, void*, hipStream_t) {
-    return set_error(CFWD_ERR_UNSUPPORTED, "winograd: not available in this build");
+
+template <int M> struct MatsF {
+    static constexpr Mats<M> d = build_mats<M>();
+};
+
+// ------------------------------------------------------------ operand types
+
+template <typename T> struct OpT;       // transformed operand storage
+template <> struct OpT<float> {
+    using type = float;
+    static __device__ __forceinline__ float from(float v) { return v; }
+};
+template <> struct OpT<bf16_t> {
+    using type = _Float16;
+    static __device__ __forceinline__ _Float16 from(float v) { return static_cast<_Float16>(v); }
+};
+
+// 32x32 fragments with fp16 operands (bf16 inputs) or fp32 operands.
+template <typename T> struct WMma;
+template <> struct WMma<bf16_t> {
+    static __device__ __forceinline__ void piece(f32x16& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                   0, 0);
+    }
+    static constexpr int pslot(int i, int h) { return 2 * i + h; }
+};
+template <> struct WMma<float> {
+    static __device__ __forceinline__ void piece(f32x16& c, const uint4& a, const uint4& b) {
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+    }
+    static constexpr int pslot(int i, int h) { return 2 * h + i; }
+};
+
+// ------------------------------------------------------------ geometry
+
+struct Geo {
+    int m, alpha, xi;       // tile size, alpha = m + 2, alpha^2
+    int th, tw, T, Tpad;    // tiles per image row/col, total tiles, padded to TB
+    int CK, nchunks;        // channels per 64-byte chunk, chunks
+    int TB, KB, ntk, ntb;   // tile block, output-channel block, block counts
+    size_t u_bytes;         // transformed-input workspace
+    size_t v_bytes;         // prepared filter
+};
+
+inline bool geometry(const Prob& p, int m, Geo* g, std::string* why) {
+    if (p.r != 3 || p.s != 3 || p.sh != 1 || p.sw != 1 || p.dh != 1 || p.dw != 1 || p.g != 1) {
+        if (why) *why = "winograd: needs 3x3, stride 1, dilation 1, groups 1";
+        return false;
+    }
+    if (p.dtype == CFWD_I8) {
+        if (why) *why = "winograd: float dtypes only (int8 needs an exact integer transform)";
+        return false;
+    }
+    g->m = m;
+    g->alpha = m + 2;
+    g->xi = g->alpha * g->alpha;
+    g->th = (p.oh + m - 1) / m;
+    g->tw = (p.ow + m - 1) / m;
+    const long long T = static_cast<long long>(p.n) * g->th * g->tw;
+    if (T > (1LL << 30)) {
+        if (why) *why = "winograd: too many tiles";
+        return false;
+    }
+    g->T = static_cast<int>(T);
+    g->TB = (m == 6) ? 32 : 64;
+    g->KB = (m == 6) ? 32 : 64;
+    g->Tpad = (g->T + g->TB - 1) / g->TB * g->TB;
+    g->CK = (p.dtype == CFWD_F32) ? 16 : 32;
+    g->nchunks = (p.c + g->CK - 1) / g->CK;
+    g->ntk = (p.k + g->KB - 1) / g->KB;
+    g->ntb = g->Tpad / g->TB;
+    g->u_bytes = static_cast<size_t>(g->xi) * g->nchunks * g->Tpad * 64;
+    g->v_bytes = static_cast<size_t>(g->xi) * g->ntk * g->nchunks * g->KB * 64;
+    return true;
 }
-cfwd_status winograd_launch(const Prob&, int, int, const void*, const void*, void*, hipStream_t) {
-    return set_error(CFWD_ERR_UNSUPPORTED, "winograd: not available in this build");
+
+// ------------------------------------------------------------ filter prepare
+// V[xi][kt][chunk][KB/32 frags][piece][32 rows][half][16 B] = G g G^T, in the
+// operand type; rows past K and channels past C are zero.
+
+template <typename T, int M>
+__global__ __launch_bounds__(256) void prepare_kernel(const T* __restrict__ w, uint8_t* __restrict__ out, int K, int C,
+                                                      int KB, int ntk, int nchunks) {
+    using O = typename OpT<T>::type;
+    constexpr int A = M + 2;
+    constexpr int E16 = 16 / static_cast<int>(sizeof(O));
+    constexpr int CK = 4 * E16;
+    constexpr Mats<M> mt = build_mats<M>();
+    // one thread per (k, c): transform, then scatter the alpha^2 values
+    const long long total = static_cast<long long>(ntk) * KB * nchunks * CK;
+    for (long long idx = blockIdx.x * 256LL + threadIdx.x; idx < total; idx += static_cast<long long>(gridDim.x) * 256) {
+        const int c = static_cast<int>(idx % (nchunks * CK));
+        const int k = static_cast<int>(idx / (nchunks * CK));
+        float gg[3][3] = {};
+        if (k < K && c < C)
+            for (int r = 0; r < 3; ++r)
+                for (int s = 0; s < 3; ++s) gg[r][s] = Elem<T>::to_f(w[(static_cast<long long>(k) * C + c) * 9 + r * 3 + s]);
+        float tmp[A][3];
+#pragma unroll
+        for (int i = 0; i < A; ++i)
+#pragma unroll
+            for (int s = 0; s < 3; ++s) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 3; ++r) acc = fmaf(static_cast<float>(mt.g[i][r]), gg[r][s], acc);
+                tmp[i][s] = acc;
+            }
+        const int kt = k / KB, kl = k % KB;
+        const int chunk = c / CK, cc = c % CK;
+        const int slot = cc / E16, e = cc % E16;
+        // which (piece, half) holds this slot
+        int piece = 0, half = 0;
+        for (int i = 0; i < 2; ++i)
+            for (int h = 0; h < 2; ++h)
+                if (WMma<T>::pslot(i, h) == slot) {
+                    piece = i;
+                    half = h;
+                }
+        const int nfr = kl / 32, row = kl % 32;
+#pragma unroll
+        for (int i = 0; i < A; ++i)
+#pragma unroll
+            for (int j = 0; j < A; ++j) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int s = 0; s < 3; ++s) acc = fmaf(tmp[i][s], static_cast<float>(mt.g[j][s]), acc);
+                const int x = i * A + j;
+                const long long base =
+                    ((((static_cast<long long>(x) * ntk + kt) * nchunks + chunk) * (KB / 32) + nfr) * 2 + piece) * 32 + row;
+                O* dst = reinterpret_cast<O*>(out + (base * 2 + half) * 16) + e;
+                *dst = OpT<T>::from(acc);
+            }
+    }
+}
+
+// ------------------------------------------------------------ input transform
+// U[xi][chunk][tile][CK], tile = (n * th + ty) * tw + tx; padded tiles are 0.
+// A workgroup covers TXB consecutive tiles of one tile row and one channel
+// chunk: the alpha input rows they read are staged in LDS with loads
+// coalesced along W ([row][col][channel], fp32), then thread (tile, channel)
+// transforms its alpha x alpha tile and the lanes of one tile write the
+// chunk's CK channels as one contiguous 64-byte run per position.
+
+template <int M, int CK> struct InGeo {
+    static constexpr int A = M + 2;
+    static constexpr int TXB = 256 / CK;               // tiles per workgroup
+    static constexpr int COLS = TXB * M + 2;           // input columns staged
+    static constexpr int LDS_FLOATS = A * COLS * CK;
+};
+
+template <typename T, int XB, int M>
+__global__ __launch_bounds__(256) void input_kernel(const T* __restrict__ x, uint8_t* __restrict__ U, int N, int C, int H,
+                                                    int W, int ph, int pw, long long x_img, int th, int tw, int T_,
+                                                    int Tpad, int nchunks, int tblocks_w) {
+    using O = typename OpT<T>::type;
+    constexpr int A = M + 2;
+    constexpr int CK = 64 / static_cast<int>(sizeof(O));
+    using IG = InGeo<M, CK>;
+    constexpr int TXB = IG::TXB;
+    constexpr int COLS = IG::COLS;
+    constexpr Mats<M> mt = build_mats<M>();
+    __shared__ float patch[IG::LDS_FLOATS];
+
+    // block -> (image n, tile row ty, tile column block bx, chunk)
+    int b = blockIdx.x;
+    const int bx = b % tblocks_w;
+    b /= tblocks_w;
+    const int ty = b % th;
+    const int n = b / th;
+    const int chunk = blockIdx.y;
+    const int tx0 = bx * TXB;
+    const int ih0 = ty * M - ph, iw0 = tx0 * M - pw;
+    const T* xn = x + n * x_img;
+
+    // stage: A rows x COLS cols x CK channels, column fastest across threads
+    for (int e = threadIdx.x; e < A * COLS * CK; e += 256) {
+        const int col = e % COLS;
+        const int t = e / COLS;
+        const int row = t % A;
+        const int cc = t / A;
+        const int c = chunk * CK + cc;
+        const int ih = ih0 + row, iw = iw0 + col;
+        float v = 0.0f;
+        if (c < C && ih >= 0 && ih < H && iw >= 0 && iw < W) v = Elem<T>::to_f(xn[act_off<XB>(c, ih, iw, H, W)]);
+        patch[(row * COLS + col) * CK + cc] = v;
+    }
+    __syncthreads();
+
+    const int cc = threadIdx.x % CK;
+    const int tl = threadIdx.x / CK;
+    const int tx = tx0 + tl;
+    int tile = (n * th + ty) * tw + tx;
+    const bool real = tx < tw;
+    float d[A][A];
+#pragma unroll
+    for (int i = 0; i < A; ++i)
+#pragma unroll
+        for (int j = 0; j < A; ++j) d[i][j] = patch[(i * COLS + tl * M + j) * CK + cc];
+    float t[A][A];
+#pragma unroll
+    for (int i = 0; i < A; ++i)
+#pragma unroll
+        for (int j = 0; j < A; ++j) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < A; ++k) {
+                const float bk = static_cast<float>(mt.bt[i][k]);
+                if (bk != 0.0f) acc = fmaf(bk, d[k][j], acc);
+            }
+            t[i][j] = acc;
+        }
+    if (!real) return;
+    O* dst = reinterpret_cast<O*>(U + (static_cast<long long>(chunk) * Tpad + tile) * 64) + cc;
+    const long long xstride = static_cast<long long>(nchunks) * Tpad * 64 / static_cast<long long>(sizeof(O));
+#pragma unroll
+    for (int i = 0; i < A; ++i)
+#pragma unroll
+        for (int j = 0; j < A; ++j) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int k = 0; k < A; ++k) {
+                const float bk = static_cast<float>(mt.bt[j][k]);
+                if (bk != 0.0f) acc = fmaf(t[i][k], bk, acc);
+            }
+            dst[(i * A + j) * xstride] = OpT<T>::from(acc);
+        }
+}
+
+// Zero rows of U for the padding tiles T .. Tpad-1 (they feed the last tile
+// block's MFMAs; their outputs are discarded, but must not be NaN garbage).
+__global__ __launch_bounds__(256) void zero_pad_tiles(uint8_t* __restrict__ U, int xi_chunks, int T_, int Tpad) {
+    const int per = (Tpad - T_) * 4;  // uint4 per (xi, chunk)
+    const long long total = static_cast<long long>(xi_chunks) * per;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < total; i += static_cast<long long>(gridDim.x) * 256) {
+        const long long xc = i / per;
+        const int r = static_cast<int>(i % per);
+        *reinterpret_cast<uint4*>(U + (xc * Tpad + T_) * 64 + r * 16) = make_uint4(0, 0, 0, 0);
+    }
+}
+
+// ------------------------------------------------------------ batched GEMM + output transform
+// Workgroup: TB tiles x KB output channels, all alpha^2 positions; wave w owns
+// positions [w * XPW, (w+1) * XPW).  Operands come straight from L2:
+// U (A operand, rows = tiles) and V (B operand, columns = output channels),
+// each lane feeding two 16-byte K pieces per 64-byte chunk.
+
+template <int M> struct GemmGeo {
+    static constexpr int NW = (M == 6) ? 8 : 4;  // waves: positions split over them
+    static constexpr int NTHR = NW * 64;
+};
+
+template <typename T, int XB, int M>
+__global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* __restrict__ U, const uint8_t* __restrict__ V,
+                                                   T* __restrict__ y, int K, int OH, int OW, long long y_img, int th,
+                                                   int tw, int T_, int Tpad, int nchunks, int ntk) {
+    constexpr int A = M + 2;
+    constexpr int XI = A * A;
+    constexpr int NW = GemmGeo<M>::NW;
+    constexpr int NTHR = GemmGeo<M>::NTHR;
+    constexpr int XPW = XI / NW;              // positions per wave
+    constexpr int TB = (M == 6) ? 32 : 64;
+    constexpr int KB = (M == 6) ? 32 : 64;
+    constexpr int TF = TB / 32, KF = KB / 32;  // fragments per wave per position
+    constexpr Mats<M> mt = build_mats<M>();
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lrow = lane & 31, h = lane >> 5;
+    // tile block fastest: consecutive workgroups share the same filter slice
+    const int tb = blockIdx.x % (Tpad / TB);
+    const int kt = blockIdx.x / (Tpad / TB);
+
+    f32x16 acc[XPW][TF][KF];
+#pragma unroll
+    for (int x = 0; x < XPW; ++x)
+#pragma unroll
+        for (int a = 0; a < TF; ++a)
+#pragma unroll
+            for (int b = 0; b < KF; ++b) acc[x][a][b] = f32x16{};
+
+    const int ps0 = WMma<T>::pslot(0, h), ps1 = WMma<T>::pslot(1, h);
+    // operands of one (chunk, position) step; two slots alternate so that the
+    // next step's loads are in flight during this step's MFMAs (XPW is even,
+    // so the slot of a position is the same in every chunk)
+    uint4 ua[2][TF][2], vb[2][KF][2];
+    // per-lane byte offsets (the same for every position and chunk); the
+    // position / chunk part of each address is uniform across the wave
+    int uoff[TF][2], voff[KF];
+#pragma unroll
+    for (int a = 0; a < TF; ++a) {
+        uoff[a][0] = (tb * TB + a * 32 + lrow) * 64 + ps0 * 16;
+        uoff[a][1] = (tb * TB + a * 32 + lrow) * 64 + ps1 * 16;
+    }
+#pragma unroll
+    for (int b = 0; b < KF; ++b) voff[b] = b * 2048 + lrow * 32 + h * 16;
+    auto load = [&](int slot, int chunk, int x) {
+        const int xi = wave * XPW + x;
+        const uint8_t* ub = U + (static_cast<long long>(xi) * nchunks + chunk) * Tpad * 64;
+        const uint8_t* vbase = V + ((static_cast<long long>(xi) * ntk + kt) * nchunks + chunk) * KF * 2048;
+#pragma unroll
+        for (int a = 0; a < TF; ++a) {
+            ua[slot][a][0] = *reinterpret_cast<const uint4*>(ub + uoff[a][0]);
+            ua[slot][a][1] = *reinterpret_cast<const uint4*>(ub + uoff[a][1]);
+        }
+#pragma unroll
+        for (int b = 0; b < KF; ++b) {
+            vb[slot][b][0] = *reinterpret_cast<const uint4*>(vbase + voff[b]);
+            vb[slot][b][1] = *reinterpret_cast<const uint4*>(vbase + voff[b] + 1024);
+        }
+    };
+    static_assert(XPW % 2 == 0, "positions per wave must be even");
+    load(0, 0, 0);
+    for (int chunk = 0; chunk < nchunks; ++chunk) {
+#pragma unroll
+        for (int x = 0; x < XPW; ++x) {
+            const int cur = x & 1;
+            if (x + 1 < XPW)
+                load(cur ^ 1, chunk, x + 1);
+            else
+                load(cur ^ 1, min(chunk + 1, nchunks - 1), 0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int a = 0; a < TF; ++a)
+#pragma unroll
+                    for (int b = 0; b < KF; ++b) WMma<T>::piece(acc[x][a][b], ua[cur][a][i], vb[cur][b][i]);
+        }
+    }
+
+    // Output transform, one slice of KS output channels at a time:
+    // M[xi][tile][KS] (fp32) in LDS, then Y = A^T M A per (tile, channel).
+    constexpr int KS = (M == 6) ? 8 : 16;
+    float* Ms = reinterpret_cast<float*>(lds);
+#pragma unroll 1
+    for (int ks = 0; ks < KB; ks += KS) {
+        // fragment D[row = tile][col = channel]: lane holds column lrow (+32*b),
+        // accumulator v is row 8*(v/4) + 4*h + v%4 (+32*a)
+#pragma unroll
+        for (int b = 0; b < KF; ++b) {
+            const int col = b * 32 + lrow;
+            if (col >= ks && col < ks + KS) {
+#pragma unroll
+                for (int x = 0; x < XPW; ++x)
+#pragma unroll
+                    for (int a = 0; a < TF; ++a)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int row = a * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                            Ms[((wave * XPW + x) * TB + row) * KS + (col - ks)] = acc[x][a][b][v];
+                        }
+            }
+        }
+        __syncthreads();
+        for (int pr = tid; pr < TB * KS; pr += NTHR) {
+            const int row = pr % TB, kl = pr / TB;  // tile fastest across lanes
+            const int tile = tb * TB + row;
+            const int k = kt * KB + ks + kl;
+            if (tile < T_ && k < K) {
+                // t = A^T M, one column of M at a time (keeps registers low)
+                float t[M][A];
+#pragma unroll
+                for (int j = 0; j < A; ++j) {
+                    float col[A];
+#pragma unroll
+                    for (int q = 0; q < A; ++q) col[q] = Ms[((q * A + j) * TB + row) * KS + kl];
+#pragma unroll
+                    for (int i = 0; i < M; ++i) {
+                        float s = 0.0f;
+#pragma unroll
+                        for (int q = 0; q < A; ++q) {
+                            const float c = static_cast<float>(mt.at[i][q]);
+                            if (c != 0.0f) s = fmaf(c, col[q], s);
+                        }
+                        t[i][j] = s;
+                    }
+                }
+                const int tx = tile % tw;
+                const int t2 = tile / tw;
+                const int ty = t2 % th;
+                const int n = t2 / th;
+#pragma unroll
+                for (int i = 0; i < M; ++i) {
+                    const int oh = ty * M + i;
+                    if (oh >= OH) continue;
+#pragma unroll
+                    for (int j = 0; j < M; ++j) {
+                        const int ow = tx * M + j;
+                        if (ow >= OW) continue;
+                        float s = 0.0f;
+#pragma unroll
+                        for (int q = 0; q < A; ++q) {
+                            const float c = static_cast<float>(mt.at[j][q]);
+                            if (c != 0.0f) s = fmaf(t[i][q], c, s);
+                        }
+                        T* dst = y + n * y_img + act_off<XB>(k, oh, ow, OH, OW);
+                        if constexpr (sizeof(T) == 4)
+                            *dst = s;
+                        else
+                            dst->bits = float_to_bf16(s);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <typename T, int XB, int M>
+cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y,
+                     hipStream_t st) {
+    {
+        using O = typename OpT<T>::type;
+        constexpr int TXB = InGeo<M, 64 / static_cast<int>(sizeof(O))>::TXB;
+        const int tblocks_w = (g.tw + TXB - 1) / TXB;
+        const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n) * g.th * tblocks_w),
+                        static_cast<unsigned>(g.nchunks));
+        input_kernel<T, XB, M><<<grid, 256, 0, st>>>(static_cast<const T*>(x), static_cast<uint8_t*>(ubuf), p.n, p.c,
+                                                     p.h, p.w, p.ph, p.pw, p.x_img, g.th, g.tw, g.T, g.Tpad,
+                                                     g.nchunks, tblocks_w);
+        cfwd_status s = check_hip(hipGetLastError(), "winograd input transform launch");
+        if (s != CFWD_OK) return s;
+        if (g.Tpad > g.T) {
+            const long long n16 = static_cast<long long>(g.xi) * g.nchunks * (g.Tpad - g.T) * 4;
+            const unsigned zb = static_cast<unsigned>(std::min<long long>((n16 + 255) / 256, 4096));
+            zero_pad_tiles<<<zb, 256, 0, st>>>(static_cast<uint8_t*>(ubuf), g.xi * g.nchunks, g.T, g.Tpad);
+            s = check_hip(hipGetLastError(), "winograd pad-tile clear launch");
+            if (s != CFWD_OK) return s;
+        }
+    }
+    constexpr int A = M + 2;
+    constexpr int TB = (M == 6) ? 32 : 64;
+    constexpr int KS = (M == 6) ? 8 : 16;
+    const size_t lds = static_cast<size_t>(A * A) * TB * KS * 4;
+    auto kern = gemm_kernel<T, XB, M>;
+    static bool attr = false;
+    if (lds > 65536 && !attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return check_hip(e, "hipFuncSetAttribute(winograd gemm)");
+        attr = true;
+    }
+    const unsigned blocks = static_cast<unsigned>(g.ntb * g.ntk);
+    kern<<<blocks, GemmGeo<M>::NTHR, lds, st>>>(static_cast<const uint8_t*>(ubuf), static_cast<const uint8_t*>(vprep),
+                                   static_cast<T*>(y), p.k, p.oh, p.ow, p.y_img, g.th, g.tw, g.T, g.Tpad, g.nchunks,
+                                   g.ntk);
+    return check_hip(hipGetLastError(), "winograd gemm launch");
+}
+
+template <typename T, int M>
+cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y,
+                     hipStream_t st) {
+    switch (p.xb) {
+        case 1: return launch_t<T, 1, M>(p, g, x, vprep, ubuf, y, st);
+        case 4: return launch_t<T, 4, M>(p, g, x, vprep, ubuf, y, st);
+        case 8: return launch_t<T, 8, M>(p, g, x, vprep, ubuf, y, st);
+        default: return set_error(CFWD_ERR_UNSUPPORTED, "winograd: bad channel block");
+    }
+}
+
+}  // namespace wg
+
+int winograd_num_configs(int) { return 1; }
+
+bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
+    if (cfg != 0 || (m != 2 && m != 6)) {
+        if (why) *why = "winograd: no such config";
+        return false;
+    }
+    wg::Geo g;
+    return wg::geometry(p, m, &g, why);
+}
+
+size_t winograd_filter_bytes(const Prob& p, int m, int) {
+    wg::Geo g;
+    if (!wg::geometry(p, m, &g, nullptr)) return 0;
+    return g.v_bytes;
+}
+
+size_t winograd_scratch_bytes(const Prob& p, int m, int) {
+    wg::Geo g;
+    if (!wg::geometry(p, m, &g, nullptr)) return 0;
+    return g.u_bytes;
+}
+
+cfwd_status winograd_prepare(const Prob& p, int m, int, const void* w, void* wp, hipStream_t st) {
+    wg::Geo g;
+    std::string why;
+    if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    const long long total = static_cast<long long>(g.ntk) * g.KB * g.nchunks * g.CK;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    const unsigned nb = static_cast<unsigned>(blocks);
+    uint8_t* out = static_cast<uint8_t*>(wp);
+    if (p.dtype == CFWD_F32) {
+        if (m == 2)
+            wg::prepare_kernel<float, 2><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+        else
+            wg::prepare_kernel<float, 6><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+    } else {
+        if (m == 2)
+            wg::prepare_kernel<bf16_t, 2><<<nb, 256, 0, st>>>(static_cast<const bf16_t*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+        else
+            wg::prepare_kernel<bf16_t, 6><<<nb, 256, 0, st>>>(static_cast<const bf16_t*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+    }
+    return check_hip(hipGetLastError(), "winograd filter transform launch");
+}
+
+cfwd_status winograd_launch(const Prob& p, int m, int, const void* x, const void* wp, void* scratch, void* y,
+                            hipStream_t st) {
+    wg::Geo g;
+    std::string why;
+    if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    if (scratch == nullptr || wp == nullptr)
+        return set_error(CFWD_ERR_WORKSPACE, "winograd: prepared filter and scratch are required");
+    if (p.dtype == CFWD_F32)
+        return (m == 2) ? wg::launch_m<float, 2>(p, g, x, wp, scratch, y, st)
+                        : wg::launch_m<float, 6>(p, g, x, wp, scratch, y, st);
+    return (m == 2) ? wg::launch_m<bf16_t, 2>(p, g, x, wp, scratch, y, st)
+                    : wg::launch_m<bf16_t, 6>(p, g, x, wp, scratch, y, st);
 }
 
 }  // namespace cfwd

@@ -132,8 +132,14 @@ cfwd_status cfwd_prepare_filter(const cfwd_conv_desc *desc, cfwd_algo algo, cons
                                 void *w_prepared, size_t bytes, void *stream);
 
 /* Workspace bytes conv2d_fwd needs for `algo` when it is given no prepared
- * filter (it then prepares one into the workspace first).  0 when none. */
+ * filter: the prepared filter (built into the workspace first), rounded up to
+ * 256 bytes, plus the algorithm's scratch.  0 when none. */
 cfwd_status cfwd_workspace_size(const cfwd_conv_desc *desc, cfwd_algo algo, size_t *bytes);
+
+/* Workspace bytes conv2d_fwd needs for `algo` when it is given a prepared
+ * filter: the algorithm's scratch only (Winograd: the transformed input
+ * tiles B^T d B, alpha^2 x ceil(C / chunk) x tiles x 64 bytes).  0 when none. */
+cfwd_status cfwd_scratch_size(const cfwd_conv_desc *desc, cfwd_algo algo, size_t *bytes);
 
 /* y = conv(x, w).  w_kcrs is required.  w_prepared may be NULL; when it is
  * not, it must hold cfwd_prepare_filter's output for the same descriptor and

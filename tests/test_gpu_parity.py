@@ -49,7 +49,7 @@ LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
 
 
 def tol_for(dtype, algo):
-    return (TOL_WINOGRAD if algo.startswith("winograd") else TOL)[dtype]
+    return (TOL_WINOGRAD if algo.startswith("winograd_f6x6") else TOL)[dtype]
 
 
 def check_float(name, y, ref, den, dtype, algo):
