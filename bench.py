@@ -1,25 +1,32 @@
 #!/usr/bin/env python3
-"""Benchmark: forward convolution of the ResNet 3x3 256-channel layer at 56x56.
+"""Benchmark of the forward-convolution library on one GPU.
 
-One step = one forward convolution of the whole batch (N=32, C=K=256,
-56x56, 3x3, stride 1, pad 1, bf16 in / fp32 accumulate / bf16 out, NCHW)
-through the C ABI with AUTO dispatch: the Fast-Run selection phase runs once
-during set-up (untimed), every timed step dispatches from the Fast-Run map
-(execution phase) with the filter prepared once, as inference does with
-constant weights.  Inputs are seeded synthetic data (x ~ N(0,1),
-w ~ N(0, 2/fan_in)), already resident in HBM; the timed loop rotates over
-enough input/output buffer sets (> 512 MB, twice the 256 MB Infinity Cache)
-that no step reads its input from the cache a previous step filled.
+One step = one forward pass of every conv layer of the chosen workload over
+one batch, each layer dispatched through the C ABI.  The default workload is
+the ResNet 3x3 256-channel layer at 56x56 (N=32, C=K=256, stride 1, pad 1,
+bf16 in / fp32 accumulate / bf16 out, NCHW).  With ``--algo auto`` (the
+default) the Fast-Run selection phase runs once per layer during set-up
+(untimed) and every timed step dispatches from the Fast-Run map (execution
+phase), with filters prepared once, as inference does with constant weights.
 
-Prints ONE JSON line with the throughput, the roofline of the dominant kernel
-(HIP events around every launch, on the stream the kernel runs on) and the CPU
-oracle timed on a bounded sample of the same workload.
+Inputs are seeded synthetic data (the distributions of each workload, drawn
+by ``cnn_convolution_fwd_amd.workloads``) already resident in HBM; the timed
+loop rotates over enough input/output buffer sets (> 512 MB, twice the 256 MB
+Infinity Cache) that no step reads its input from the cache a previous step
+filled.
 
-    python bench.py [--steps K] [--warmup W] [--dtype bf16|f32] [--algo auto|implicit_gemm/<cfg>|...]
+Prints ONE JSON line: whole-step throughput, the roofline of the dominant
+kernel (HIP events around every launch, on the stream the kernel runs on),
+and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--workload NAME] [--n N] [--dtype bf16|f32|i8] [--algo auto|family[/cfg]]
+                    [--steps K] [--warmup W]
+    python bench.py --copy-calibration    # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,126 +37,248 @@ sys.path.insert(0, ROOT)
 
 METRIC = "conv TFLOP/s (int8 TOP/s) + % MFMA/HBM roofline, ResNet 3x3 256ch@56x56"
 
+# name -> (benchmark configuration, layer indices, dtypes (first = default))
+WORKLOADS = {
+    "resnet_3x3_256ch_56x56": (3, [0], ("bf16", "f32")),
+    "single_conv_16to32_32x32": (1, [0], ("f32",)),
+    "mobilenet_stem_dw_pw": (2, [0, 1, 2], ("f32", "bf16")),
+    "mobilenet_stem3x3s2_3to32_224": (2, [0], ("f32", "bf16")),
+    "mobilenet_dw3x3_32ch_112": (2, [1], ("f32", "bf16")),
+    "mobilenet_pw1x1_32to64_112": (2, [2], ("f32", "bf16")),
+    "bottleneck_1x1_3x3_1x1_56x56": (4, [0, 1, 2], ("bf16",)),
+    "plain_3x3_256_56x56": (4, [3], ("bf16",)),
+    "resnet18_int8_nchw4": (5, list(range(20)), ("i8",)),
+}
+ALIASES = {
+    "resnet3x3": "resnet_3x3_256ch_56x56", "single": "single_conv_16to32_32x32",
+    "mobilenet": "mobilenet_stem_dw_pw", "stem": "mobilenet_stem3x3s2_3to32_224",
+    "depthwise": "mobilenet_dw3x3_32ch_112", "pointwise": "mobilenet_pw1x1_32to64_112",
+    "bottleneck": "bottleneck_1x1_3x3_1x1_56x56", "plain": "plain_3x3_256_56x56",
+    "resnet18_int8": "resnet18_int8_nchw4",
+}
+ROTATE_BYTES = 512 * 2**20
+MAX_SETS = 256
+
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f32"])
-    ap.add_argument("--algo", default="auto", help="auto (Fast-Run) or family[/config], e.g. implicit_gemm/1")
+    ap.add_argument("--workload", default="resnet3x3", help="one of %s" % ", ".join(list(ALIASES) + list(WORKLOADS)))
+    ap.add_argument("--n", type=int, default=0, help="batch size (0: the workload's own)")
+    ap.add_argument("--dtype", default="", choices=["", "bf16", "f32", "i8"])
+    ap.add_argument("--algo", default="auto", help="auto (Fast-Run) or family[/config], e.g. implicit_gemm/7")
     ap.add_argument("--sets", type=int, default=0, help="rotated buffer sets (0: enough for > 512 MB)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle CPU work at most")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain device copy of 1 GiB instead (scales HBM byte counters)")
     return ap.parse_args()
+
+
+def sources_digest(names) -> str:
+    """sha256 (16 hex digits) over the named kernel source files, in the given order."""
+    d = os.path.join(ROOT, "cnn_convolution_fwd_amd", "csrc")
+    h = hashlib.sha256()
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, dtype: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when there is none or the kernel's sources changed since
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (workload, dtype))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                kv[k.strip()] = v.strip()
+    try:
+        if kv["sources_sha256"] != sources_digest(kv["sources"].split()):
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, OSError, ValueError):
+        return None
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    nbytes = 2**30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
+                      "gb_per_s": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (batch sharding is described in "
+        print("bench.py measures one GPU: this library has no multi-GPU path (batch sharding is described in "
               "DESIGN.md); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
     import torch
 
-    from cnn_convolution_fwd_amd import binding as B
-    from cnn_convolution_fwd_amd.roofline import PEAK, layer_bytes, layer_flops
-    from cnn_convolution_fwd_amd.workloads import CONFIGS, bf16_bits, float_problem
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.copy_calibration:
+        copy_calibration()
+        return
+
+    from cnn_convolution_fwd_amd import binding as B
+    from cnn_convolution_fwd_amd.roofline import PEAK, bound, layer_bytes, layer_flops
+    from cnn_convolution_fwd_amd.workloads import CONFIGS, bf16_bits, float_problem, int8_problem, pack_nchwx
+
+    base = ALIASES.get(a.workload, a.workload)
+    if base not in WORKLOADS:
+        print("unknown workload %s" % a.workload, file=sys.stderr)
+        sys.exit(2)
+    cfg_idx, layer_ids, dtypes = WORKLOADS[base]
+    cfg = CONFIGS[cfg_idx]
+    dtype = a.dtype or dtypes[0]
+    if dtype not in dtypes:
+        print("workload %s runs in %s" % (base, "/".join(dtypes)), file=sys.stderr)
+        sys.exit(2)
+    N = a.n or cfg.n
+    workload = "%s_n%d" % (base, N)
     dev = torch.device("cuda:0")
-    cfg = CONFIGS[3]
-    L = cfg.layers[0]
-    N = cfg.n
-    pr = float_problem(3, dtype=a.dtype)
+    int8 = dtype == "i8"
+    layout = "NCHWX" if int8 else "NCHW"
 
     def to_dev(arr):
-        if a.dtype == "bf16":
+        if dtype == "bf16":
             return torch.from_numpy(bf16_bits(arr).view(np.int16)).to(dev).view(torch.bfloat16)
+        if int8:
+            return torch.from_numpy(np.ascontiguousarray(arr, np.int8)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
 
-    x0 = to_dev(pr.x)
-    w = to_dev(pr.w)
-    esize = 2 if a.dtype == "bf16" else 4
-    set_bytes = (x0.numel() + N * L.k * L.h * L.w) * esize
-    nsets = a.sets or max(2, -(-512 * 2**20 // set_bytes) + 1)
-    xs = [x0] + [x0.clone() for _ in range(nsets - 1)]
-    desc = B.desc_for(x0, w, L.stride, L.pad, L.dil, L.groups)
-    oh, ow = B.output_dims(desc)
-    ys = [torch.empty((N, L.k, oh, ow), dtype=x0.dtype, device=dev) for _ in range(nsets)]
+    # ---- per-layer set-up: inputs, algorithm (Fast-Run), prepared filter, scratch
+    layers = []
+    for li in layer_ids:
+        L = cfg.layers[li]
+        if int8:
+            pr = int8_problem(cfg_idx, li, n=N)
+            x0 = to_dev(pack_nchwx(pr.x, cfg.x_block))
+            scale = torch.from_numpy(pr.scale).to(dev)
+        else:
+            pr = float_problem(cfg_idx, li, n=N, dtype=dtype)
+            x0 = to_dev(pr.x)
+            scale = None
+        w = to_dev(pr.w)
+        desc = B.desc_for(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c)
+        y0 = torch.empty(B._out_shape(desc), dtype=x0.dtype, device=dev)
+        if a.algo == "auto":
+            best, _ = B.fastrun_select(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c,
+                                       requant_scale=scale, out=y0)
+            chosen = B.resolve_algo(desc, B.algo())
+            assert chosen.key() == best.key()
+            algo_arg = B.algo()  # AUTO: dispatch from the Fast-Run map
+        else:
+            fam, _, cid = a.algo.partition("/")
+            chosen = B.resolve_algo(desc, B.algo(fam, int(cid) if cid else -1))
+            algo_arg = chosen
+        wp = B.prepare_filter(w, desc, chosen)
+        sbytes = B.scratch_size(desc, chosen)
+        layers.append(dict(L=L, pr=pr, x0=x0, y0=y0, w=w, scale=scale, desc=desc, chosen=chosen,
+                           algo_arg=algo_arg, wp=wp, sbytes=sbytes,
+                           scratch=torch.empty(max(sbytes, 1), dtype=torch.uint8, device=dev)))
 
-    # Fast-Run selection (untimed set-up), then the execution phase dispatches from the map.
-    if a.algo == "auto":
-        B.fastrun_clear()
-        best, _ = B.fastrun_select(x0, w, L.stride, L.pad, L.dil, L.groups, out=ys[0])
-        chosen = B.resolve_algo(desc, B.algo())
-        assert chosen.key() == best.key()
-        algo_arg = B.algo()  # AUTO: dispatch from the Fast-Run map
-    else:
-        fam, _, cid = a.algo.partition("/")
-        chosen = B.resolve_algo(desc, B.algo(fam, int(cid) if cid else -1))
-        algo_arg = chosen
-    wp = B.prepare_filter(w, desc, chosen)
-    wp_ptr = wp.data_ptr() if wp is not None else 0
-    sbytes = B.scratch_size(desc, chosen)  # Winograd: transformed-input tiles
-    scratch = torch.empty(max(sbytes, 1), dtype=torch.uint8, device=dev)
+    set_bytes = sum(l["x0"].numel() * l["x0"].element_size() + l["y0"].numel() * l["y0"].element_size()
+                    for l in layers)
+    nsets = a.sets or min(MAX_SETS, max(2, -(-ROTATE_BYTES // set_bytes) + 1))
+    for l in layers:
+        l["xs"] = [l["x0"]] + [l["x0"].clone() for _ in range(nsets - 1)]
+        l["ys"] = [l["y0"]] + [torch.empty_like(l["y0"]) for _ in range(nsets - 1)]
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def step(i):
-        st = B.conv2d_fwd_raw(desc, algo_arg, xs[i % nsets].data_ptr(), w.data_ptr(), wp_ptr, 0,
-                              ys[i % nsets].data_ptr(), scratch.data_ptr() if sbytes else 0, sbytes, sptr)
+    def launch(l, i):
+        st = B.conv2d_fwd_raw(l["desc"], l["algo_arg"], l["xs"][i % nsets].data_ptr(), l["w"].data_ptr(),
+                              l["wp"].data_ptr() if l["wp"] is not None else 0,
+                              l["scale"].data_ptr() if l["scale"] is not None else 0,
+                              l["ys"][i % nsets].data_ptr(), l["scratch"].data_ptr() if l["sbytes"] else 0,
+                              l["sbytes"], sptr)
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
 
     for i in range(a.warmup):
-        step(i)
+        for l in layers:
+            launch(l, i)
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(a.steps):
-        starts[i].record(stream)
-        step(i)
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    kernel_ms = sum(per_launch) / len(per_launch)
-    ms_per_step = total_ms / a.steps
+    nl = len(layers)
+
+    def timed(fn, reps):
+        """ms per rep of ``fn(i)`` over ``reps`` reps, bracketed by one event pair on the stream."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    # the timed region: whole steps (every layer), nothing else on the stream
+    ms_per_step = timed(lambda i: [launch(l, i) for l in layers], a.steps)
+    # per-kernel durations: each layer's launches back to back, same rotation
+    if nl == 1:
+        layer_avg = [ms_per_step]
+    else:
+        layer_avg = [timed(lambda i, l=l: launch(l, i), a.steps) for l in layers]
 
     # warm (same buffers every step) secondary figure
-    for i in range(3):
-        step(0)
-    torch.cuda.synchronize()
-    wb = torch.cuda.Event(enable_timing=True)
-    we = torch.cuda.Event(enable_timing=True)
-    wb.record(stream)
-    for i in range(a.steps):
-        step(0)
-    we.record(stream)
-    torch.cuda.synchronize()
-    warm_ms = wb.elapsed_time(we) / a.steps
+    for _ in range(3):
+        for l in layers:
+            launch(l, 0)
+    warm_ms = timed(lambda i: [launch(l, 0) for l in layers], a.steps)
 
-    flops = layer_flops(L, N)
-    nbytes = layer_bytes(L, N, a.dtype)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    peak = PEAK[a.dtype]
-    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    peak_key = "i8" if int8 else dtype
+    unit = "TOP/s" if int8 else "TFLOP/s"
+    total_flops = 0
+    per_layer = []
+    for l, t in zip(layers, layer_avg):
+        L = l["L"]
+        fl = layer_flops(L, N)
+        by = layer_bytes(L, N, dtype)
+        kind, _ = bound(fl, by, peak_key)
+        total_flops += fl
+        if kind == "hbm":
+            ach, pk, u = by / (t * 1e-3) / 1e9, PEAK["hbm_bytes_per_s"] / 1e9, "GB/s"
+        else:
+            ach, pk, u = fl / (t * 1e-3) / 1e12, PEAK[peak_key] / 1e12, unit
+        per_layer.append(dict(name=L.name, algo=B.algo_name(l["chosen"]), ms=round(t, 5), bound=kind,
+                              achieved=round(ach, 2), peak=pk, unit=u, frac=round(ach / pk, 4), flops=fl, bytes=by))
+    dom = max(range(nl), key=lambda j: layer_avg[j])
+    d = per_layer[dom]
+    value = total_flops / (ms_per_step * 1e-3) / 1e12
 
     out = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": "TFLOP/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
@@ -157,46 +286,61 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": a.dtype,
-        "data": "synthetic (seeded N(0,1) activations, N(0,2/fan_in) weights)",
+        "dtype": dtype,
+        "data": "synthetic (seeded draws with each workload's distributions; no dataset, no trained weights)",
         "config": {
-            "workload": "resnet_3x3_256ch_56x56_n32", "n": N, "c": L.c, "k": L.k, "h": L.h, "w": L.w,
-            "r": L.r, "s": L.s, "stride": L.stride, "pad": L.pad, "layout": "NCHW",
-            "algo": B.algo_name(chosen), "dispatch": "fastrun_map" if a.algo == "auto" else "fixed",
-            "rotated_buffer_sets": nsets, "gflop_per_step": round(flops / 1e9, 3),
-            "mb_per_step": round(nbytes / 1e6, 2), "warm_ms_per_step": round(warm_ms, 5),
+            "workload": workload, "n": N, "layers": nl, "layout": layout,
+            "algo": "+".join(sorted({p["algo"] for p in per_layer})),
+            "dispatch": "fastrun_map" if a.algo == "auto" else "fixed", "rotated_buffer_sets": nsets,
+            "gflop_per_step": round(total_flops / 1e9, 3),
+            "mb_per_step": round(sum(p["bytes"] for p in per_layer) / 1e6, 2),
+            "warm_ms_per_step": round(warm_ms, 5),
         },
         "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": peak / 1e12,
-            "unit": "TFLOP/s",
-            "frac": round(achieved * 1e12 / peak, 4),
-            "traffic": None,
-            "kernel_avg_ms": round(kernel_ms, 5),
+            "bound": d["bound"],
+            "achieved": d["achieved"],
+            "peak": d["peak"],
+            "unit": d["unit"],
+            "frac": d["frac"],
+            "traffic": stored_traffic(workload, dtype),
+            "kernel": "%s (%s)" % (d["name"], d["algo"]),
+            "kernel_avg_ms": d["ms"],
+            "algorithmic_bytes": d["bytes"],
+            "algorithmic_flops": d["flops"],
         },
     }
+    if nl > 1:
+        out["layers"] = [{k: p[k] for k in ("name", "algo", "ms", "bound", "achieved", "unit", "frac")}
+                         for p in per_layer]
 
     if not a.no_cpu:
         import oracle
-        # bounded sample of the same workload: whole images, as many as the budget allows
-        t0 = time.perf_counter()
-        oracle.conv2d(pr.x[:1], pr.w, L.stride, L.pad, L.dil, L.groups)
-        t1 = time.perf_counter() - t0
+
+        def run_oracle(nimg):
+            t0 = time.perf_counter()
+            for l in layers:
+                L, pr = l["L"], l["pr"]
+                if int8:
+                    oracle.conv2d_int8_requant(pr.x[:nimg], pr.w, pr.scale, L.stride, L.pad, L.dil, L.groups)
+                else:
+                    oracle.conv2d(pr.x[:nimg], pr.w, L.stride, L.pad, L.dil, L.groups)
+            return time.perf_counter() - t0
+
+        # bounded sample of the same workload: whole images through every layer of the step
         nimg = 1
+        t1 = run_oracle(1)
         if 2 * t1 < a.cpu_budget:
             nimg = max(1, min(N, int(a.cpu_budget / t1) - 1))
             if nimg > 1:
-                t0 = time.perf_counter()
-                oracle.conv2d(pr.x[:nimg], pr.w, L.stride, L.pad, L.dil, L.groups)
-                t1 = time.perf_counter() - t0
-        sflops = layer_flops(L, nimg)
+                t1 = run_oracle(nimg)
+        sflops = sum(layer_flops(l["L"], nimg) for l in layers)
         out["cpu_baseline"] = {
             "value": round(sflops / t1 / 1e12, 6),
-            "unit": "TFLOP/s",
+            "unit": unit,
             "cores": oracle.max_threads(),
             "kind": "oracle",
-            "sample": "%d of %d images (%.2f GFLOP, fp64 loop nest, %.1f s)" % (nimg, N, sflops / 1e9, t1),
+            "sample": "%d of %d images through %d layer(s) (%.2f G%s, %s loop nest, %.1f s)" % (
+                nimg, N, nl, sflops / 1e9, "OP" if int8 else "FLOP", "int64" if int8 else "fp64", t1),
         }
     print(json.dumps(out), flush=True)
 

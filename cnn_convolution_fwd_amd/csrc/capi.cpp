@@ -275,7 +275,7 @@ bool map_lookup(const Prob& p, cfwd_algo* out) {
 cfwd_algo heuristic(const Prob& p) {
     // Stands in for the article's hand-written preference table (its figure is
     // not preserved): depthwise -> direct, 1x1 -> pointwise, else implicit GEMM.
-    if (p.depthwise()) return cfwd_algo{CFWD_ALGO_DIRECT, direct_supported(p, 1, nullptr) ? 1 : 0, 0.0f};
+    if (p.depthwise()) return cfwd_algo{CFWD_ALGO_DIRECT, direct_default_config(p), 0.0f};
     if (p.pointwise())
         for (int c = 0; c < pointwise_num_configs(); ++c)
             if (pointwise_supported(p, c, nullptr)) return cfwd_algo{CFWD_ALGO_POINTWISE, c, 0.0f};
@@ -292,7 +292,7 @@ bool family_default(const Prob& p, cfwd_algo_kind k, int* cfg) {
         return *cfg >= 0;
     }
     if (k == CFWD_ALGO_DIRECT) {
-        *cfg = direct_supported(p, 1, nullptr) ? 1 : 0;
+        *cfg = direct_default_config(p);
         return true;
     }
     for (int c = 0; c < num_configs(k); ++c)

@@ -225,8 +225,8 @@ template <> __device__ __forceinline__ void store_out4<float>(float* y, long lon
     *reinterpret_cast<float4*>(y + off) = make_float4(acc[0], acc[1], acc[2], acc[3]);
 }
 template <> __device__ __forceinline__ void store_out4<bf16_t>(bf16_t* y, long long off, f32x4 acc, float) {
-    const uint32_t lo = static_cast<uint32_t>(float_to_bf16(acc[0])) | (static_cast<uint32_t>(float_to_bf16(acc[1])) << 16);
-    const uint32_t hi = static_cast<uint32_t>(float_to_bf16(acc[2])) | (static_cast<uint32_t>(float_to_bf16(acc[3])) << 16);
+    const uint32_t lo = pack_bf16x2(acc[0], acc[1]);
+    const uint32_t hi = pack_bf16x2(acc[2], acc[3]);
     *reinterpret_cast<uint2*>(y + off) = make_uint2(lo, hi);
 }
 template <> __device__ __forceinline__ void store_out4<int8_t>(int8_t* y, long long off, i32x4 acc, float scale) {

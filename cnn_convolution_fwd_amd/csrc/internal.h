@@ -47,6 +47,7 @@ cfwd_status check_hip(hipError_t e, const char* what);
 
 // Direct summation (generic fallback; depthwise specialisation inside).
 int direct_num_configs();
+int direct_default_config(const Prob& p);  // fastest expected supported config
 bool direct_supported(const Prob& p, int cfg, std::string* why);
 cfwd_status direct_launch(const Prob& p, int cfg, const void* x, const void* w,
                           const float* scale, void* y, hipStream_t st);
@@ -106,12 +107,21 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
 }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi);
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  gfx950's
+// packed convert does exactly this (checked against the bit-level rule on all
+// 2^32 inputs), so both helpers use it.
 __device__ __forceinline__ uint16_t float_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return static_cast<uint16_t>(pack_bf16x2(f, 0.0f) & 0xffffu);
+}
+
+// Two fp32 values -> one 32-bit word of two bf16 (lo in bits 0-15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // int32 accumulator -> int8: clamp(rne(fp32(acc) * scale), -127, 127).

@@ -9,10 +9,16 @@
 //
 // config 0: generic -- one thread per output element, any shape / layout /
 //           dtype / groups.  The correctness fallback.
-// config 1: depthwise 3x3, stride 1, dilation 1, NCHW, W a multiple of the
-//           vector width -- each thread owns a strip of VEC columns and walks
-//           ROWS output rows down it, keeping the three input rows it needs in
-//           registers (a register-blocked sliding window).
+// configs 1-6: depthwise 3x3, stride 1, pad 1, dilation 1, NCHW, W a
+//           multiple of the vector -- each thread owns a strip of one 16-byte
+//           (configs 1-4) or 8-byte (configs 5-6) vector of columns and RB
+//           output rows (RB = 1, 2, 4, 8, 2, 4).  It
+//           issues all RB + 2 input-row loads before computing (many bytes in
+//           flight per thread, which is what an HBM-bound kernel needs), takes
+//           the left / right neighbour columns from the adjacent lanes with a
+//           cross-lane shuffle instead of extra loads, and writes the outputs
+//           with streaming (non-temporal) stores.  Every input byte comes from
+//           HBM once: the halo rows of a strip are the rows adjacent lanes load.
 #include "internal.h"
 
 namespace cfwd {
@@ -94,101 +100,180 @@ __global__ __launch_bounds__(256) void direct_generic_i8(const int8_t* __restric
     }
 }
 
-// ------------------------------------------------------------ config 1
-// Depthwise 3x3, stride 1, dilation 1, NCHW.  VEC output columns per thread
-// (16 bytes of input per row), ROWS output rows per thread.
+// ------------------------------------------------------------ configs 1-6
+// Each thread holds NW 32-bit words of every input row it needs (NW = 4: a
+// 16-byte vector, NW = 2: 8 bytes): VPT = NW (fp32) or 2 NW (bf16) columns.
 
-template <typename T> struct Vec16;
-template <> struct Vec16<float> {
-    static constexpr int N = 4;
-    static __device__ __forceinline__ void load(const float* p, float* v) {
-        const float4 q = *reinterpret_cast<const float4*>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
-    }
-    static __device__ __forceinline__ void store(float* p, const float* v) {
-        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-    }
+template <typename T> struct Words;
+template <> struct Words<float> {
+    static constexpr int PER_WORD = 1;
+    static __device__ __forceinline__ float elem(const uint32_t* wd, int e) { return __uint_as_float(wd[e]); }
+    static __device__ __forceinline__ float first(uint32_t word) { return __uint_as_float(word); }
+    static __device__ __forceinline__ float last(uint32_t word) { return __uint_as_float(word); }
+    static __device__ __forceinline__ uint32_t pack(const float* v, int i) { return __float_as_uint(v[i]); }
 };
-template <> struct Vec16<bf16_t> {
-    static constexpr int N = 8;
-    static __device__ __forceinline__ void load(const bf16_t* p, float* v) {
+template <> struct Words<bf16_t> {
+    static constexpr int PER_WORD = 2;
+    static __device__ __forceinline__ float elem(const uint32_t* wd, int e) {
+        const uint32_t w = wd[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    // a word's first element sits in its low half, its last in the high half
+    static __device__ __forceinline__ float first(uint32_t word) { return __uint_as_float(word << 16); }
+    static __device__ __forceinline__ float last(uint32_t word) { return __uint_as_float(word & 0xffff0000u); }
+    static __device__ __forceinline__ uint32_t pack(const float* v, int i) { return pack_bf16x2(v[2 * i], v[2 * i + 1]); }
+};
+
+template <int NW> struct RawVec;
+template <> struct RawVec<4> {
+    static __device__ __forceinline__ void load(const void* p, uint32_t* d) {
         const uint4 q = *reinterpret_cast<const uint4*>(p);
-        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(u[i] << 16);
-            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-        }
+        d[0] = q.x; d[1] = q.y; d[2] = q.z; d[3] = q.w;
     }
-    static __device__ __forceinline__ void store(bf16_t* p, const float* v) {
-        uint32_t u[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            u[i] = static_cast<uint32_t>(float_to_bf16(v[2 * i])) |
-                   (static_cast<uint32_t>(float_to_bf16(v[2 * i + 1])) << 16);
-        *reinterpret_cast<uint4*>(p) = make_uint4(u[0], u[1], u[2], u[3]);
+    static __device__ __forceinline__ void store_nt(void* p, const uint32_t* d) {
+        typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+        const u32x4_t v = {d[0], d[1], d[2], d[3]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+    }
+};
+template <> struct RawVec<2> {
+    static __device__ __forceinline__ void load(const void* p, uint32_t* d) {
+        const uint2 q = *reinterpret_cast<const uint2*>(p);
+        d[0] = q.x; d[1] = q.y;
+    }
+    static __device__ __forceinline__ void store_nt(void* p, const uint32_t* d) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        const u32x2_t v = {d[0], d[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2_t*>(p));
     }
 };
 
-template <typename T, int ROWS>
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T, int NW> constexpr int dw_vpt() { return NW * Words<T>::PER_WORD; }
+
+// Workgroup = SPB whole strips (a strip = one plane n*C + c and one band of
+// RB output rows, all `cols` column vectors of it), SPB = floor(256 / cols),
+// so a thread's left and right neighbour columns always belong to threads
+// of the same workgroup: they are exchanged through LDS.  Every load is
+// issued up front and nothing branches: rows outside the image are read
+// clamped (in bounds) and zeroed with selects; threads past the last strip
+// work on a clamped strip and store nothing.  Outputs are written with
+// streaming (non-temporal) stores.
+template <typename T, int RB, int NW>
 __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, const T* __restrict__ w,
-                                                       T* __restrict__ y, DirectArgs a, int col_groups,
-                                                       int row_bands, long long total) {
-    constexpr int V = Vec16<T>::N;
-    const long long idx = blockIdx.x * 256LL + threadIdx.x;
-    if (idx >= total) return;
-    const int cgp = static_cast<int>(idx % col_groups);
-    long long t = idx / col_groups;
-    const int band = static_cast<int>(t % row_bands);
-    const long long plane = t / row_bands;  // n * C + c
-    const int c = static_cast<int>(plane % a.C);
-    const int n = static_cast<int>(plane / a.C);
-    const T* xp = x + n * a.x_img + static_cast<long long>(c) * a.H * a.W;
-    T* yp = y + n * a.y_img + static_cast<long long>(c) * a.OH * a.OW;
+                                                       T* __restrict__ y, int C, int H, int W, long long x_img,
+                                                       long long y_img, int cols, int bands, int strips) {
+    using WD = Words<T>;
+    constexpr int V = dw_vpt<T, NW>();
+    __shared__ uint32_t first_w[RB + 2][256], last_w[RB + 2][256];
+    const int tid = threadIdx.x;
+    const int spb = 256 / cols;
+    const int sl = tid / cols;
+    const int cg = tid - sl * cols;
+    const int strip_raw = static_cast<int>(blockIdx.x) * spb + sl;
+    const bool valid = sl < spb && strip_raw < strips;
+    const int strip = min(strip_raw, strips - 1);
+    const int band = strip % bands;
+    const int plane = strip / bands;
+    const int c = plane % C;
+    const int n = plane / C;
+    const long long plane_off = static_cast<long long>(c) * H * W;
+    const T* xp = x + n * x_img + plane_off;
+    T* yp = y + n * y_img + plane_off;
+    const int ow0 = cg * V;
+    const int oh0 = band * RB;
+
     float wk[9];
 #pragma unroll
     for (int i = 0; i < 9; ++i) wk[i] = Elem<T>::to_f(w[c * 9 + i]);
-    const int ow0 = cgp * V;
-    const int oh0 = band * ROWS;
-    // rows[j][0..V+1] holds input columns ow0-1 .. ow0+V of input row (oh0 - 1 + j)
-    float rows[3][V + 2];
-    auto load_row = [&](int ih, float* dst) {
-        if (ih < 0 || ih >= a.H) {
+    // input rows oh0 - 1 .. oh0 + RB, this thread's NW words of columns
+    uint32_t raw[RB + 2][NW];
 #pragma unroll
-            for (int i = 0; i < V + 2; ++i) dst[i] = 0.0f;
-            return;
+    for (int j = 0; j < RB + 2; ++j) {
+        const int ih = min(max(oh0 - 1 + j, 0), H - 1);
+        RawVec<NW>::load(xp + (ih * W + ow0), raw[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < RB + 2; ++j) {
+        const int ih = oh0 - 1 + j;
+        const bool in = ih >= 0 && ih < H;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) raw[j][q] = in ? raw[j][q] : 0u;
+        first_w[j][tid] = raw[j][0];
+        last_w[j][tid] = raw[j][NW - 1];
+    }
+    __syncthreads();
+    // neighbour columns ow0 - 1 and ow0 + V (zero at the image border)
+    const int tl = max(tid - 1, 0), tr = min(tid + 1, 255);
+    float left[RB + 2], right[RB + 2];
+#pragma unroll
+    for (int j = 0; j < RB + 2; ++j) {
+        const float l = WD::last(last_w[j][tl]);
+        const float r = WD::first(first_w[j][tr]);
+        left[j] = (cg > 0) ? l : 0.0f;
+        right[j] = (cg < cols - 1) ? r : 0.0f;
+    }
+    // bf16: weight pairs (w0, w1) and (w1, w2) of each filter row, packed
+    bf16x2_t w01[3], w12[3];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const uint32_t a0 = pack_bf16x2(wk[3 * r], 0.0f), a1 = pack_bf16x2(wk[3 * r + 1], 0.0f),
+                           a2 = pack_bf16x2(wk[3 * r + 2], 0.0f);
+            w01[r] = __builtin_bit_cast(bf16x2_t, a0 | (a1 << 16));
+            w12[r] = __builtin_bit_cast(bf16x2_t, a1 | (a2 << 16));
         }
-        const T* rp = xp + static_cast<long long>(ih) * a.W;
-        Vec16<T>::load(rp + ow0, dst + 1);
-        dst[0] = (ow0 > 0) ? Elem<T>::to_f(rp[ow0 - 1]) : 0.0f;
-        dst[V + 1] = (ow0 + V < a.W) ? Elem<T>::to_f(rp[ow0 + V]) : 0.0f;
-    };
-    load_row(oh0 - 1, rows[0]);
-    load_row(oh0, rows[1]);
+    }
+
 #pragma unroll
-    for (int i = 0; i < ROWS; ++i) {
+    for (int i = 0; i < RB; ++i) {
         const int oh = oh0 + i;
-        if (oh >= a.OH) break;
-        load_row(oh + 1, rows[(i + 2) % 3]);
-        const float* r0 = rows[i % 3];
-        const float* r1 = rows[(i + 1) % 3];
-        const float* r2 = rows[(i + 2) % 3];
         float out[V];
+        if constexpr (sizeof(T) == 2) {
+            // bf16: the pair (e, e + 1) of an even e is one 32-bit word, so
+            // each filter row costs one two-wide dot product plus one FMA:
+            //   even e = 2m: dot(word m, (w1, w2)) + x[e - 1] * w0
+            //   odd  e = 2m + 1: dot(word m, (w0, w1)) + x[e + 1] * w2
 #pragma unroll
-        for (int j = 0; j < V; ++j) {
-            float acc = 0.0f;
-            acc = fmaf(r0[j], wk[0], acc);
-            acc = fmaf(r0[j + 1], wk[1], acc);
-            acc = fmaf(r0[j + 2], wk[2], acc);
-            acc = fmaf(r1[j], wk[3], acc);
-            acc = fmaf(r1[j + 1], wk[4], acc);
-            acc = fmaf(r1[j + 2], wk[5], acc);
-            acc = fmaf(r2[j], wk[6], acc);
-            acc = fmaf(r2[j + 1], wk[7], acc);
-            acc = fmaf(r2[j + 2], wk[8], acc);
-            out[j] = acc;
+            for (int m = 0; m < NW; ++m) {
+                float ev = 0.0f, od = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    const uint32_t* wd = raw[i + r];
+                    const float xm1 = (m == 0) ? left[i + r] : __uint_as_float(wd[m - 1] & 0xffff0000u);
+                    const float xp2 = (m == NW - 1) ? right[i + r] : __uint_as_float(wd[m + 1] << 16);
+                    ev = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wd[m]), w12[r], ev, false);
+                    ev = fmaf(xm1, wk[3 * r], ev);
+                    od = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, wd[m]), w01[r], od, false);
+                    od = fmaf(xp2, wk[3 * r + 2], od);
+                }
+                out[2 * m] = ev;
+                out[2 * m + 1] = od;
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) {
+                float acc = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    const uint32_t* wd = raw[i + r];
+                    const float a0 = (e == 0) ? left[i + r] : WD::elem(wd, e - 1);
+                    const float a1 = WD::elem(wd, e);
+                    const float a2 = (e == V - 1) ? right[i + r] : WD::elem(wd, e + 1);
+                    acc = fmaf(a0, wk[3 * r], acc);
+                    acc = fmaf(a1, wk[3 * r + 1], acc);
+                    acc = fmaf(a2, wk[3 * r + 2], acc);
+                }
+                out[e] = acc;
+            }
         }
-        Vec16<T>::store(yp + static_cast<long long>(oh) * a.OW + ow0, out);
+        if (valid && oh < H) {
+            uint32_t o[NW];
+#pragma unroll
+            for (int q = 0; q < NW; ++q) o[q] = WD::pack(out, q);
+            RawVec<NW>::store_nt(yp + (oh * W + ow0), o);
+        }
     }
 }
 
@@ -207,10 +292,11 @@ unsigned grid_for(long long total) {
     return static_cast<unsigned>(blocks);
 }
 
-constexpr int kDwRows = 8;
+// (RB, NW) of configs 1-6
+constexpr int kDwRB[7] = {0, 1, 2, 4, 8, 2, 4};
+constexpr int kDwNW[7] = {0, 4, 4, 4, 4, 2, 2};
 
-bool depthwise_fast_ok(const Prob& p, std::string* why) {
-    const int V = (p.dtype == CFWD_F32) ? 4 : 8;
+bool depthwise_fast_ok(const Prob& p, int cfg, std::string* why) {
     if (!p.depthwise() || p.r != 3 || p.s != 3 || p.sh != 1 || p.sw != 1 || p.dh != 1 || p.dw != 1 ||
         p.ph != 1 || p.pw != 1) {
         if (why) *why = "depthwise fast path needs G=C=K, 3x3, stride 1, pad 1, dilation 1";
@@ -220,20 +306,58 @@ bool depthwise_fast_ok(const Prob& p, std::string* why) {
         if (why) *why = "depthwise fast path needs NCHW fp32 or bf16";
         return false;
     }
-    if (p.w % V != 0) {
-        if (why) *why = "depthwise fast path needs W divisible by the vector width";
+    const int V = kDwNW[cfg] * (p.dtype == CFWD_F32 ? 1 : 2);
+    if (p.w % V != 0 || p.w / V > 256) {
+        if (why) *why = "depthwise fast path needs W a multiple of the vector width, at most 256 vectors";
+        return false;
+    }
+    if (static_cast<long long>(p.h) * p.w >= (1LL << 31) || static_cast<long long>(p.n) * p.c * p.h >= (1LL << 31)) {
+        if (why) *why = "depthwise fast path needs 32-bit plane offsets and strip ids";
         return false;
     }
     return true;
 }
 
+template <typename T, int RB, int NW>
+cfwd_status launch_dw(const Prob& p, const void* x, const void* w, void* y, hipStream_t st) {
+    constexpr int V = dw_vpt<T, NW>();
+    const int cols = p.w / V;
+    const int bands = (p.oh + RB - 1) / RB;
+    const long long strips = static_cast<long long>(p.n) * p.c * bands;
+    const int spb = 256 / cols;  // whole strips per workgroup (cols <= 256 is checked)
+    if (strips >= (1LL << 31)) return set_error(CFWD_ERR_UNSUPPORTED, "depthwise: too many strips");
+    const unsigned blocks = static_cast<unsigned>((strips + spb - 1) / spb);
+    depthwise3x3_s1<T, RB, NW><<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const T*>(w),
+                                                     static_cast<T*>(y), p.c, p.h, p.w, p.x_img, p.y_img, cols,
+                                                     bands, static_cast<int>(strips));
+    return check_hip(hipGetLastError(), "depthwise3x3_s1 launch");
+}
+
+template <typename T>
+cfwd_status launch_dw_cfg(const Prob& p, int cfg, const void* x, const void* w, void* y, hipStream_t st) {
+    switch (cfg) {
+        case 1: return launch_dw<T, 1, 4>(p, x, w, y, st);
+        case 2: return launch_dw<T, 2, 4>(p, x, w, y, st);
+        case 3: return launch_dw<T, 4, 4>(p, x, w, y, st);
+        case 4: return launch_dw<T, 8, 4>(p, x, w, y, st);
+        case 5: return launch_dw<T, 2, 2>(p, x, w, y, st);
+        default: return launch_dw<T, 4, 2>(p, x, w, y, st);
+    }
+}
+
 }  // namespace
 
-int direct_num_configs() { return 2; }
+int direct_num_configs() { return 7; }
+
+int direct_default_config(const Prob& p) {
+    if (depthwise_fast_ok(p, 2, nullptr)) return 2;
+    if (depthwise_fast_ok(p, 5, nullptr)) return 5;
+    return 0;
+}
 
 bool direct_supported(const Prob& p, int cfg, std::string* why) {
     if (cfg == 0) return true;
-    if (cfg == 1) return depthwise_fast_ok(p, why);
+    if (cfg >= 1 && cfg <= 6) return depthwise_fast_ok(p, cfg, why);
     if (why) *why = "no such direct config";
     return false;
 }
@@ -241,21 +365,9 @@ bool direct_supported(const Prob& p, int cfg, std::string* why) {
 cfwd_status direct_launch(const Prob& p, int cfg, const void* x, const void* w, const float* scale, void* y,
                           hipStream_t st) {
     const DirectArgs a = make_args(p);
-    if (cfg == 1) {
-        const int V = (p.dtype == CFWD_F32) ? 4 : 8;
-        const int col_groups = p.w / V;
-        const int row_bands = (p.oh + kDwRows - 1) / kDwRows;
-        const long long total = static_cast<long long>(p.n) * p.c * row_bands * col_groups;
-        const unsigned blocks = static_cast<unsigned>((total + 255) / 256);
-        if (p.dtype == CFWD_F32)
-            depthwise3x3_s1<float, kDwRows><<<blocks, 256, 0, st>>>(
-                static_cast<const float*>(x), static_cast<const float*>(w), static_cast<float*>(y), a, col_groups,
-                row_bands, total);
-        else
-            depthwise3x3_s1<bf16_t, kDwRows><<<blocks, 256, 0, st>>>(
-                static_cast<const bf16_t*>(x), static_cast<const bf16_t*>(w), static_cast<bf16_t*>(y), a,
-                col_groups, row_bands, total);
-        return check_hip(hipGetLastError(), "depthwise3x3_s1 launch");
+    if (cfg >= 1 && cfg <= 6) {
+        if (p.dtype == CFWD_F32) return launch_dw_cfg<float>(p, cfg, x, w, y, st);
+        return launch_dw_cfg<bf16_t>(p, cfg, x, w, y, st);
     }
     const long long total = static_cast<long long>(p.n) * p.k * p.oh * p.ow;
     const unsigned blocks = grid_for(total);

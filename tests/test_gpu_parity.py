@@ -38,6 +38,8 @@ SMALL = [
     ("5x5_d2", 1, 12, 15, 14, 20, 5, 5, 1, 4, 2, 1),
     ("grouped", 2, 12, 10, 11, 18, 3, 3, 1, 1, 1, 3),
     ("depthwise", 2, 16, 12, 16, 16, 3, 3, 1, 1, 1, 16),
+    ("dw_wave_split", 3, 5, 9, 24, 5, 3, 3, 1, 1, 1, 5),
+    ("dw_w20", 2, 3, 7, 20, 3, 3, 3, 1, 1, 1, 3),
     ("stem7x7s2", 2, 3, 20, 22, 8, 7, 7, 2, 3, 1, 1),
     ("tiny", 1, 1, 1, 1, 1, 1, 1, 1, 0, 1, 1),
     ("asym", 1, 9, 7, 33, 130, 3, 1, (2, 1), (0, 1), 1, 1),
