@@ -204,20 +204,23 @@ def main():
                            algo_arg=algo_arg, wp=wp, sbytes=sbytes,
                            scratch=torch.empty(max(sbytes, 1), dtype=torch.uint8, device=dev)))
 
-    set_bytes = sum(l["x0"].numel() * l["x0"].element_size() + l["y0"].numel() * l["y0"].element_size()
-                    for l in layers)
-    nsets = a.sets or min(MAX_SETS, max(2, -(-ROTATE_BYTES // set_bytes) + 1))
+    # every layer rotates over its own buffer sets, > 512 MB per layer, so a
+    # layer timed alone (per-kernel figures) cannot read from the cache either
     for l in layers:
-        l["xs"] = [l["x0"]] + [l["x0"].clone() for _ in range(nsets - 1)]
-        l["ys"] = [l["y0"]] + [torch.empty_like(l["y0"]) for _ in range(nsets - 1)]
+        set_bytes = l["x0"].numel() * l["x0"].element_size() + l["y0"].numel() * l["y0"].element_size()
+        ns = a.sets or min(MAX_SETS, max(2, -(-ROTATE_BYTES // set_bytes) + 1))
+        l["nsets"] = ns
+        l["xs"] = [l["x0"]] + [l["x0"].clone() for _ in range(ns - 1)]
+        l["ys"] = [l["y0"]] + [torch.empty_like(l["y0"]) for _ in range(ns - 1)]
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
     def launch(l, i):
-        st = B.conv2d_fwd_raw(l["desc"], l["algo_arg"], l["xs"][i % nsets].data_ptr(), l["w"].data_ptr(),
+        ns = l["nsets"]
+        st = B.conv2d_fwd_raw(l["desc"], l["algo_arg"], l["xs"][i % ns].data_ptr(), l["w"].data_ptr(),
                               l["wp"].data_ptr() if l["wp"] is not None else 0,
                               l["scale"].data_ptr() if l["scale"] is not None else 0,
-                              l["ys"][i % nsets].data_ptr(), l["scratch"].data_ptr() if l["sbytes"] else 0,
+                              l["ys"][i % ns].data_ptr(), l["scratch"].data_ptr() if l["sbytes"] else 0,
                               l["sbytes"], sptr)
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
@@ -291,7 +294,7 @@ def main():
         "config": {
             "workload": workload, "n": N, "layers": nl, "layout": layout,
             "algo": "+".join(sorted({p["algo"] for p in per_layer})),
-            "dispatch": "fastrun_map" if a.algo == "auto" else "fixed", "rotated_buffer_sets": nsets,
+            "dispatch": "fastrun_map" if a.algo == "auto" else "fixed", "rotated_buffer_sets": max(l["nsets"] for l in layers),
             "gflop_per_step": round(total_flops / 1e9, 3),
             "mb_per_step": round(sum(p["bytes"] for p in per_layer) / 1e6, 2),
             "warm_ms_per_step": round(warm_ms, 5),

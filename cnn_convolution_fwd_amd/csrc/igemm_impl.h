@@ -331,19 +331,11 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int lrow = lane % FR;  // A row / B column this lane feeds
     const int lgrp = lane / FR;  // K group (FR=16: slot 0..3; FR=32: half 0..1)
 
-    // ---- XCD-aware work order.  Workgroups are dispatched round-robin over
-    // the 8 XCDs; give each XCD a contiguous range of the linear tile order,
-    // in which the output-channel tiles of one pixel tile are adjacent (they
-    // share the input patch in that XCD's L2) and consecutive pixel tiles are
-    // spatial neighbours (they share halo rows).
-    int lin;
-    {
-        const int total = static_cast<int>(gridDim.x);
-        const int bid = static_cast<int>(blockIdx.x);
-        const int xcd = bid & 7, local = bid >> 3;
-        const int per = total >> 3, rem = total & 7;
-        lin = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
-    }
+    // ---- XCD-aware work order: in the linear tile order the output-channel
+    // tiles of one pixel tile are adjacent (they share the input patch in an
+    // XCD's L2) and consecutive pixel tiles are spatial neighbours (they share
+    // halo rows).
+    int lin = xcd_linear(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int kt = lin % a.ntk;
     lin /= a.ntk;
     const int ntm = a.tiles_w * a.tiles_h * a.tiles_n;

@@ -109,6 +109,16 @@ __device__ __forceinline__ float bf16_to_float(uint16_t b) {
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi);
 
+// XCD-aware work order: workgroups are dispatched round-robin over the 8
+// XCDs (each with its own L2), so give each XCD a contiguous range of the
+// logical work order; logically adjacent work items (which share input rows
+// or weights) then run at about the same time on the same L2.
+__device__ __forceinline__ int xcd_linear(int bid, int total) {
+    const int xcd = bid & 7, local = bid >> 3;
+    const int per = total >> 3, rem = total & 7;
+    return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
 // fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  gfx950's
 // packed convert does exactly this (checked against the bit-level rule on all
 // 2^32 inputs), so both helpers use it.

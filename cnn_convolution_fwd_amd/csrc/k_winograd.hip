@@ -22,7 +22,8 @@
 //   input    U[xi][chunk][tile][CK] = (B^T d B)[xi]: one thread per (tile,
 //            channel group), written channel-contiguous;
 //   gemm     per workgroup a block of TB tiles x KB output channels for all
-//            alpha^2 positions (split over the four waves), reduced over the
+//            alpha^2 positions (split over the waves: four for F(2x2), eight
+//            for F(6x6)), reduced over the
 //            input channels on the matrix cores; the alpha^2 products of each
 //            (tile, channel) are then exchanged through LDS in channel slices
 //            and transformed back, Y = A^T M A, straight into the output.

@@ -35,6 +35,8 @@ SMALL = [
     ("3x3_s2", 1, 35, 9, 30, 70, 3, 3, 2, 1, 1, 1),
     ("1x1", 3, 16, 8, 8, 16, 1, 1, 1, 0, 1, 1),
     ("1x1_s2", 2, 40, 14, 14, 72, 1, 1, 2, 0, 1, 1),
+    ("1x1_ragged", 3, 20, 6, 10, 40, 1, 1, 1, 0, 1, 1),
+    ("1x1_wide_k", 2, 64, 8, 8, 300, 1, 1, 1, 0, 1, 1),
     ("5x5_d2", 1, 12, 15, 14, 20, 5, 5, 1, 4, 2, 1),
     ("grouped", 2, 12, 10, 11, 18, 3, 3, 1, 1, 1, 3),
     ("depthwise", 2, 16, 12, 16, 16, 3, 3, 1, 1, 1, 16),
