@@ -60,6 +60,14 @@ cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipSt
 cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp,
                          const float* scale, void* y, hipStream_t st);
 int igemm_default_config(const Prob& p);
+// gather form of implicit GEMM for few input channels (implicit-GEMM configs
+// after the tiled ones)
+int lowc_num_configs();
+bool lowc_supported(const Prob& p, int cfg, std::string* why);
+size_t lowc_filter_bytes(const Prob& p, int cfg);
+cfwd_status lowc_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
+cfwd_status lowc_launch(const Prob& p, int cfg, const void* x, const void* wp, const float* scale, void* y,
+                        hipStream_t st);
 
 // Pointwise (1x1) path.
 int pointwise_num_configs();

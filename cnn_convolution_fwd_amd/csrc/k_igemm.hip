@@ -4,9 +4,12 @@
 
 namespace cfwd {
 
-int igemm_num_configs() { return ig::kNumCfgs; }
+// Configs 0 .. kNumCfgs-1: the tiled kernel of igemm_impl.h; the next
+// lowc_num_configs(): the gather form for few input channels (k_lowc.hip).
+int igemm_num_configs() { return ig::kNumCfgs + lowc_num_configs(); }
 
 bool igemm_supported(const Prob& p, int cfg, std::string* why) {
+    if (cfg >= ig::kNumCfgs && cfg < igemm_num_configs()) return lowc_supported(p, cfg - ig::kNumCfgs, why);
     if (cfg < 0 || cfg >= ig::kNumCfgs) {
         if (why) *why = "implicit GEMM: no such config";
         return false;
@@ -16,12 +19,14 @@ bool igemm_supported(const Prob& p, int cfg, std::string* why) {
 }
 
 size_t igemm_filter_bytes(const Prob& p, int cfg) {
+    if (cfg >= ig::kNumCfgs) return lowc_filter_bytes(p, cfg - ig::kNumCfgs);
     ig::Geo g;
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, nullptr)) return 0;
     return ig::filter_bytes(p, ig::kCfgs[cfg], g);
 }
 
 cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
+    if (cfg >= ig::kNumCfgs) return lowc_prepare(p, cfg - ig::kNumCfgs, w, wp, st);
     ig::Geo g;
     std::string why;
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
@@ -34,6 +39,7 @@ cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipSt
 
 cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp, const float* scale, void* y,
                          hipStream_t st) {
+    if (cfg >= ig::kNumCfgs) return lowc_launch(p, cfg - ig::kNumCfgs, x, wp, scale, y, st);
     ig::Geo g;
     std::string why;
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
@@ -48,6 +54,8 @@ cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp, 
 // work (pixels and channels past the problem's edges), ties to the larger
 // tile (fewer re-reads of the weights and the patch halo).
 int igemm_default_config(const Prob& p) {
+    // image stems (a handful of input channels): the gather form
+    if (p.cg <= 4 && lowc_supported(p, 0, nullptr)) return ig::kNumCfgs + (p.k > 32 ? 4 : 3);
     int best = -1;
     double best_score = -1.0;
     for (int c = 0; c < ig::kNumCfgs; ++c) {
