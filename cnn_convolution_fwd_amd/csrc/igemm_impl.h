@@ -385,10 +385,10 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         if (u < nunits) {
             int j, tn, prow, pcol;
             if (STG == 1) {
-                const int cb = u % ncb;
-                const int t = u / ncb;
-                const int row = t % nrows;
-                j = t / nrows;
+                j = u & 3;
+                const int t = u >> 2;
+                const int cb = t % ncb;
+                const int row = t / ncb;
                 tn = row / a.PH;
                 prow = row - tn * a.PH;
                 pcol = (cb0 + cb) * PP - iw0;
@@ -450,11 +450,15 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         for (int i = 0; i < MAXU; ++i) {
             if (u_j[i] < 0) continue;
             if (STG == 1) {
+                // pixels outside this patch row go to a per-thread dummy slot
+                // past both patch buffers (no branch per pixel)
+                uint8_t* dummy = lds + 2 * patch_bytes + tid * 16;
 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
                     const int col = u_pc[i] + p;
-                    if (col < 0 || col >= a.PW) continue;  // outside this patch row
-                    *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i] + p, u_j[i])) = wide_pick<WD::SZ>(stg[i], p);
+                    const bool ok = col >= 0 && col < a.PW;
+                    uint8_t* dst = ok ? base + lds_slot<FR>(u_q[i] + p, u_j[i]) : dummy;
+                    *reinterpret_cast<uint4*>(dst) = wide_pick<WD::SZ>(stg[i], p);
                 }
             } else {
                 *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i], u_j[i])) = stg[i][0];
@@ -907,7 +911,8 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     g->ntk = (p.kg + c.nt() - 1) / c.nt();
     // two patch buffers; the epilogue reuses them for an 8-byte offset per
     // register-tile pixel row
-    g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64), static_cast<size_t>(c.pixels()) * 8);
+    g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64) + static_cast<size_t>(c.threads()) * 16,
+                            static_cast<size_t>(c.pixels()) * 8);
     g->stg = 0;
     {
         const int sz = wide_sz(p);
