@@ -236,6 +236,8 @@ template <> __device__ __forceinline__ void store_out4<int8_t>(int8_t* y, long l
     *reinterpret_cast<uint32_t*>(y + off) = v;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr int kMaxUnitsPerThread = 8;
 
 // LDS byte offset of 16-byte slot j of patch pixel q.  The slot is XORed with
@@ -709,6 +711,50 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         }
     }
 
+    // ---- epilogue, transposed through LDS (16-bit outputs, NCHW, tiles of
+    // whole output rows): the accumulators hold, per lane, one output channel
+    // of several 4-pixel groups, so storing them directly would scatter every
+    // store instruction over 64 channel planes.  Instead the tile is written
+    // to LDS as [channel][tile pixel] (row pitch padded by 16 bytes) and then
+    // stored row by row: a channel's tile pixels are contiguous in NCHW, so
+    // consecutive lanes write consecutive 16-byte pieces.
+    if constexpr (sizeof(T) == 2 && XB == 1 && FR == 32) {
+        const bool rows_ok = a.TN == 1 && a.TW == a.OW && oh0 + a.TH <= a.OH && (tile_pix % 8) == 0 &&
+                             (a.OW % 8) == 0;
+        if (rows_ok) {
+            const int pitch = tile_pix * 2 + 16;  // bytes per channel row in LDS
+#pragma unroll
+            for (int nf = 0; nf < FN; ++nf) {
+                const int kk = (wn * FN + nf) * FR + lrow;  // channel within the tile
+#pragma unroll
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int grp = 0; grp < FT::NACC / 4; ++grp) {
+                        const int p0 = (wm * FM + f) * FR + 8 * grp + 4 * lgrp;
+                        if (p0 < tile_pix) {
+                            const uint2 q = make_uint2(pack_bf16x2(acc[f][nf][grp * 4 + 0], acc[f][nf][grp * 4 + 1]),
+                                                       pack_bf16x2(acc[f][nf][grp * 4 + 2], acc[f][nf][grp * 4 + 3]));
+                            *reinterpret_cast<uint2*>(lds + kk * pitch + p0 * 2) = q;
+                        }
+                    }
+            }
+            __syncthreads();
+            const int pieces = tile_pix / 8;  // 16-byte pieces per channel row
+            const long long OHW = static_cast<long long>(a.OH) * a.OW;
+            uint8_t* ybase = static_cast<uint8_t*>(a.y) +
+                             (static_cast<long long>(n0) * a.y_img + static_cast<long long>(oh0) * a.OW) * 2;
+            const int kbase = g * a.Kg + kt * NT;
+            const int nk = min(NT, a.Kg - kt * NT);  // valid channels of this tile
+            for (int q = tid; q < nk * pieces; q += NTHR) {
+                const int kk = q / pieces, j = q - (q / pieces) * pieces;
+                const uint4 v = *reinterpret_cast<const uint4*>(lds + kk * pitch + j * 16);
+                const u32x4_t w = {v.x, v.y, v.z, v.w};
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(ybase + (kbase + kk) * OHW * 2 + j * 16));
+            }
+            return;
+        }
+    }
+
     // ---- epilogue: convert and store in the caller's layout.  The patch
     // buffers are free now (the last chunk ended with a barrier); they hold a
     // table of each tile pixel's output offset (without the channel term),
@@ -736,6 +782,35 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const bool vec4 = (XB == 1) && (a.TW % 4 == 0) && (a.OW % 4 == 0);
     const long long OHW = static_cast<long long>(a.OH) * a.OW;
     constexpr int NG = FT::NACC / 4;  // groups of 4 consecutive rows per accumulator
+    // rows of group (f, grp): FR=16: 4*lgrp + v; FR=32: 8*grp + 4*lgrp + v
+    auto row0 = [&](int f, int grp) { return (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp); };
+    if (vec4) {
+        // four consecutive pixels of one channel per store: read this lane's
+        // FM*NG pixel-row offsets in one batch, then issue every store
+        long long o[FM][NG];
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int grp = 0; grp < NG; ++grp) o[f][grp] = otab[row0(f, grp)];
+#pragma unroll
+        for (int nf = 0; nf < FN; ++nf) {
+            const int kl = kt * NT + (wn * FN + nf) * FR + lrow;
+            if (kl >= a.Kg) continue;
+            const int k = g * a.Kg + kl;
+            const float sc = (a.scale != nullptr) ? a.scale[k] : 1.0f;
+            const long long coff = k * OHW;
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int grp = 0; grp < NG; ++grp) {
+                    typename Mma<T>::acc_t quad;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) quad[v] = acc[f][nf][grp * 4 + v];
+                    if (o[f][grp] >= 0) store_out4<T>(y, o[f][grp] + coff, quad, sc);
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int nf = 0; nf < FN; ++nf) {
         const int kl = kt * NT + (wn * FN + nf) * FR + lrow;
@@ -747,20 +822,14 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         for (int f = 0; f < FM; ++f) {
 #pragma unroll
             for (int grp = 0; grp < NG; ++grp) {
-                // rows of this group: FR=16: 4*lgrp + v; FR=32: 8*grp + 4*lgrp + v
-                const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
+                const int p0 = row0(f, grp);
                 typename Mma<T>::acc_t quad;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) quad[v] = acc[f][nf][grp * 4 + v];
-                if (vec4) {
-                    const long long o = otab[p0];
-                    if (o >= 0) store_out4<T>(y, o + coff, quad, sc);
-                } else {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const long long o = otab[p0 + v];
-                        if (o >= 0) store_out<T>(y, o + coff, quad, v, sc);
-                    }
+                for (int v = 0; v < 4; ++v) {
+                    const long long ov = otab[p0 + v];
+                    if (ov >= 0) store_out<T>(y, ov + coff, quad, v, sc);
                 }
             }
         }
@@ -913,6 +982,10 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     // register-tile pixel row
     g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64) + static_cast<size_t>(c.threads()) * 16,
                             static_cast<size_t>(c.pixels()) * 8);
+    // 16-bit NCHW outputs of whole-row tiles leave through an LDS transpose:
+    // [NT channels][tile pixels * 2 + 16 bytes]
+    if (c.fr == 32 && p.esize == 2 && p.xb == 1)
+        g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(c.nt()) * (static_cast<size_t>(g->TN) * g->TH * g->TW * 2 + 16));
     g->stg = 0;
     {
         const int sz = wide_sz(p);
