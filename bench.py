@@ -88,10 +88,10 @@ def sources_digest(names) -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, dtype: str):
+def stored_traffic(workload: str, dtype: str, algo: str):
     """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when there is none or the kernel's sources changed since
-    the counters were taken."""
+    summary, or None when there is none, when it was taken for another
+    algorithm, or when the kernel's sources changed since."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (workload, dtype))
     if not os.path.exists(path):
         return None
@@ -102,7 +102,7 @@ def stored_traffic(workload: str, dtype: str):
                 k, _, v = line.partition(":")
                 kv[k.strip()] = v.strip()
     try:
-        if kv["sources_sha256"] != sources_digest(kv["sources"].split()):
+        if kv.get("algo") != algo or kv["sources_sha256"] != sources_digest(kv["sources"].split()):
             return None
         return int(float(kv["traffic_bytes_per_launch"]))
     except (KeyError, OSError, ValueError):
@@ -305,7 +305,7 @@ def main():
             "peak": d["peak"],
             "unit": d["unit"],
             "frac": d["frac"],
-            "traffic": stored_traffic(workload, dtype),
+            "traffic": stored_traffic(workload, dtype, d["algo"]),
             "kernel": "%s (%s)" % (d["name"], d["algo"]),
             "kernel_avg_ms": d["ms"],
             "algorithmic_bytes": d["bytes"],
