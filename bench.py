@@ -15,6 +15,12 @@ loop rotates over enough input/output buffer sets (> 512 MB, twice the 256 MB
 Infinity Cache) that no step reads its input from the cache a previous step
 filled.
 
+Before the W warm-up steps, the same launches run untimed for about a third of
+a second (at least ``--settle`` seconds), so that the timed steps see the
+clock the GPU holds under sustained load rather than one still ramping up
+from idle (this matters for a fixed ``--algo``, where no Fast-Run search has
+run first).
+
 Prints ONE JSON line: whole-step throughput, the roofline of the dominant
 kernel (HIP events around every launch, on the stream the kernel runs on),
 and the CPU oracle timed on a bounded sample of the same workload.
@@ -69,6 +75,7 @@ def parse():
     ap.add_argument("--n", type=int, default=0, help="batch size (0: the workload's own)")
     ap.add_argument("--dtype", default="", choices=["", "bf16", "f32", "i8"])
     ap.add_argument("--algo", default="auto", help="auto (Fast-Run) or family[/config], e.g. implicit_gemm/7")
+    ap.add_argument("--settle", type=float, default=0.3, help="seconds of untimed launches before the warm-up steps")
     ap.add_argument("--sets", type=int, default=0, help="rotated buffer sets (0: enough for > 512 MB)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle CPU work at most")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -225,6 +232,14 @@ def main():
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
 
+    t_end = time.perf_counter() + a.settle
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            for l in layers:
+                launch(l, i)
+            i += 1
+        torch.cuda.synchronize()
     for i in range(a.warmup):
         for l in layers:
             launch(l, i)

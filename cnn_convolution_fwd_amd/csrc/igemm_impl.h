@@ -355,6 +355,9 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int thw = a.TH * a.TW;
     const int tile_pix = a.TN * thw;
     const int patch_bytes = a.npix * PatchStride<FR>::value;
+    // patch buffers in LDS: three for the nine-tap path (chunk c + 1 is staged
+    // while chunk c runs), two otherwise
+    constexpr int NBUF = (RSV == 9) ? 3 : 2;
     const int ih0 = oh0 * a.sh - a.ph;
     const int iw0 = ow0 * a.sw - a.pw;
     const T* __restrict__ x = static_cast<const T*>(a.x);
@@ -416,11 +419,11 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     }
 
     uint4 stg[MAXU][PP];
-    auto stage_load = [&](int chunk) {
+    auto stage_load = [&](int chunk, uint4 (&dst)[MAXU][PP]) {
 #pragma unroll
         for (int i = 0; i < MAXU; ++i) {
 #pragma unroll
-            for (int l = 0; l < PP; ++l) stg[i][l] = make_uint4(0, 0, 0, 0);
+            for (int l = 0; l < PP; ++l) dst[i][l] = make_uint4(0, 0, 0, 0);
             if (u_sp[i] < 0) continue;
             const int cl = chunk * CK + u_j[i] * E16;
             const int nval = a.Cg - cl;
@@ -435,18 +438,18 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 for (int l = 0; l < PP; ++l) {
                     if (XB == 1) {
                         if (l < nval)
-                            stg[i][l] = *reinterpret_cast<const uint4*>(xr + (c0 + l) * HW + u_sp[i]);
+                            dst[i][l] = *reinterpret_cast<const uint4*>(xr + (c0 + l) * HW + u_sp[i]);
                     } else {
                         if (l * XB < nval)
-                            stg[i][l] = *reinterpret_cast<const uint4*>(xr + ((c0 / XB + l) * HW + u_sp[i]) * XB);
+                            dst[i][l] = *reinterpret_cast<const uint4*>(xr + ((c0 / XB + l) * HW + u_sp[i]) * XB);
                     }
                 }
             } else {
-                stg[i][0] = load_unit<T, XB>(xn, a.H, a.W, c0, nval, u_sp[i]);
+                dst[i][0] = load_unit<T, XB>(xn, a.H, a.W, c0, nval, u_sp[i]);
             }
         }
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](int buf, const uint4 (&src)[MAXU][PP]) {
         uint8_t* base = lds + buf * patch_bytes;
 #pragma unroll
         for (int i = 0; i < MAXU; ++i) {
@@ -454,16 +457,16 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             if (STG == 1) {
                 // pixels outside this patch row go to a per-thread dummy slot
                 // past both patch buffers (no branch per pixel)
-                uint8_t* dummy = lds + 2 * patch_bytes + tid * 16;
+                uint8_t* dummy = lds + NBUF * patch_bytes + tid * 16;
 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
                     const int col = u_pc[i] + p;
                     const bool ok = col >= 0 && col < a.PW;
                     uint8_t* dst = ok ? base + lds_slot<FR>(u_q[i] + p, u_j[i]) : dummy;
-                    *reinterpret_cast<uint4*>(dst) = wide_pick<WD::SZ>(stg[i], p);
+                    *reinterpret_cast<uint4*>(dst) = wide_pick<WD::SZ>(src[i], p);
                 }
             } else {
-                *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i], u_j[i])) = stg[i][0];
+                *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i], u_j[i])) = src[i][0];
             }
         }
     };
@@ -549,10 +552,12 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     };
 
     uint4 bcur[FN][NP], bnxt[FN][NP];
-    if constexpr (RSV != 9) load_b(bcur, 0);
-    stage_load(0);
-    stage_store(0);
-    __syncthreads();
+    if constexpr (RSV != 9) {
+        load_b(bcur, 0);
+        stage_load(0, stg);
+        stage_store(0, stg);
+        __syncthreads();
+    }
 
     const int total_it = a.nchunks * RS;
     int it = 0;
@@ -562,10 +567,17 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         // at compile time (a copy between prefetch buffers would make the
         // compiler wait for the load behind it):
         //  * weights: a ring of three tap buffers, tap t+2 requested at tap t;
-        //  * activations of the next chunk: the eight 16-byte loads of this
-        //    thread, one per tap, each issued after that tap's weight request,
-        //    so that no weight wait ever waits for an activation load;
-        //  * A: rolling single buffer refilled right after each use.
+        //  * activations: three patch buffers, chunk c in buffer c % 3.  While
+        //    chunk c runs, chunk c + 1 is already in LDS and the eight 16-byte
+        //    loads of chunk c + 2 are issued, one per tap, each after that
+        //    tap's weight request (so no weight wait waits for an activation
+        //    load); they are written to LDS at the chunk's end, followed by
+        //    the chunk's only barrier;
+        //  * A: rolling single buffer refilled right after each use; the last
+        //    tap's refill already reads the next chunk's first tap, so the
+        //    matrix cores do not wait for LDS across a chunk boundary.
+        // Buffer (c + 2) % 3 held chunk c - 1, whose last reads were issued
+        // and completed before the barrier that ended chunk c - 1.
         static_assert(FR == 32 && STG == 1 && MAXU * PP == 8, "nine-tap path needs 32x32 tiles and wide staging");
         uint4 ring[3][FN][NP];
         uint4 ra[FM][NP];
@@ -581,21 +593,34 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
         for (int f = 0; f < FM; ++f) abase[f] = qbase[f] * PS + pslot[0] * 16;
         const int last_it = total_it - 1;
+        // prologue: the weights of the first two taps and the first two
+        // chunks' activations are all requested before anything is waited for
         load_b(ring[0], 0);
         load_b(ring[1], min(1, last_it));
+        {
+            uint4 stg1[MAXU][PP];
+            stage_load(0, stg);
+            stage_load(1, stg1);  // zeros past the last chunk
+            stage_store(0, stg);
+            stage_store(1, stg1);
+        }
+        __syncthreads();
 #pragma unroll
         for (int f = 0; f < FM; ++f)
 #pragma unroll
             for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(lds + abase[f] + i * PSTEP);
+        int bc = 0;  // buffer of chunk c
         for (int chunk = 0; chunk < a.nchunks; ++chunk) {
-            const int buf = chunk & 1;
-            const uint8_t* pb = lds + buf * patch_bytes;
+            const int bnext = (bc == 2) ? 0 : bc + 1;
+            const int bfar = (bnext == 2) ? 0 : bnext + 1;
+            const uint8_t* pb = lds + bc * patch_bytes;
+            const uint8_t* pn = lds + bnext * patch_bytes;
             const int it0 = chunk * 9;
 #pragma unroll
             for (int t = 0; t < 9; ++t) {
                 load_b(ring[(t + 2) % 3], min(it0 + t + 2, last_it));
-                if (t < 8) stage_piece(chunk + 1, t);
-                const uint8_t* pt = pb + toffs[t < 8 ? t + 1 : 8];
+                if (t < 8) stage_piece(chunk + 2, t);
+                const uint8_t* pt = (t < 8) ? pb + toffs[t + 1] : pn + toffs[0];
 #pragma unroll
                 for (int i = 0; i < NP; ++i) {
 #pragma unroll
@@ -606,13 +631,9 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                     }
                 }
             }
-            stage_store(buf ^ 1);
+            if (chunk + 2 < a.nchunks) stage_store(bfar, stg);
             __syncthreads();
-            const uint8_t* pn = lds + (buf ^ 1) * patch_bytes;
-#pragma unroll
-            for (int f = 0; f < FM; ++f)
-#pragma unroll
-                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pn + abase[f] + i * PSTEP);
+            bc = bnext;
         }
         it = total_it;
     } else if constexpr (FR == 32) {
@@ -643,7 +664,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             const int buf = chunk & 1;
             const bool more = chunk + 1 < a.nchunks;
             const uint8_t* pb = lds + buf * patch_bytes;
-            if (more) stage_load(chunk + 1);
+            if (more) stage_load(chunk + 1, stg);
             int r = 0, s = 0;
             for (int rs = 0; rs < RS; ++rs, ++it) {
                 load_b(b2, min(it + 2, last_it));
@@ -683,7 +704,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                     s = sn;
                 }
             }
-            if (more) stage_store(buf ^ 1);
+            if (more) stage_store(buf ^ 1, stg);
             __syncthreads();
             if (more) read_a(lds + (buf ^ 1) * patch_bytes, 0);
         }
@@ -692,7 +713,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             const int buf = chunk & 1;
             const bool more = chunk + 1 < a.nchunks;
             const uint8_t* pb = lds + buf * patch_bytes;
-            if (more) stage_load(chunk + 1);
+            if (more) stage_load(chunk + 1, stg);
             int r = 0, s = 0;
             for (int rs = 0; rs < RS; ++rs, ++it) {
                 if (it + 1 < total_it) load_b(bnxt, it + 1);
@@ -706,7 +727,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                     ++r;
                 }
             }
-            if (more) stage_store(buf ^ 1);
+            if (more) stage_store(buf ^ 1, stg);
             __syncthreads();
         }
     }
@@ -931,9 +952,60 @@ struct Geo {
 // Bytes per pixel sub-element of one 16-byte load along W (see Wide<>).
 inline int wide_sz(const Prob& p) { return p.xb == 1 ? p.esize : p.xb * p.esize; }
 
+// Geometry of tiles of TN images x TH x TW output pixels (the tile must
+// fit: its input patch within the staging capacity of the config).
+inline bool tile_geometry(const Prob& p, const Cfg& c, int TN, int TH, int TW, Geo* g, std::string* why) {
+    const int CK = 64 / p.esize;
+    const int maxpix = kMaxUnitsPerThread * c.threads() / 4;
+    const int PH = (TH - 1) * p.sh + (p.r - 1) * p.dh + 1;
+    const int PW = (TW - 1) * p.sw + (p.s - 1) * p.dw + 1;
+    const long long npix = static_cast<long long>(TN) * PH * PW;
+    if (npix > maxpix) {
+        if (why) *why = "implicit GEMM: the input patch of one output row does not fit this tile config";
+        return false;
+    }
+    g->TN = TN;
+    g->TH = TH;
+    g->TW = TW;
+    g->PH = PH;
+    g->PW = PW;
+    g->npix = static_cast<int>(npix);
+    g->tiles_n = (p.n + g->TN - 1) / g->TN;
+    g->tiles_h = (p.oh + g->TH - 1) / g->TH;
+    g->tiles_w = (p.ow + g->TW - 1) / g->TW;
+    g->nchunks = (p.cg + CK - 1) / CK;
+    g->ntk = (p.kg + c.nt() - 1) / c.nt();
+    g->stg = 0;
+    {
+        const int sz = wide_sz(p);
+        if (sz == 2 || sz == 4 || sz == 8) {
+            const int pp = 16 / sz;
+            const int maxu = std::max(1, 32 / (4 * pp));
+            const long long ncb = (g->PW + pp - 1) / pp + 1;
+            const long long units = 4LL * g->TN * g->PH * ncb;
+            const bool chan_ok = (p.xb == 1) || (p.cg % p.xb == 0);
+            if (p.w % pp == 0 && chan_ok && units <= static_cast<long long>(maxu) * c.threads()) g->stg = 1;
+        }
+    }
+    // patch buffers (three on the nine-tap path, see launch_cfg) and one
+    // 16-byte dummy slot per thread; the epilogue reuses them for an 8-byte
+    // offset per register-tile pixel row
+    const size_t nbuf = (c.fr == 32 && g->stg == 1 && p.r * p.s == 9) ? 3 : 2;
+    g->lds_bytes = std::max(nbuf * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64) + static_cast<size_t>(c.threads()) * 16,
+                            static_cast<size_t>(c.pixels()) * 8);
+    // 16-bit NCHW outputs of whole-row tiles leave through an LDS transpose:
+    // [NT channels][tile pixels * 2 + 16 bytes]
+    if (c.fr == 32 && p.esize == 2 && p.xb == 1)
+        g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(c.nt()) * (static_cast<size_t>(g->TN) * g->TH * g->TW * 2 + 16));
+    if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk * p.g > 0x7fffffffLL) {
+        if (why) *why = "implicit GEMM: grid too large";
+        return false;
+    }
+    return true;
+}
+
 inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     const int P = c.pixels();
-    const int CK = 64 / p.esize;
     int TN, TH, TW;
     if (p.oh * p.ow <= P) {
         TN = std::min(p.n, P / (p.oh * p.ow));
@@ -948,20 +1020,12 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
         TH = 1;
         TW = P;
     }
+    // shrink the tile until its input patch fits
     const int maxpix = kMaxUnitsPerThread * c.threads() / 4;
     for (;;) {
         const int PH = (TH - 1) * p.sh + (p.r - 1) * p.dh + 1;
         const int PW = (TW - 1) * p.sw + (p.s - 1) * p.dw + 1;
-        const long long npix = static_cast<long long>(TN) * PH * PW;
-        if (npix <= maxpix) {
-            g->TN = TN;
-            g->TH = TH;
-            g->TW = TW;
-            g->PH = PH;
-            g->PW = PW;
-            g->npix = static_cast<int>(npix);
-            break;
-        }
+        if (static_cast<long long>(TN) * PH * PW <= maxpix) break;
         if (TN > 1)
             --TN;
         else if (TH > 1)
@@ -973,45 +1037,14 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
             return false;
         }
     }
-    g->tiles_n = (p.n + g->TN - 1) / g->TN;
-    g->tiles_h = (p.oh + g->TH - 1) / g->TH;
-    g->tiles_w = (p.ow + g->TW - 1) / g->TW;
-    g->nchunks = (p.cg + CK - 1) / CK;
-    g->ntk = (p.kg + c.nt() - 1) / c.nt();
-    // two patch buffers; the epilogue reuses them for an 8-byte offset per
-    // register-tile pixel row
-    g->lds_bytes = std::max(2 * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64) + static_cast<size_t>(c.threads()) * 16,
-                            static_cast<size_t>(c.pixels()) * 8);
-    // 16-bit NCHW outputs of whole-row tiles leave through an LDS transpose:
-    // [NT channels][tile pixels * 2 + 16 bytes]
-    if (c.fr == 32 && p.esize == 2 && p.xb == 1)
-        g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(c.nt()) * (static_cast<size_t>(g->TN) * g->TH * g->TW * 2 + 16));
-    g->stg = 0;
-    {
-        const int sz = wide_sz(p);
-        if (sz == 2 || sz == 4 || sz == 8) {
-            const int pp = 16 / sz;
-            const int maxu = std::max(1, 32 / (4 * pp));
-            const long long ncb = (g->PW + pp - 1) / pp + 1;
-            const long long units = 4LL * g->TN * g->PH * ncb;
-            const bool chan_ok = (p.xb == 1) || (p.cg % p.xb == 0);
-            if (p.w % pp == 0 && chan_ok && units <= static_cast<long long>(maxu) * c.threads()) g->stg = 1;
-        }
-    }
-    if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk * p.g > 0x7fffffffLL) {
-        if (why) *why = "implicit GEMM: grid too large";
-        return false;
-    }
-    return true;
+    return tile_geometry(p, c, TN, TH, TW, g, why);
 }
 
 inline size_t filter_bytes(const Prob& p, const Cfg& c, const Geo& g) {
     return static_cast<size_t>(p.g) * g.ntk * g.nchunks * p.r * p.s * c.nt() * 64;
 }
 
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV>
-cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
-                       hipStream_t st) {
+inline Args make_args(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y) {
     Args a;
     a.x = x;
     a.wp = wp;
@@ -1024,15 +1057,32 @@ cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* w
     a.TN = g.TN; a.TH = g.TH; a.TW = g.TW; a.PH = g.PH; a.PW = g.PW; a.npix = g.npix;
     a.tiles_w = g.tiles_w; a.tiles_h = g.tiles_h; a.tiles_n = g.tiles_n;
     a.nchunks = g.nchunks; a.ntk = g.ntk;
-    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV>;
-    static bool attr_done = false;
-    if (g.lds_bytes > 65536 && !attr_done) {
+    return a;
+}
+
+inline long long tile_count(const Prob& p, const Geo& g) {
+    return static_cast<long long>(g.tiles_n) * g.tiles_h * g.tiles_w * g.ntk * p.g;
+}
+
+template <typename K> cfwd_status allow_big_lds(K kern, size_t lds_bytes, bool* done) {
+    if (lds_bytes > 65536 && !*done) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return check_hip(e, "hipFuncSetAttribute(igemm)");
-        attr_done = true;
+        *done = true;
     }
-    const dim3 grid(static_cast<unsigned>(static_cast<long long>(g.tiles_n) * g.tiles_h * g.tiles_w * g.ntk * p.g));
+    return CFWD_OK;
+}
+
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV>
+cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
+                       hipStream_t st) {
+    const Args a = make_args(p, g, x, wp, scale, y);
+    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV>;
+    static bool attr_done = false;
+    const cfwd_status s = allow_big_lds(kern, g.lds_bytes, &attr_done);
+    if (s != CFWD_OK) return s;
+    const dim3 grid(static_cast<unsigned>(tile_count(p, g)));
     kern<<<grid, WM * WN * 64, g.lds_bytes, st>>>(a);
     return check_hip(hipGetLastError(), "igemm_kernel launch");
 }

@@ -47,6 +47,10 @@ SMALL = [
     ("asym", 1, 9, 7, 33, 130, 3, 1, (2, 1), (0, 1), 1, 1),
     ("multi_tile_k", 1, 70, 6, 6, 200, 3, 3, 1, 1, 1, 1),
     ("wide_row", 1, 8, 3, 300, 16, 3, 3, 1, 1, 1, 1),
+    # tiles of several whole 56-wide output rows whose last row band runs
+    # past the output, ragged channel chunk and output-channel tile; stride 2
+    ("rows56_ragged", 2, 40, 19, 56, 72, 3, 3, 1, 1, 1, 1),
+    ("rows28_s2", 1, 24, 40, 56, 40, 3, 3, 2, 1, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
