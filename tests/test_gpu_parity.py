@@ -107,16 +107,16 @@ def test_prepared_filter_path_matches():
     np.testing.assert_array_equal(a, b)
 
 
-def test_config1_full():
+def test_single_conv_16to32_32x32_full():
     """Single 3x3 conv 16->32 at 32x32, fp32, every candidate, full tensor."""
     torch_cuda()
     pr = float_problem(1)
     L = pr.layer
     yref, den = oracle.conv2d(pr.x, pr.w, L.stride, L.pad, L.dil, L.groups)
     for algo, cfg in candidates_for((1, 16, 32, 32, 32, 3, 3), "f32", 1, 1):
-        say("config1", algo, cfg)
+        say("single conv", algo, cfg)
         y = run_conv(pr.x, pr.w, "f32", 1, 1, algo=algo, config_id=cfg)
-        check_float("config1 %s/%d" % (algo, cfg), y, yref, den, "f32", algo)
+        check_float("single conv %s/%d" % (algo, cfg), y, yref, den, "f32", algo)
 
 
 def sample_points(shape, n, seed):
@@ -140,19 +140,19 @@ def check_points_float(name, y, pr, dtype, algo, n=3000):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_config3_full_size_sampled(dtype):
+def test_resnet3x3_256ch_56x56_n32_sampled(dtype):
     """ResNet 3x3 256->256 at 56x56, N=32: every IG config on sampled outputs."""
     torch_cuda()
     pr = float_problem(3, dtype=dtype)
     for algo, cfg in candidates_for((32, 256, 56, 56, 256, 3, 3), dtype, 1, 1):
         if algo == "direct":
             continue  # generic direct at this size is slow and covered on small shapes
-        say("config3", dtype, algo, cfg)
+        say("resnet3x3 256ch", dtype, algo, cfg)
         y = run_conv(pr.x, pr.w, dtype, 1, 1, algo=algo, config_id=cfg)
-        check_points_float("config3 %s %s/%d" % (dtype, algo, cfg), y, pr, dtype, algo)
+        check_points_float("resnet3x3 256ch %s %s/%d" % (dtype, algo, cfg), y, pr, dtype, algo)
 
 
-def test_config3_deterministic():
+def test_resnet3x3_256ch_deterministic():
     torch_cuda()
     pr = float_problem(3, dtype="bf16")
     a = run_conv(pr.x, pr.w, "bf16", 1, 1, algo="implicit_gemm")
@@ -162,38 +162,38 @@ def test_config3_deterministic():
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("layer_idx", [0, 1, 2])
-def test_config2_layers_n64_sampled(dtype, layer_idx):
+def test_mobilenet_layers_n64_sampled(dtype, layer_idx):
     """MobileNet-style stem / depthwise / pointwise at N=64, default algorithm."""
     torch_cuda()
     pr = float_problem(2, layer_idx, dtype=dtype)
     L = pr.layer
-    say("config2", L.name, dtype)
+    say("mobilenet", L.name, dtype)
     y = run_conv(pr.x, pr.w, dtype, L.stride, L.pad, L.dil, L.groups)
-    check_points_float("config2 %s %s" % (L.name, dtype), y, pr, dtype, "auto")
+    check_points_float("mobilenet %s %s" % (L.name, dtype), y, pr, dtype, "auto")
 
 
 @pytest.mark.parametrize("layer_idx", [0, 1, 2, 3])
-def test_config4_layers_sampled(layer_idx):
+def test_bottleneck_layers_sampled(layer_idx):
     torch_cuda()
     pr = float_problem(4, layer_idx, dtype="bf16")
     L = pr.layer
-    say("config4", L.name)
+    say("bottleneck", L.name)
     y = run_conv(pr.x, pr.w, "bf16", L.stride, L.pad, L.dil, L.groups)
-    check_points_float("config4 %s" % L.name, y, pr, "bf16", "auto")
+    check_points_float("bottleneck %s" % L.name, y, pr, "bf16", "auto")
 
 
 @pytest.mark.parametrize("layer_idx", range(20))
-def test_config5_int8_layer_exact(layer_idx):
+def test_resnet18_int8_layer_exact(layer_idx):
     """int8 ResNet-18 layer, NCHW4: full tensor at N=2 and sampled at N=64, bit-exact."""
     torch_cuda()
     L = CONFIGS[5].layers[layer_idx]
     small = int8_problem(5, layer_idx, n=2)
     yref, _ = oracle.conv2d_int8_requant(small.x, small.w, small.scale, L.stride, L.pad, L.dil, L.groups)
-    say("config5 full N=2", L.name)
+    say("resnet18 int8 full N=2", L.name)
     y = run_conv(small.x, small.w, "i8", L.stride, L.pad, L.dil, L.groups, "NCHWX", 4, scale=small.scale)
     assert np.array_equal(y, yref), "%s N=2: %d outputs differ" % (L.name, int((y != yref).sum()))
     big = int8_problem(5, layer_idx)
-    say("config5 N=64", L.name)
+    say("resnet18 int8 N=64", L.name)
     y = run_conv(big.x, big.w, "i8", L.stride, L.pad, L.dil, L.groups, "NCHWX", 4, scale=big.scale)
     idx = sample_points(y.shape, 2000, 2)
     acc = oracle.conv2d_int8_points(big.x, big.w, idx, L.stride, L.pad, L.dil, L.groups)
@@ -208,7 +208,7 @@ def test_fastrun_select_and_dispatch(tmp_path):
     pr = float_problem(1)
     from tests.gpu_util import to_device, from_device
     xd, wd = to_device(pr.x, "f32"), to_device(pr.w, "f32")
-    say("fastrun config1")
+    say("fastrun single conv")
     best, y = B.fastrun_select(xd, wd, 1, 1)
     yref, den = oracle.conv2d(pr.x, pr.w, 1, 1)
     check_float("fastrun output", from_device(y, "f32"), yref, den, "f32", B.algo_name(best))
