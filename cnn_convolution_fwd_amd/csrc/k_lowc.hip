@@ -19,6 +19,10 @@
 //     matrix cores (two-deep pipeline, last pair peeled);
 //   * the epilogue writes D[k][pixel] in the caller's layout; for int8 NCHW4
 //     a lane's four consecutive channels of one pixel leave as one dword.
+//     For fp32/bf16 NCHW, where a workgroup's output is a run of consecutive
+//     pixels of each of its channels, the tile is first transposed through
+//     LDS ([channel][pixel]) and leaves as 16-byte streaming stores, each
+//     channel's run written by consecutive lanes.
 // Step (units per MFMA step): fp32 8 (four v_mfma_f32_32x32x2f32), bf16 16
 // (one v_mfma_f32_32x32x16_bf16), int8 8 dwords = 32 bytes (one
 // v_mfma_i32_32x32x32_i8).
@@ -32,13 +36,18 @@ using f32x16_t = float __attribute__((ext_vector_type(16)));
 using i32x16_t = int __attribute__((ext_vector_type(16)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kMaxUnits = 1024;  // LDS table entries (12 KB)
+constexpr int kMaxUnits = 1024;  // unit table entries at most (12 KB of LDS)
 
 struct LcArgs {
     int N, C, H, W, K, OH, OW, R, S, sh, sw, ph, pw, dh, dw;
     long long x_img, y_img;  // elements (bytes for int8)
     int units, nss, nkb, KW, ngk;
     long long npix;
+    int vec_ok;  // output pieces of 16 bytes are aligned (checked on the host)
+    // staged variants: each workgroup copies the input rows its pixels read
+    // into LDS, [channel][ROWS][RW] gather elements, the image columns at
+    // padL .. padL + W - 1 and zeros around them
+    int ROWS, RW, padL, st_bytes;
 };
 
 struct Tap {
@@ -119,25 +128,46 @@ __global__ __launch_bounds__(256) void lc_prepare_kernel(const T* __restrict__ w
     }
 }
 
+// Bytes of the LDS-transposed output tile of one workgroup (0: not used):
+// (4 / KW) * NCB * 32 pixels x KW * KBW * 32 channels, whatever KW is.
+template <typename T, int XB, int NCB, int KBW>
+constexpr int lc_tile_bytes() {
+    constexpr int b = 4 * NCB * KBW * 32 * 32 * static_cast<int>(sizeof(T));
+    return (sizeof(T) != 1 && XB == 1 && b <= 32768) ? b : 0;
+}
+
 // Workgroup: 4 waves = (4 / KW) pixel groups x KW k groups; a wave owns NCB
 // columns blocks of 32 pixels x KBW blocks of 32 output channels.
-template <typename T, int XB, int NCB, int KBW>
+template <typename T, int XB, int NCB, int KBW, bool STG>
 __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const uint8_t* __restrict__ wp,
                                                  const float* __restrict__ scale, T* __restrict__ y, LcArgs a) {
     using L = Lc<T>;
     using G = typename L::G;
-    __shared__ Tap tab[kMaxUnits];
+    constexpr int TILE = lc_tile_bytes<T, XB, NCB, KBW>();
+    // dynamic LDS (sized by lc_lds_bytes): [staged input rows (STG)][unit
+    // table] while gathering, then, after a barrier, the transposed output
+    // tile in the same bytes
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+    const G* lx = reinterpret_cast<const G*>(lds_dyn);
+    Tap* tab = reinterpret_cast<Tap*>(lds_dyn + (STG ? a.st_bytes : 0));
+    uint8_t* otile = lds_dyn;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, h = lane >> 5;
+    const int ohw = a.OH * a.OW;
+    const int wk = wave % a.KW, wpx = wave / a.KW;
+    const int kg = static_cast<int>(blockIdx.x) % a.ngk;
+    const long long pg = static_cast<long long>(blockIdx.x) / a.ngk;
+    const int wpix = (4 / a.KW) * NCB * 32;  // pixels of this workgroup (all in one image when STG)
 
-    // reduction unit -> (row delta, column delta, channel offset)
+    // reduction unit -> (row delta, column delta, channel offset); staged:
+    // off = the unit's LDS element offset from a pixel's base, -1 = padding
     const int RS = a.R * a.S;
     const int ntab = a.nss * L::SSU;
     for (int u = tid; u < ntab; u += 256) {
         Tap t;
         t.dr = -(1 << 28);  // padding unit: always out of range -> 0
         t.ds = 0;
-        t.off = 0;
+        t.off = STG ? -1 : 0;
         const int nu = (sizeof(T) == 1) ? RS : a.units;
         if (u < nu) {
             const int c = (sizeof(T) == 1) ? 0 : u / RS;
@@ -145,23 +175,47 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             const int r = tap / a.S, s = tap % a.S;
             t.dr = r * a.dh;
             t.ds = s * a.dw;
-            if (sizeof(T) != 1) t.off = (XB == 1) ? c * a.H * a.W : (c / XB) * a.H * a.W * XB + c % XB;
+            if (STG)
+                t.off = (c * a.ROWS + r * a.dh) * a.RW + s * a.dw;
+            else if (sizeof(T) != 1)
+                t.off = (XB == 1) ? c * a.H * a.W : (c / XB) * a.H * a.W * XB + c % XB;
         }
         tab[u] = t;
     }
+    // staged: first input row of this workgroup and its image
+    int st_n = 0, st_row0 = 0;
+    if constexpr (STG) {
+        const long long W0 = pg * wpix;
+        st_n = static_cast<int>(W0 / ohw);
+        st_row0 = static_cast<int>(W0 - static_cast<long long>(st_n) * ohw) / a.OW * a.sh - a.ph;
+        // 16-byte chunks of every staged row; chunks are wholly inside or
+        // wholly outside the image (W and padL are multiples of a chunk)
+        constexpr int CE = 16 / static_cast<int>(sizeof(G));  // gather elements per chunk
+        const int cpr = a.RW / CE;
+        const int nch = (sizeof(T) == 1) ? 1 : a.C;
+        const G* xg = reinterpret_cast<const G*>(x) + static_cast<long long>(st_n) * (sizeof(T) == 1 ? a.x_img / 4 : a.x_img);
+        for (int q = tid; q < nch * a.ROWS * cpr; q += 256) {
+            const int col = q % cpr, t2 = q / cpr;
+            const int rr = t2 % a.ROWS, c = t2 / a.ROWS;
+            const int ih = st_row0 + rr, iw = col * CE - a.padL;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) && iw >= 0 && iw < a.W)
+                v = *reinterpret_cast<const uint4*>(xg + (static_cast<long long>(c) * a.H + ih) * a.W + iw);
+            *reinterpret_cast<uint4*>(lds_dyn + ((static_cast<long long>(c) * a.ROWS + rr) * a.RW + col * CE) * sizeof(G)) = v;
+        }
+    }
     __syncthreads();
 
-    const int wk = wave % a.KW, wpx = wave / a.KW;
-    const int kg = static_cast<int>(blockIdx.x) % a.ngk;
-    const long long pg = static_cast<long long>(blockIdx.x) / a.ngk;
     const int kb0 = (kg * a.KW + wk) * KBW;
-    if (kb0 >= a.nkb) return;  // after the only barrier
+    // a wave past the last k block has no work; with the transposed epilogue
+    // it still takes part in the workgroup's barrier
+    const bool active = kb0 < a.nkb;
+    if (TILE == 0 && !active) return;  // after the only barrier
     const long long P0 = (pg * (4 / a.KW) + wpx) * (NCB * 32);
 
     // this lane's pixel in each column block
-    const int ohw = a.OH * a.OW;
     long long xbase[NCB];
-    int ih0[NCB], iw0[NCB];
+    int ih0[NCB], iw0[NCB], lbase[NCB];
     bool pok[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -174,6 +228,8 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
         ih0[cb] = oh * a.sh - a.ph;
         iw0[cb] = ow * a.sw - a.pw;
         xbase[cb] = (sizeof(T) == 1) ? n * (a.x_img / 4) : n * a.x_img;
+        // staged: element of tap (0, 0), channel 0 of this pixel in LDS
+        lbase[cb] = pok[cb] ? (ih0[cb] - st_row0) * a.RW + iw0[cb] + a.padL : 0;
     }
 
     typename L::Acc acc[KBW][NCB];
@@ -189,6 +245,12 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             const Tap t = tab[ss * L::SSU + L::unit(g, h)];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
+                if constexpr (STG) {
+                    const bool ok = t.off >= 0;
+                    const G val = lx[ok ? lbase[cb] + t.off : 0];
+                    v[cb][g] = ok ? val : G{};
+                    continue;
+                }
                 const int ih = ih0[cb] + t.dr, iw = iw0[cb] + t.ds;
                 const bool ok = static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) &&
                                 static_cast<unsigned>(iw) < static_cast<unsigned>(a.W);
@@ -211,19 +273,83 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                 for (int cb = 0; cb < NCB; ++cb) L::mma(acc[b][cb], wv[b], v[cb], i);
     };
 
-    G va[NCB][L::NG], vb[NCB][L::NG];
-    uint4 wa[KBW], wb[KBW];
-    gather(0, va, wa);
-    int ss = 0;
-    for (; ss + 2 < a.nss; ss += 2) {
+    if (active) {
+        G va[NCB][L::NG], vb[NCB][L::NG];
+        uint4 wa[KBW], wb[KBW];
+        gather(0, va, wa);
+        int ss = 0;
+        for (; ss + 2 < a.nss; ss += 2) {
+            gather(ss + 1, vb, wb);
+            compute(va, wa);
+            gather(ss + 2, va, wa);
+            compute(vb, wb);
+        }
         gather(ss + 1, vb, wb);
         compute(va, wa);
-        gather(ss + 2, va, wa);
         compute(vb, wb);
     }
-    gather(ss + 1, vb, wb);
-    compute(va, wa);
-    compute(vb, wb);
+
+    if constexpr (TILE > 0) {
+        // [channel of the workgroup][pixel of the workgroup], row pitch padded
+        // by 16 bytes; then each thread stores 16-byte pieces of channel rows
+        constexpr int E = static_cast<int>(sizeof(T));
+        const int wch = a.KW * KBW * 32;         // channels of this workgroup
+        const int pitch = wpix * E + 16;
+        __syncthreads();  // every wave is done with the unit table
+        if (active) {
+#pragma unroll
+            for (int b = 0; b < KBW; ++b)
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const int pl = (wpx * NCB + cb) * 32 + j;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int cl = (wk * KBW + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                        uint8_t* d = otile + cl * pitch + pl * E;
+                        if constexpr (sizeof(T) == 4)
+                            *reinterpret_cast<float*>(d) = acc[b][cb][v];
+                        else
+                            *reinterpret_cast<uint16_t*>(d) = float_to_bf16(acc[b][cb][v]);
+                    }
+                }
+        }
+        __syncthreads();
+        constexpr int PE = 16 / E;  // pixels per 16-byte piece
+        const int pieces = wpix / PE;
+        const long long W0 = pg * wpix;  // first pixel of this workgroup
+        const int kbase = kg * a.KW * KBW * 32;
+        for (int q = tid; q < wch * pieces; q += 256) {
+            const int cl = q / pieces, pc = q - (q / pieces) * pieces;
+            const int k = kbase + cl;
+            if (k >= a.K) continue;
+            const long long G0 = W0 + pc * PE;
+            if (G0 >= a.npix) continue;
+            const int n = static_cast<int>(G0 / ohw);
+            const int pix = static_cast<int>(G0 - static_cast<long long>(n) * ohw);
+            const uint8_t* src = otile + cl * pitch + pc * 16;
+            T* dst = y + n * a.y_img + static_cast<long long>(k) * ohw + pix;
+            if (a.vec_ok && G0 + PE <= a.npix && pix + PE <= ohw) {
+                const uint4 v = *reinterpret_cast<const uint4*>(src);
+                typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+                const u32x4_t w = {v.x, v.y, v.z, v.w};
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(dst));
+            } else {
+                // a piece that crosses an image boundary or the end
+                for (int e = 0; e < PE; ++e) {
+                    long long Ge = G0 + e;
+                    if (Ge >= a.npix) break;
+                    const int ne = static_cast<int>(Ge / ohw);
+                    const int pe = static_cast<int>(Ge - static_cast<long long>(ne) * ohw);
+                    T* de = y + ne * a.y_img + static_cast<long long>(k) * ohw + pe;
+                    if constexpr (sizeof(T) == 4)
+                        *de = *reinterpret_cast<const float*>(src + e * E);
+                    else
+                        de->bits = *reinterpret_cast<const uint16_t*>(src + e * E);
+                }
+            }
+        }
+        return;
+    }
 
     // D[row = channel][col = pixel]: lane (j, hh), element v -> channel
     // 8 (v / 4) + 4 hh + v % 4 of the block
@@ -271,8 +397,12 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
 struct LcCfg {
     int ncb, kbw;
 };
+// configs 0-5 gather from global memory; 6-11 are the same tiles gathering
+// from input rows staged in LDS
 constexpr LcCfg kLc[6] = {{4, 1}, {2, 2}, {4, 2}, {1, 1}, {1, 2}, {2, 1}};
-constexpr int kLcN = 6;
+constexpr int kLcBase = 6;
+constexpr int kLcN = 2 * kLcBase;
+constexpr size_t kLcStageMax = 48 * 1024;  // LDS for staged rows + unit table
 
 bool lc_geometry(const Prob& p, int cfg, LcArgs* a, std::string* why) {
     auto fail = [&](const char* m) {
@@ -280,6 +410,8 @@ bool lc_geometry(const Prob& p, int cfg, LcArgs* a, std::string* why) {
         return false;
     };
     if (cfg < 0 || cfg >= kLcN) return fail("implicit GEMM (gather): no such config");
+    const bool staged = cfg >= kLcBase;
+    const LcCfg lc = kLc[cfg % kLcBase];
     if (p.g != 1) return fail("implicit GEMM (gather): groups must be 1");
     int units, ssu;
     if (p.dtype == CFWD_I8) {
@@ -301,33 +433,88 @@ bool lc_geometry(const Prob& p, int cfg, LcArgs* a, std::string* why) {
     a->x_img = p.x_img; a->y_img = p.y_img;
     a->units = units;
     a->nss = nss;
-    const int kbw = kLc[cfg].kbw;
+    const int kbw = lc.kbw;
     const int kwaves = ((p.k + 31) / 32 + kbw - 1) / kbw;
     a->nkb = kwaves * kbw;
     a->KW = kwaves >= 4 ? 4 : (kwaves >= 2 ? 2 : 1);
     a->ngk = (kwaves + a->KW - 1) / a->KW;
     a->npix = static_cast<long long>(p.n) * p.oh * p.ow;
-    const long long per_wg = static_cast<long long>(4 / a->KW) * kLc[cfg].ncb * 32;
+    const long long per_wg = static_cast<long long>(4 / a->KW) * lc.ncb * 32;
     const long long pgroups = (a->npix + per_wg - 1) / per_wg;
     if (pgroups * a->ngk >= (1LL << 31)) return fail("implicit GEMM (gather): grid too large");
+    a->ROWS = a->RW = a->padL = a->st_bytes = 0;
+    if (staged) {
+        // gather element: the dtype's element, or an NCHW4 int8 pixel's dword
+        const int gsz = (p.dtype == CFWD_I8) ? 4 : p.esize;
+        const int ce = 16 / gsz;  // elements per 16-byte chunk
+        const long long ohw = static_cast<long long>(p.oh) * p.ow;
+        if (p.dtype != CFWD_I8 && p.xb != 1) return fail("implicit GEMM (gather, staged): NCHW only");
+        if (ohw % per_wg != 0) return fail("implicit GEMM (gather, staged): workgroups would straddle images");
+        if (p.w % ce != 0 || p.pw > ce) return fail("implicit GEMM (gather, staged): row width or padding");
+        const long long spanned = (p.ow - 1 + per_wg - 1) / p.ow + 1;  // output rows a workgroup can touch
+        const long long rows = (spanned - 1) * p.sh + static_cast<long long>(p.r - 1) * p.dh + 1;
+        const long long need = ce + static_cast<long long>(p.ow - 1) * p.sw - p.pw + static_cast<long long>(p.s - 1) * p.dw + 1;
+        long long rw = std::max<long long>(ce + p.w, need);
+        rw = (rw + ce - 1) / ce * ce;
+        const long long nch = (p.dtype == CFWD_I8) ? 1 : p.c;
+        const long long sb = (nch * rows * rw * gsz + 15) / 16 * 16;
+        if (sb + static_cast<long long>(nss) * ssu * static_cast<long long>(sizeof(Tap)) > static_cast<long long>(kLcStageMax))
+            return fail("implicit GEMM (gather, staged): input rows of a workgroup exceed the LDS budget");
+        a->ROWS = static_cast<int>(rows);
+        a->RW = static_cast<int>(rw);
+        a->padL = ce;
+        a->st_bytes = static_cast<int>(sb);
+    }
     return true;
+}
+
+// Dynamic LDS of one workgroup: the larger of the unit table and the
+// transposed output tile (with its 16-byte row padding).
+template <typename T, int XB, int NCB, int KBW>
+size_t lc_lds_bytes(const LcArgs& a) {
+    const size_t tabb = static_cast<size_t>(a.st_bytes) + static_cast<size_t>(a.nss) * Lc<T>::SSU * sizeof(Tap);
+    size_t tile = 0;
+    if (lc_tile_bytes<T, XB, NCB, KBW>() > 0)
+        tile = static_cast<size_t>(a.KW) * KBW * 32 * ((4 / a.KW) * NCB * 32 * sizeof(T) + 16);
+    return std::max(tabb, tile);
+}
+
+template <typename T, int XB, int NCB, int KBW>
+void lc_launch_cfg(bool staged, unsigned blocks, const LcArgs& b, const T* xt, const uint8_t* w8, const float* scale,
+                   T* yt, hipStream_t st) {
+    const size_t lds = lc_lds_bytes<T, XB, NCB, KBW>(b);
+    if constexpr (sizeof(T) == 1 || XB == 1) {
+        if (staged) {
+            lc_kernel<T, XB, NCB, KBW, true><<<blocks, 256, lds, st>>>(xt, w8, scale, yt, b);
+            return;
+        }
+    }
+    lc_kernel<T, XB, NCB, KBW, false><<<blocks, 256, lds, st>>>(xt, w8, scale, yt, b);
 }
 
 template <typename T, int XB>
 cfwd_status lc_launch_t(int cfg, const LcArgs& a, const void* x, const void* wp, const float* scale, void* y,
                         hipStream_t st) {
+    const bool staged = cfg >= kLcBase;
+    cfg %= kLcBase;
     const long long per_wg = static_cast<long long>(4 / a.KW) * kLc[cfg].ncb * 32;
     const unsigned blocks = static_cast<unsigned>((a.npix + per_wg - 1) / per_wg * a.ngk);
     const T* xt = static_cast<const T*>(x);
     const uint8_t* w8 = static_cast<const uint8_t*>(wp);
     T* yt = static_cast<T*>(y);
+    // 16-byte output pieces start at pixel multiples of 16 / sizeof(T) of a
+    // channel plane: aligned when the planes and the tensor are
+    LcArgs b = a;
+    const long long pe = 16 / static_cast<long long>(sizeof(T));
+    b.vec_ok = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (static_cast<long long>(a.OH) * a.OW) % pe == 0 &&
+               a.y_img % pe == 0;
     switch (cfg) {
-        case 0: lc_kernel<T, XB, 4, 1><<<blocks, 256, 0, st>>>(xt, w8, scale, yt, a); break;
-        case 1: lc_kernel<T, XB, 2, 2><<<blocks, 256, 0, st>>>(xt, w8, scale, yt, a); break;
-        case 2: lc_kernel<T, XB, 4, 2><<<blocks, 256, 0, st>>>(xt, w8, scale, yt, a); break;
-        case 3: lc_kernel<T, XB, 1, 1><<<blocks, 256, 0, st>>>(xt, w8, scale, yt, a); break;
-        case 4: lc_kernel<T, XB, 1, 2><<<blocks, 256, 0, st>>>(xt, w8, scale, yt, a); break;
-        default: lc_kernel<T, XB, 2, 1><<<blocks, 256, 0, st>>>(xt, w8, scale, yt, a); break;
+        case 0: lc_launch_cfg<T, XB, 4, 1>(staged, blocks, b, xt, w8, scale, yt, st); break;
+        case 1: lc_launch_cfg<T, XB, 2, 2>(staged, blocks, b, xt, w8, scale, yt, st); break;
+        case 2: lc_launch_cfg<T, XB, 4, 2>(staged, blocks, b, xt, w8, scale, yt, st); break;
+        case 3: lc_launch_cfg<T, XB, 1, 1>(staged, blocks, b, xt, w8, scale, yt, st); break;
+        case 4: lc_launch_cfg<T, XB, 1, 2>(staged, blocks, b, xt, w8, scale, yt, st); break;
+        default: lc_launch_cfg<T, XB, 2, 1>(staged, blocks, b, xt, w8, scale, yt, st); break;
     }
     return check_hip(hipGetLastError(), "implicit GEMM (gather) launch");
 }

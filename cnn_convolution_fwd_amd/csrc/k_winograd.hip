@@ -595,6 +595,15 @@ bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
         if (why) *why = "winograd: no such config";
         return false;
     }
+    // F(6x6) rounds its transformed operands to fp16 for bf16 inputs; the
+    // error that adds, relative to the sum of |x*w| an output is normalised
+    // by, falls off like one over the square root of the channel count (about
+    // 0.02 at 4 channels, 0.01 at 16, 0.005 at 32 for unit-scale data), so
+    // below 32 channels per group it would not stay within the bf16 bound
+    if (m == 6 && p.dtype == CFWD_BF16 && p.cg < 32) {
+        if (why) *why = "winograd F(6x6): bf16 needs at least 32 input channels per group to meet its error bound";
+        return false;
+    }
     wg::Geo g;
     return wg::geometry(p, m, &g, why);
 }

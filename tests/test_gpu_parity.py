@@ -51,6 +51,11 @@ SMALL = [
     # past the output, ragged channel chunk and output-channel tile; stride 2
     ("rows56_ragged", 2, 40, 19, 56, 72, 3, 3, 1, 1, 1, 1),
     ("rows28_s2", 1, 24, 40, 56, 40, 3, 3, 2, 1, 1, 1),
+    # few input channels with output planes a multiple of the gather form's
+    # workgroup (its input rows staged in LDS), padding on every side
+    ("stem3x3s2_32", 2, 3, 32, 32, 32, 3, 3, 2, 1, 1, 1),
+    ("stem7x7s2_32", 2, 3, 32, 32, 64, 7, 7, 2, 3, 1, 1),
+    ("c4_k40_s1", 1, 4, 16, 24, 40, 3, 3, 1, 1, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
