@@ -355,9 +355,11 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int thw = a.TH * a.TW;
     const int tile_pix = a.TN * thw;
     const int patch_bytes = a.npix * PatchStride<FR>::value;
-    // patch buffers in LDS: three for the nine-tap path (chunk c + 1 is staged
-    // while chunk c runs), two otherwise
-    constexpr int NBUF = (RSV == 9) ? 3 : 2;
+    // patch buffers in LDS: three on the nine-tap path of big per-wave tiles
+    // (chunk c + 1 is staged while chunk c runs; their registers allow one
+    // workgroup per CU anyway, so the LDS costs no occupancy), two otherwise
+    constexpr bool TB = (RSV == 9) && (FM * FN >= 8);
+    constexpr int NBUF = TB ? 3 : 2;
     const int ih0 = oh0 * a.sh - a.ph;
     const int iw0 = ow0 * a.sw - a.pw;
     const T* __restrict__ x = static_cast<const T*>(a.x);
@@ -567,17 +569,19 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         // at compile time (a copy between prefetch buffers would make the
         // compiler wait for the load behind it):
         //  * weights: a ring of three tap buffers, tap t+2 requested at tap t;
-        //  * activations: three patch buffers, chunk c in buffer c % 3.  While
-        //    chunk c runs, chunk c + 1 is already in LDS and the eight 16-byte
-        //    loads of chunk c + 2 are issued, one per tap, each after that
-        //    tap's weight request (so no weight wait waits for an activation
-        //    load); they are written to LDS at the chunk's end, followed by
-        //    the chunk's only barrier;
-        //  * A: rolling single buffer refilled right after each use; the last
-        //    tap's refill already reads the next chunk's first tap, so the
-        //    matrix cores do not wait for LDS across a chunk boundary.
-        // Buffer (c + 2) % 3 held chunk c - 1, whose last reads were issued
-        // and completed before the barrier that ended chunk c - 1.
+        //  * activations, big per-wave tiles (TB): three patch buffers, chunk
+        //    c in buffer c % 3.  While chunk c runs, chunk c + 1 is already in
+        //    LDS and the eight 16-byte loads of chunk c + 2 are issued, one per
+        //    tap, each after that tap's weight request (so no weight wait
+        //    waits for an activation load); they are written to LDS at the
+        //    chunk's end, followed by the chunk's only barrier.  Buffer
+        //    (c + 2) % 3 held chunk c - 1, whose last reads were issued and
+        //    completed before the barrier that ended chunk c - 1;
+        //  * activations, otherwise: two buffers, the loads of chunk c + 1
+        //    issued during chunk c and written at its end;
+        //  * A: rolling single buffer refilled right after each use; with TB
+        //    the last tap's refill already reads the next chunk's first tap,
+        //    so the matrix cores do not wait for LDS across a chunk boundary.
         static_assert(FR == 32 && STG == 1 && MAXU * PP == 8, "nine-tap path needs 32x32 tiles and wide staging");
         uint4 ring[3][FN][NP];
         uint4 ra[FM][NP];
@@ -593,16 +597,19 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
         for (int f = 0; f < FM; ++f) abase[f] = qbase[f] * PS + pslot[0] * 16;
         const int last_it = total_it - 1;
-        // prologue: the weights of the first two taps and the first two
-        // chunks' activations are all requested before anything is waited for
+        // prologue: the weights of the first two taps and the first chunk(s)
+        // of activations are all requested before anything is waited for
         load_b(ring[0], 0);
         load_b(ring[1], min(1, last_it));
-        {
+        if constexpr (TB) {
             uint4 stg1[MAXU][PP];
             stage_load(0, stg);
             stage_load(1, stg1);  // zeros past the last chunk
             stage_store(0, stg);
             stage_store(1, stg1);
+        } else {
+            stage_load(0, stg);
+            stage_store(0, stg);
         }
         __syncthreads();
 #pragma unroll
@@ -611,7 +618,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(lds + abase[f] + i * PSTEP);
         int bc = 0;  // buffer of chunk c
         for (int chunk = 0; chunk < a.nchunks; ++chunk) {
-            const int bnext = (bc == 2) ? 0 : bc + 1;
+            const int bnext = TB ? ((bc == 2) ? 0 : bc + 1) : (bc ^ 1);
             const int bfar = (bnext == 2) ? 0 : bnext + 1;
             const uint8_t* pb = lds + bc * patch_bytes;
             const uint8_t* pn = lds + bnext * patch_bytes;
@@ -619,8 +626,8 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
             for (int t = 0; t < 9; ++t) {
                 load_b(ring[(t + 2) % 3], min(it0 + t + 2, last_it));
-                if (t < 8) stage_piece(chunk + 2, t);
-                const uint8_t* pt = (t < 8) ? pb + toffs[t + 1] : pn + toffs[0];
+                if (t < 8) stage_piece(chunk + (TB ? 2 : 1), t);
+                const uint8_t* pt = (t < 8) ? pb + toffs[t + 1] : (TB ? pn + toffs[0] : pb + toffs[8]);
 #pragma unroll
                 for (int i = 0; i < NP; ++i) {
 #pragma unroll
@@ -631,8 +638,17 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                     }
                 }
             }
-            if (chunk + 2 < a.nchunks) stage_store(bfar, stg);
-            __syncthreads();
+            if constexpr (TB) {
+                if (chunk + 2 < a.nchunks) stage_store(bfar, stg);
+                __syncthreads();
+            } else {
+                stage_store(bnext, stg);  // zeros past the last chunk: harmless
+                __syncthreads();
+#pragma unroll
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pn + abase[f] + i * PSTEP);
+            }
             bc = bnext;
         }
         it = total_it;
@@ -987,10 +1003,11 @@ inline bool tile_geometry(const Prob& p, const Cfg& c, int TN, int TH, int TW, G
             if (p.w % pp == 0 && chan_ok && units <= static_cast<long long>(maxu) * c.threads()) g->stg = 1;
         }
     }
-    // patch buffers (three on the nine-tap path, see launch_cfg) and one
+    // patch buffers (three on the nine-tap path of big per-wave tiles, see
+    // launch_cfg and the kernel) and one
     // 16-byte dummy slot per thread; the epilogue reuses them for an 8-byte
     // offset per register-tile pixel row
-    const size_t nbuf = (c.fr == 32 && g->stg == 1 && p.r * p.s == 9) ? 3 : 2;
+    const size_t nbuf = (c.fr == 32 && g->stg == 1 && p.r * p.s == 9 && c.fm * c.fn >= 8) ? 3 : 2;
     g->lds_bytes = std::max(nbuf * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64) + static_cast<size_t>(c.threads()) * 16,
                             static_cast<size_t>(c.pixels()) * 8);
     // 16-bit NCHW outputs of whole-row tiles leave through an LDS transpose:
