@@ -748,6 +748,69 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         }
     }
 
+    // ---- epilogue for int8 NCHW4 outputs of tiles of whole output rows (or
+    // whole images): a lane holds four consecutive pixels of one channel,
+    // whose bytes lie 4 bytes apart in NCHW4, so storing them directly writes
+    // single bytes all over the planes.  Instead the requantised tile is
+    // written to LDS in NCHW4 order, [channel block][tile pixel][4 channels]
+    // (row pitch padded by 16 bytes); a channel block's pixels of one image
+    // are contiguous in the output, so consecutive lanes then write
+    // consecutive 16-byte pieces of 4 pixels x 4 channels, or, where pieces
+    // would not be aligned, consecutive pixels' dwords.
+    if constexpr (sizeof(T) == 1 && XB == 4) {
+        const bool rows_ok = a.TW == a.OW && (a.TN == 1 ? oh0 + a.TH <= a.OH : a.TH == a.OH) && (a.Kg % 4) == 0;
+        if (rows_ok) {
+            const int pitch = tile_pix * 4 + 16;  // bytes per channel block in LDS
+            const int kt0 = g * a.Kg + kt * NT;   // first output channel of the tile
+            constexpr int NG = FT::NACC / 4;
+#pragma unroll
+            for (int nf = 0; nf < FN; ++nf) {
+                const int kk = (wn * FN + nf) * FR + lrow;  // channel within the tile
+                const int k = kt0 + kk;
+                const bool kval = kt * NT + kk < a.Kg;
+                const float sc = kval ? a.scale[k] : 0.0f;
+                uint8_t* lrow_base = lds + (kk >> 2) * pitch + (kk & 3);
+#pragma unroll
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int grp = 0; grp < NG; ++grp) {
+                        const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
+                        if (p0 < tile_pix) {
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(requant_i8(acc[f][nf][grp * 4 + v], sc));
+                        }
+                    }
+            }
+            __syncthreads();
+            const long long OHW = static_cast<long long>(a.OH) * a.OW;
+            uint8_t* ybase = static_cast<uint8_t*>(a.y) + static_cast<long long>(n0) * a.y_img +
+                             static_cast<long long>(oh0) * a.OW * 4;
+            const int nkb4 = min(NT, a.Kg - kt * NT) / 4;  // channel blocks of this tile
+            if (a.TN == 1 && (tile_pix % 4) == 0 && (a.OW % 4) == 0) {
+                const int pieces = tile_pix / 4;  // 16-byte pieces per channel block
+                for (int q = tid; q < nkb4 * pieces; q += NTHR) {
+                    const int kb = q / pieces, j = q - (q / pieces) * pieces;
+                    const uint4 v = *reinterpret_cast<const uint4*>(lds + kb * pitch + j * 16);
+                    const u32x4_t w = {v.x, v.y, v.z, v.w};
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(ybase + ((kt0 / 4 + kb) * OHW) * 4 + j * 16));
+                }
+            } else {
+                // one pixel's 4 channels (a dword) per lane; tile pixel p is
+                // pixel p % (TH * TW) of image n0 + p / (TH * TW)
+                const int nimg = min(a.TN, a.N - n0);
+                for (int q = tid; q < nkb4 * tile_pix; q += NTHR) {
+                    const int kb = q / tile_pix, pp = q - (q / tile_pix) * tile_pix;
+                    const int tn = pp / thw, rem = pp - (pp / thw) * thw;
+                    if (tn >= nimg) continue;
+                    const uint32_t v = *reinterpret_cast<const uint32_t*>(lds + kb * pitch + pp * 4);
+                    *reinterpret_cast<uint32_t*>(ybase + tn * a.y_img + ((kt0 / 4 + kb) * OHW + rem) * 4) = v;
+                }
+            }
+            return;
+        }
+    }
+
     // ---- epilogue, transposed through LDS (16-bit outputs, NCHW, tiles of
     // whole output rows): the accumulators hold, per lane, one output channel
     // of several 4-pixel groups, so storing them directly would scatter every
@@ -1014,6 +1077,9 @@ inline bool tile_geometry(const Prob& p, const Cfg& c, int TN, int TH, int TW, G
     // [NT channels][tile pixels * 2 + 16 bytes]
     if (c.fr == 32 && p.esize == 2 && p.xb == 1)
         g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(c.nt()) * (static_cast<size_t>(g->TN) * g->TH * g->TW * 2 + 16));
+    // int8 NCHW4 outputs likewise: [NT / 4 channel blocks][tile pixels * 4 + 16 bytes]
+    if (p.esize == 1 && p.xb == 4)
+        g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(c.nt() / 4) * (static_cast<size_t>(g->TN) * g->TH * g->TW * 4 + 16));
     if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk * p.g > 0x7fffffffLL) {
         if (why) *why = "implicit GEMM: grid too large";
         return false;
