@@ -388,6 +388,13 @@ def test_requant_converts_acc_to_fp32_first():
     assert float(np.float32(acc)) == 2**25 + 2**19
     assert oracle.requant_one(acc, 2.0**-20) == 32
     assert oracle.requant_one(acc + 4, 2.0**-20) == 33
+    # 2^30 + 63 becomes 2^30 in fp32; with the scale one fp32 step below
+    # 63.5 * 2^-30 the fp32 product is exactly 63.5 - 2^-18 -> 63, while the
+    # exact product, 63.5 - 9e-8, would round to the fp32 value 63.5 -> 64
+    acc = 2**30 + 63
+    scale = 127 * 2.0**-31 - 2.0**-48
+    assert float(np.float32(scale)) == scale and float(np.float32(acc)) == 2**30
+    assert oracle.requant_one(acc, scale) == 63
 
 
 def test_requant_array_matches_scalar_rule():
