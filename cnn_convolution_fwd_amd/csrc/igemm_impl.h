@@ -250,10 +250,13 @@ constexpr int kMaxUnitsPerThread = 8;
 // 32-pixel fragments instead pad each pixel to 80 bytes (also measured
 // conflict-free), which keeps the address linear in the pixel index: a filter
 // tap is then a uniform offset added to a per-fragment base.
-template <int FR> struct PatchStride { static constexpr int value = (FR == 32) ? 80 : 64; };
-template <int FR>
+// LIN: the linear 80-byte layout, used by 32x32 fragments and by the
+// nine-tap 16x16 path, where a tap must be a uniform offset (16x16 fragment
+// reads -- 16 consecutive pixels of one slot -- are conflict-free in it too).
+template <bool LIN> struct PatchStride { static constexpr int value = LIN ? 80 : 64; };
+template <bool LIN>
 __device__ __forceinline__ int lds_slot(int q, int j) {
-    if constexpr (FR == 32) return q * 80 + j * 16;
+    if constexpr (LIN) return q * 80 + j * 16;
     return q * 64 + ((j ^ ((q >> 1) & 3)) << 4);
 }
 
@@ -314,6 +317,7 @@ template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, i
 __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
     constexpr int NT = WN * FN * FR;
+    constexpr bool LIN = (FR == 32) || (RSV == 9);  // patch layout (see lds_slot)
     constexpr int E16 = 16 / static_cast<int>(sizeof(T));
     constexpr int CK = 4 * E16;
     using FT = Frag<T, FR>;
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     const int PHW = a.PH * a.PW;
     const int thw = a.TH * a.TW;
     const int tile_pix = a.TN * thw;
-    const int patch_bytes = a.npix * PatchStride<FR>::value;
+    const int patch_bytes = a.npix * PatchStride<LIN>::value;
     // patch buffers in LDS: three on the nine-tap path of big per-wave tiles
     // (chunk c + 1 is staged while chunk c runs; their registers allow one
     // workgroup per CU anyway, so the LDS costs no occupancy), two otherwise
@@ -464,11 +468,11 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 for (int p = 0; p < PP; ++p) {
                     const int col = u_pc[i] + p;
                     const bool ok = col >= 0 && col < a.PW;
-                    uint8_t* dst = ok ? base + lds_slot<FR>(u_q[i] + p, u_j[i]) : dummy;
+                    uint8_t* dst = ok ? base + lds_slot<LIN>(u_q[i] + p, u_j[i]) : dummy;
                     *reinterpret_cast<uint4*>(dst) = wide_pick<WD::SZ>(src[i], p);
                 }
             } else {
-                *reinterpret_cast<uint4*>(base + lds_slot<FR>(u_q[i], u_j[i])) = src[i][0];
+                *reinterpret_cast<uint4*>(base + lds_slot<LIN>(u_q[i], u_j[i])) = src[i][0];
             }
         }
     };
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         for (int f = 0; f < FM; ++f) {
             const int q = qbase[f] + toff;
 #pragma unroll
-            for (int i = 0; i < NP; ++i) af[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot<FR>(q, pslot[i]));
+            for (int i = 0; i < NP; ++i) af[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot<LIN>(q, pslot[i]));
         }
     };
 
@@ -563,7 +567,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 
     const int total_it = a.nchunks * RS;
     int it = 0;
-    if constexpr (RSV == 9) {
+    if constexpr (RSV == 9 && FR == 32) {
         // 3x3 (nine-tap) filters, 32x32 fragments, wide staging: the nine taps
         // of a chunk are unrolled so that every register buffer is addressed
         // at compile time (a copy between prefetch buffers would make the
@@ -588,7 +592,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         // byte offsets: tap (uniform) and fragment base (per lane); piece i of
         // a fragment is a further i * PSTEP bytes (piece_slot is 2i + h for
         // 16-bit / 8-bit types and 2h + i for fp32)
-        constexpr int PS = PatchStride<FR>::value;
+        constexpr int PS = PatchStride<LIN>::value;
         constexpr int PSTEP = (sizeof(T) == 4) ? 16 : 32;
         int toffs[9];
 #pragma unroll
@@ -652,6 +656,64 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             bc = bnext;
         }
         it = total_it;
+    } else if constexpr (RSV == 9) {
+        // 3x3 filters, 16x16 fragments: thin per-wave tiles (a few MFMAs per
+        // tap), chosen for layers with a deep reduction and few pixels, where
+        // a weight fetch from L2 outlasts several taps of MFMAs.  The nine
+        // taps of a chunk are unrolled with one weight buffer per tap,
+        // refilled right after its use with the same tap of the next chunk,
+        // so every weight fetch has a whole chunk to land.  Two patch buffers
+        // (chunk c + 1 written at the end of chunk c; its loads issued at the
+        // start of chunk c, or one per tap with wide staging), A refilled
+        // right after each use; the patch uses the linear layout, so a tap is
+        // a uniform offset.
+        static_assert(FR == 16 && (STG == 0 || MAXU * PP == 8), "nine-tap 16x16 path");
+        uint4 wr9[9][FN][NP];
+        uint4 ra[FM];
+        constexpr int PS = PatchStride<LIN>::value;
+        int toffs[9];  // byte offset of each tap (uniform)
+#pragma unroll
+        for (int t = 0; t < 9; ++t) toffs[t] = ((t / a.S) * a.dh * a.PW + (t % a.S) * a.dw) * PS;
+        int abase[FM];
+#pragma unroll
+        for (int f = 0; f < FM; ++f) abase[f] = lds_slot<LIN>(qbase[f], pslot[0]);
+        const int last_it = total_it - 1;
+#pragma unroll
+        for (int t = 0; t < 9; ++t) load_b(wr9[t], t);
+        stage_load(0, stg);
+        stage_store(0, stg);
+        __syncthreads();
+#pragma unroll
+        for (int f = 0; f < FM; ++f) ra[f] = *reinterpret_cast<const uint4*>(lds + abase[f]);
+        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+            const int buf = chunk & 1;
+            const bool more = chunk + 1 < a.nchunks;
+            const uint8_t* pb = lds + buf * patch_bytes;
+            const int itn = (chunk + 1) * 9;  // first tap of the next chunk
+            if constexpr (STG == 0) {
+                if (more) stage_load(chunk + 1, stg);
+            }
+#pragma unroll
+            for (int t = 0; t < 9; ++t) {
+                if constexpr (STG == 1) {
+                    if (t < 8) stage_piece(chunk + 1, t);
+                }
+                const uint8_t* pt = pb + toffs[t < 8 ? t + 1 : 8];
+#pragma unroll
+                for (int f = 0; f < FM; ++f) {
+#pragma unroll
+                    for (int nf = 0; nf < FN; ++nf) Mma<T>::run(acc[f][nf], ra[f], wr9[t][nf][0]);
+                    ra[f] = *reinterpret_cast<const uint4*>(pt + abase[f]);
+                }
+                load_b(wr9[t], min(itn + t, last_it));
+            }
+            if (STG == 1 || more) stage_store(buf ^ 1, stg);  // wide: zeros past the last chunk
+            __syncthreads();
+            const uint8_t* pn = lds + (buf ^ 1) * patch_bytes;
+#pragma unroll
+            for (int f = 0; f < FM; ++f) ra[f] = *reinterpret_cast<const uint4*>(pn + abase[f]);
+        }
+        it = total_it;
     } else if constexpr (FR == 32) {
         // 32x32 fragments run one wave per SIMD and are software-pipelined
         // by hand, with a branch-free tap body:
@@ -670,7 +732,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             for (int f = 0; f < FM; ++f) {
                 const int q = qbase[f] + toff;
 #pragma unroll
-                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot<FR>(q, pslot[i]));
+                for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pb + lds_slot<LIN>(q, pslot[i]));
             }
         };
         load_b(bnxt, total_it > 1 ? 1 : 0);
@@ -705,7 +767,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
                         for (int nf = 0; nf < FN; ++nf) Mma32<T>::piece(acc[f][nf], ra[f][i], bcur[nf][i], i);
                         ra[f][i] = *reinterpret_cast<const uint4*>(
-                            pb + lds_slot<FR>(qbase[f] + toff_next, pslot[i]));
+                            pb + lds_slot<LIN>(qbase[f] + toff_next, pslot[i]));
                     }
                 }
 #pragma unroll
@@ -1071,7 +1133,10 @@ inline bool tile_geometry(const Prob& p, const Cfg& c, int TN, int TH, int TW, G
     // 16-byte dummy slot per thread; the epilogue reuses them for an 8-byte
     // offset per register-tile pixel row
     const size_t nbuf = (c.fr == 32 && g->stg == 1 && p.r * p.s == 9 && c.fm * c.fn >= 8) ? 3 : 2;
-    g->lds_bytes = std::max(nbuf * static_cast<size_t>(g->npix) * (c.fr == 32 ? 80 : 64) + static_cast<size_t>(c.threads()) * 16,
+    // linear 80-byte pixel slots for 32x32 fragments and the nine-tap 16x16
+    // path, swizzled 64-byte slots otherwise
+    const size_t pstride = (c.fr == 32 || p.r * p.s == 9) ? 80 : 64;
+    g->lds_bytes = std::max(nbuf * static_cast<size_t>(g->npix) * pstride + static_cast<size_t>(c.threads()) * 16,
                             static_cast<size_t>(c.pixels()) * 8);
     // 16-bit NCHW outputs of whole-row tiles leave through an LDS transpose:
     // [NT channels][tile pixels * 2 + 16 bytes]
@@ -1179,12 +1244,14 @@ cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, cons
         constexpr Cfg c = kCfgs[ID];                                                                       \
         if constexpr (Wide<T, XB>::ok) {                                                                   \
             if (g.stg == 1) {                                                                              \
-                if constexpr (c.fr == 32)                                                                  \
-                    if (p.r * p.s == 9)                                                                    \
-                        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9>(p, g, x, wp, scale, y, st); \
+                if (p.r * p.s == 9)                                                                        \
+                    return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9>(p, g, x, wp, scale, y, st);   \
                 return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 0>(p, g, x, wp, scale, y, st);   \
             }                                                                                              \
         }                                                                                                  \
+        if constexpr (c.fr == 16)                                                                          \
+            if (p.r * p.s == 9)                                                                            \
+                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 9>(p, g, x, wp, scale, y, st);   \
         return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 0>(p, g, x, wp, scale, y, st);           \
     }
         CFWD_IG_CFG(0)
