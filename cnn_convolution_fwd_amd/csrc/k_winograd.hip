@@ -31,103 +31,12 @@
 // transform entries reach 32, so bf16's 8 bits lose too much for F(6x6)); fp32
 // inputs keep fp32 operands on the fp32 matrix cores.  Accumulation is fp32.
 #include "igemm_impl.h"
+#include "winograd_mats.h"
 
 namespace cfwd {
 namespace wg {
 
 using ig::f32x16;
-
-// ------------------------------------------------------------ matrices
-
-template <int M> struct Mats {
-    static constexpr int A = M + 2;
-    double at[M][A] = {};
-    double g[A][3] = {};
-    double bt[A][A] = {};
-};
-
-constexpr double kInf = 1e300;  // marks the point at infinity
-
-template <int M>
-constexpr Mats<M> build_mats() {
-    constexpr int A = M + 2;
-    double pts[A] = {};
-    if (M == 2) {
-        const double p[4] = {0.0, 1.0, -1.0, kInf};
-        for (int i = 0; i < 4; ++i) pts[i] = p[i];
-    } else {
-        const double p[8] = {0.0, 1.0, -1.0, 2.0, -2.0, 0.5, -0.5, kInf};
-        for (int i = 0; i < 8; ++i) pts[i] = p[i];
-    }
-    // evaluation matrices
-    double v[A][A] = {};
-    for (int i = 0; i < A; ++i)
-        for (int j = 0; j < A; ++j) {
-            if (pts[i] == kInf) {
-                v[i][j] = (j == A - 1) ? 1.0 : 0.0;
-            } else {
-                double x = 1.0;
-                for (int e = 0; e < j; ++e) x *= pts[i];
-                v[i][j] = x;
-            }
-        }
-    Mats<M> r{};
-    for (int i = 0; i < A; ++i) {
-        for (int j = 0; j < M; ++j) {
-            double x = 1.0;
-            if (pts[i] == kInf) {
-                x = (j == M - 1) ? 1.0 : 0.0;
-            } else {
-                for (int e = 0; e < j; ++e) x *= pts[i];
-            }
-            r.at[j][i] = x;  // A^T = V_m^T
-        }
-        for (int j = 0; j < 3; ++j) {
-            double x = 1.0;
-            if (pts[i] == kInf) {
-                x = (j == 2) ? 1.0 : 0.0;
-            } else {
-                for (int e = 0; e < j; ++e) x *= pts[i];
-            }
-            r.g[i][j] = x;  // G = V_3
-        }
-    }
-    // V^-1 by Gauss-Jordan with partial pivoting
-    double aug[A][2 * A] = {};
-    for (int i = 0; i < A; ++i)
-        for (int j = 0; j < A; ++j) {
-            aug[i][j] = v[i][j];
-            aug[i][A + j] = (i == j) ? 1.0 : 0.0;
-        }
-    for (int col = 0; col < A; ++col) {
-        int piv = col;
-        for (int rr = col + 1; rr < A; ++rr) {
-            const double a = aug[rr][col] < 0 ? -aug[rr][col] : aug[rr][col];
-            const double b = aug[piv][col] < 0 ? -aug[piv][col] : aug[piv][col];
-            if (a > b) piv = rr;
-        }
-        for (int j = 0; j < 2 * A; ++j) {
-            const double t = aug[col][j];
-            aug[col][j] = aug[piv][j];
-            aug[piv][j] = t;
-        }
-        const double inv = 1.0 / aug[col][col];
-        for (int j = 0; j < 2 * A; ++j) aug[col][j] *= inv;
-        for (int rr = 0; rr < A; ++rr) {
-            if (rr == col) continue;
-            const double f = aug[rr][col];
-            if (f == 0.0) continue;
-            for (int j = 0; j < 2 * A; ++j) aug[rr][j] -= f * aug[col][j];
-        }
-    }
-    for (int i = 0; i < A; ++i)
-        for (int j = 0; j < A; ++j) r.bt[i][j] = aug[j][A + i];  // B^T = (V^-1)^T
-    return r;
-}
-
-template <int M> struct MatsF {
-    static constexpr Mats<M> d = build_mats<M>();
-};
 
 // ------------------------------------------------------------ operand types
 
@@ -588,9 +497,12 @@ cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vpr
 
 }  // namespace wg
 
-int winograd_num_configs(int) { return 1; }
+// F(2x2): config 0 = the three-launch form above (any float dtype and
+// layout), config 1 = the fused single-launch kernel (bf16 NCHW).
+int winograd_num_configs(int m) { return m == 2 ? 2 : 1; }
 
 bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
+    if (m == 2 && cfg == 1) return winograd_fused_supported(p, why);
     if (cfg != 0 || (m != 2 && m != 6)) {
         if (why) *why = "winograd: no such config";
         return false;
@@ -608,19 +520,22 @@ bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
     return wg::geometry(p, m, &g, why);
 }
 
-size_t winograd_filter_bytes(const Prob& p, int m, int) {
+size_t winograd_filter_bytes(const Prob& p, int m, int cfg) {
+    if (m == 2 && cfg == 1) return winograd_fused_filter_bytes(p);
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
     return g.v_bytes;
 }
 
-size_t winograd_scratch_bytes(const Prob& p, int m, int) {
+size_t winograd_scratch_bytes(const Prob& p, int m, int cfg) {
+    if (m == 2 && cfg == 1) return 0;
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
     return g.u_bytes;
 }
 
-cfwd_status winograd_prepare(const Prob& p, int m, int, const void* w, void* wp, hipStream_t st) {
+cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st) {
+    if (m == 2 && cfg == 1) return winograd_fused_prepare(p, w, wp, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
@@ -643,8 +558,9 @@ cfwd_status winograd_prepare(const Prob& p, int m, int, const void* w, void* wp,
     return check_hip(hipGetLastError(), "winograd filter transform launch");
 }
 
-cfwd_status winograd_launch(const Prob& p, int m, int, const void* x, const void* wp, void* scratch, void* y,
+cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch, void* y,
                             hipStream_t st) {
+    if (m == 2 && cfg == 1) return winograd_fused_launch(p, x, wp, y, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);

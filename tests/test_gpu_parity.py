@@ -56,6 +56,11 @@ SMALL = [
     ("stem3x3s2_32", 2, 3, 32, 32, 32, 3, 3, 2, 1, 1, 1),
     ("stem7x7s2_32", 2, 3, 32, 32, 64, 7, 7, 2, 3, 1, 1),
     ("c4_k40_s1", 1, 4, 16, 24, 40, 3, 3, 1, 1, 1, 1),
+    # fused Winograd F(2x2) tile blocks: 8 x 8 tiles with pad 0 and an output
+    # width that is not a multiple of 8; two 32-tile column blocks with a
+    # ragged channel chunk and output-channel block
+    ("wino_p0_w16", 2, 48, 16, 16, 64, 3, 3, 1, 0, 1, 1),
+    ("wino_w72", 1, 33, 10, 72, 70, 3, 3, 1, 1, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
