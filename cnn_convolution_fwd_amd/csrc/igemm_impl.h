@@ -1081,8 +1081,16 @@ constexpr Cfg kCfgs[] = {
     {2, 2, 2, 2, 32},  // 11: 128 px x 128 ch
     {1, 4, 4, 1, 32},  // 12: 128 px x 128 ch
     {2, 2, 4, 1, 32},  // 13: 256 px x  64 ch
+    // eight waves, two per SIMD: for layers whose tiles only just fill the
+    // CUs (deep, small-image layers), where one wave per SIMD leaves the
+    // operand latencies exposed
+    {4, 2, 2, 2, 16},  // 14: 128 px x  64 ch
+    {4, 2, 2, 4, 16},  // 15: 128 px x 128 ch
+    {4, 2, 4, 2, 16},  // 16: 256 px x  64 ch
 };
 constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
+
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one CU (gfx950)
 
 struct Geo {
     int TN, TH, TW, PH, PW, npix, tiles_n, tiles_h, tiles_w, nchunks, ntk;
@@ -1145,6 +1153,10 @@ inline bool tile_geometry(const Prob& p, const Cfg& c, int TN, int TH, int TW, G
     // int8 NCHW4 outputs likewise: [NT / 4 channel blocks][tile pixels * 4 + 16 bytes]
     if (p.esize == 1 && p.xb == 4)
         g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(c.nt() / 4) * (static_cast<size_t>(g->TN) * g->TH * g->TW * 4 + 16));
+    if (g->lds_bytes > kLdsBytes) {
+        if (why) *why = "implicit GEMM: the tile needs more LDS than a CU has";
+        return false;
+    }
     if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk * p.g > 0x7fffffffLL) {
         if (why) *why = "implicit GEMM: grid too large";
         return false;
@@ -1168,8 +1180,13 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
         TH = 1;
         TW = P;
     }
-    // shrink the tile until its input patch fits
-    const int maxpix = kMaxUnitsPerThread * c.threads() / 4;
+    // shrink the tile until its input patch fits: the staging units of the
+    // workgroup, and the patch buffers (plus the per-thread dummy slots) in
+    // the 160 KiB of LDS of a CU
+    const size_t nbuf = (c.fr == 32 && p.r * p.s == 9 && c.fm * c.fn >= 8) ? 3 : 2;
+    const size_t pstride = (c.fr == 32 || p.r * p.s == 9) ? 80 : 64;
+    const int lds_pix = static_cast<int>((kLdsBytes - static_cast<size_t>(c.threads()) * 16) / (nbuf * pstride));
+    const int maxpix = std::min(kMaxUnitsPerThread * c.threads() / 4, lds_pix);
     for (;;) {
         const int PH = (TH - 1) * p.sh + (p.r - 1) * p.dh + 1;
         const int PW = (TW - 1) * p.sw + (p.s - 1) * p.dw + 1;
@@ -1268,6 +1285,9 @@ cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, cons
         CFWD_IG_CFG(11)
         CFWD_IG_CFG(12)
         CFWD_IG_CFG(13)
+        CFWD_IG_CFG(14)
+        CFWD_IG_CFG(15)
+        CFWD_IG_CFG(16)
 #undef CFWD_IG_CFG
         default:
             return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM: no such config");
