@@ -86,12 +86,12 @@ cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void*
 cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch,
                             void* y, hipStream_t st);
 
-// Fused Winograd F(2x2,3x3) for bf16 NCHW (config 1 of F(2x2)): the
+// Fused Winograd F(2x2,3x3) for bf16 NCHW (configs 1 and 2 of F(2x2)): the
 // transformed input stays on chip, no scratch.
-bool winograd_fused_supported(const Prob& p, std::string* why);
-size_t winograd_fused_filter_bytes(const Prob& p);
-cfwd_status winograd_fused_prepare(const Prob& p, const void* w, void* wp, hipStream_t st);
-cfwd_status winograd_fused_launch(const Prob& p, const void* x, const void* wp, void* y, hipStream_t st);
+bool winograd_fused_supported(const Prob& p, int cfg, std::string* why);
+size_t winograd_fused_filter_bytes(const Prob& p, int cfg);
+cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
+cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, hipStream_t st);
 
 // Writes 0 to the NCHWX output channels past K (no-op unless K % xb != 0).
 cfwd_status zero_output_channel_padding(const Prob& p, void* y, hipStream_t st);

@@ -498,11 +498,11 @@ cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vpr
 }  // namespace wg
 
 // F(2x2): config 0 = the three-launch form above (any float dtype and
-// layout), config 1 = the fused single-launch kernel (bf16 NCHW).
-int winograd_num_configs(int m) { return m == 2 ? 2 : 1; }
+// layout), configs 1 and 2 = the fused single-launch kernels (bf16 NCHW).
+int winograd_num_configs(int m) { return m == 2 ? 3 : 1; }
 
 bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
-    if (m == 2 && cfg == 1) return winograd_fused_supported(p, why);
+    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_supported(p, cfg, why);
     if (cfg != 0 || (m != 2 && m != 6)) {
         if (why) *why = "winograd: no such config";
         return false;
@@ -521,21 +521,21 @@ bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
 }
 
 size_t winograd_filter_bytes(const Prob& p, int m, int cfg) {
-    if (m == 2 && cfg == 1) return winograd_fused_filter_bytes(p);
+    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_filter_bytes(p, cfg);
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
     return g.v_bytes;
 }
 
 size_t winograd_scratch_bytes(const Prob& p, int m, int cfg) {
-    if (m == 2 && cfg == 1) return 0;
+    if (m == 2 && (cfg == 1 || cfg == 2)) return 0;
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
     return g.u_bytes;
 }
 
 cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st) {
-    if (m == 2 && cfg == 1) return winograd_fused_prepare(p, w, wp, st);
+    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_prepare(p, cfg, w, wp, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
@@ -560,7 +560,7 @@ cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void*
 
 cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch, void* y,
                             hipStream_t st) {
-    if (m == 2 && cfg == 1) return winograd_fused_launch(p, x, wp, y, st);
+    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_launch(p, cfg, x, wp, y, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);

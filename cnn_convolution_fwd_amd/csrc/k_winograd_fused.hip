@@ -151,6 +151,15 @@ constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008;
 // The eight MFMAs of one step interleaved with NV VALU instructions each of
 // the next step's work.
 template <int NV>
+__device__ __forceinline__ void interleave3() {
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, NV, 0);
+    }
+}
+
+template <int NV>
 __device__ __forceinline__ void interleave() {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -481,14 +490,385 @@ __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
     }
 }
 
+// ---------------------------------------------------------------- folded form (config 2)
+// The same staging and input transform, with A^T's fold over j moved into
+// the reduction: Z[w][q] = sum_j A^T[q][j] (U[w][j] V[w][j]) is accumulated
+// directly (A^T has three nonzeros per row, entries +-1, so 6 MFMAs per tile
+// fragment and k-step instead of 4, with U[j] negated where A^T[q][j] = -1).
+// That halves the accumulators per output channel, so a workgroup covers
+// KB2 = 128 output channels (2 q x 2 tile fragments x 4 channel fragments =
+// 256 accumulators per lane), and each staged patch, LDS read, transform
+// and filter byte feeds three times the MFMA work of config 1.  The filter
+// of one k-step (64 VGPRs) is reloaded fragment by fragment right after its
+// last MFMA, so it needs no second register set.
+constexpr int KB2 = 128;
+
+template <int TCB, int PWO>
+__global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
+    using G = Geo<TCB>;
+    constexpr int TR = G::TR, PUE = G::PUE, MAXU = G::MAXU;
+    constexpr F2 f2 = build_f2();
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int m = lane & 31;
+    const int h = lane >> 5;
+
+    int lin = xcd_linear(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    const int kt = lin % a.ntk;
+    lin /= a.ntk;
+    const int tbc = lin % a.tbw;
+    lin /= a.tbw;
+    const int tbr = lin % a.tbh;
+    const int n = lin / a.tbh;
+    const int tr0 = tbr * TR, tc0 = tbc * TCB;
+    const int ih0 = 2 * tr0 - a.ph, iw0 = 2 * tc0 - PWO;
+    const int HW = a.H * a.W;
+    const int HW2 = 2 * HW;
+    const uint8_t* __restrict__ xn = reinterpret_cast<const uint8_t*>(a.x + n * a.x_img);
+
+    const int cbf = (iw0 >= 0) ? iw0 / 8 : -((-iw0 + 7) / 8);
+    int u_voff[MAXU];
+    int u_lds[MAXU];
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+        const int u = tid + i * NTHR;
+        const int t = u >> 2;
+        const int cb = t % a.nblk;
+        const int row = t / a.nblk;
+        const int j = u & 3;
+        const int ih = ih0 + row;
+        const int iwb = (cbf + cb) * 8;
+        const bool unit = row < G::PH;
+        const bool in = unit && static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) &&
+                        static_cast<unsigned>(iwb) < static_cast<unsigned>(a.W);
+        u_voff[i] = in ? (j * 8 * HW + ih * a.W + iwb) * 2 : static_cast<int>(0x80000000u);
+        const int colx0 = iwb - iw0 + 8;
+        u_lds[i] = unit ? ((row * 2) * PUE + (colx0 >> 1)) * PIX + j * 16 : 2 * G::PATCH;
+    }
+    uint4 stg[MAXU][8];
+    auto stage_load = [&](int chunk) {
+        const int cleft = a.C - chunk * CK;
+        const int nrec = cleft > 0 ? cleft * HW2 : 0;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(xn) + static_cast<long long>(chunk) * CK * HW2, 0, nrec, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i)
+#pragma unroll
+            for (int l = 0; l < 8; ++l) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, u_voff[i] + l * HW2, 0, 0);
+                stg[i][l] = make_uint4(v.x, v.y, v.z, v.w);
+            }
+    };
+    auto stage_store = [&](int bufoff) {
+#pragma unroll
+        for (int i = 0; i < MAXU; ++i) {
+            uint8_t* base = lds + bufoff + u_lds[i];
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+                const int off = (((PWO + p) & 1) * PUE + ((PWO + p) >> 1)) * PIX;
+                uint4 o;
+                o.x = cvt_pair(word_of(stg[i][0], p >> 1), word_of(stg[i][1], p >> 1), p & 1);
+                o.y = cvt_pair(word_of(stg[i][2], p >> 1), word_of(stg[i][3], p >> 1), p & 1);
+                o.z = cvt_pair(word_of(stg[i][4], p >> 1), word_of(stg[i][5], p >> 1), p & 1);
+                o.w = cvt_pair(word_of(stg[i][6], p >> 1), word_of(stg[i][7], p >> 1), p & 1);
+                *reinterpret_cast<uint4*>(base + off) = o;
+            }
+        }
+    };
+
+    const int ra = wave == 0 ? f2.ra[0] : wave == 1 ? f2.ra[1] : wave == 2 ? f2.ra[2] : f2.ra[3];
+    const int rb = wave == 0 ? f2.rb[0] : wave == 1 ? f2.rb[1] : wave == 2 ? f2.rb[2] : f2.rb[3];
+    const int sa = wave == 0 ? f2.sa[0] : wave == 1 ? f2.sa[1] : wave == 2 ? f2.sa[2] : f2.sa[3];
+    const h2 sa2 = {static_cast<_Float16>(sa), static_cast<_Float16>(sa)};
+    int tbase[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int s = m + 32 * f;
+        const int tr = s / TCB, tc = s % TCB;
+        tbase[f] = ((2 * tr) * 2 * PUE + tc + 4) * PIX + h * 16;
+    }
+    const int offA = ra * 2 * PUE * PIX, offB = rb * 2 * PUE * PIX;
+
+    // prepared filter: [kt][chunk][xi][b (4)][ks][32 rows][half][16 B], 128 KiB
+    // per (kt, chunk); this wave's four positions are 32 KiB
+    constexpr int VCH = 16 * (KB2 / 32) * 2048;
+    const uint8_t* __restrict__ vbase =
+        a.v + static_cast<long long>(kt) * a.nchunks * VCH + wave * 4 * (KB2 / 32) * 2048 + m * 32 + h * 16;
+    uint4 vb[4][4];  // [j][b] of the current k-step
+    auto load_vb = [&](int chunk, int ks, int b) {
+        const uint8_t* p = vbase + static_cast<long long>(chunk) * VCH + ks * 1024 + b * 2048;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vb[j][b] = *reinterpret_cast<const uint4*>(p + j * (KB2 / 32) * 2048);
+    };
+
+    uint4 da[4], db[4];
+    auto read_d = [&](int bufoff, int ks, int f) {
+        const uint8_t* q = lds + bufoff + tbase[f] + ks * 32;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int co = ((c & 1) * PUE + (c >> 1)) * PIX;
+            da[c] = *reinterpret_cast<const uint4*>(q + offA + co);
+            db[c] = *reinterpret_cast<const uint4*>(q + offB + co);
+        }
+    };
+    // U[j] for j = 0..3, and -U[j] in slot 4 + j where A^T needs it
+    auto transform = [&](uint4 (&U)[8]) {
+        h2 t[4][4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                t[c][e] = __builtin_bit_cast(h2, word_of(da[c], e)) * sa2 + __builtin_bit_cast(h2, word_of(db[c], e));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bool neg = false;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) neg = neg || f2.at[q][j] < 0;
+            uint32_t wp[4], wn[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                h2 s = {0, 0};
+                bool first = true;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int co = f2.bt[j][c];
+                    if (co == 0) continue;
+                    if (first) {
+                        s = co > 0 ? t[c][e] : -t[c][e];
+                        first = false;
+                    } else {
+                        s = co > 0 ? s + t[c][e] : s - t[c][e];
+                    }
+                }
+                wp[e] = __builtin_bit_cast(uint32_t, s);
+                wn[e] = wp[e] ^ 0x80008000u;
+            }
+            U[j] = make_uint4(wp[0], wp[1], wp[2], wp[3]);
+            if (neg) U[4 + j] = make_uint4(wn[0], wn[1], wn[2], wn[3]);
+        }
+    };
+
+    f32x16 acc[2][2][4];  // [q][f][b]
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[q][f][b] = f32x16{};
+    // MFMAs of channel fragment b of one step
+    auto mma_b = [&](const uint4 (&U)[8], int f, int b) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int co = f2.at[q][j];
+                if (co == 0) continue;
+                acc[q][f][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    __builtin_bit_cast(f16x8, co > 0 ? U[j] : U[4 + j]), __builtin_bit_cast(f16x8, vb[j][b]),
+                    acc[q][f][b], 0, 0, 0);
+            }
+    };
+    // one step: its 24 MFMAs with the next step's VALU work between them;
+    // with `reload`, each channel fragment's filter is reloaded for
+    // (rchunk, rks) right after its last MFMA of this k-step
+    auto step = [&](const uint4 (&U)[8], int f, bool reload, int rchunk, int rks) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            mma_b(U, f, b);
+            if (reload) load_vb(rchunk, rks, b);
+        }
+    };
+
+    // ---- prologue
+    stage_load(0);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) load_vb(0, 0, b);
+    stage_store(0);
+    __syncthreads();
+    uint4 ucur[8], unext[8];
+    read_d(0, 0, 0);
+    transform(ucur);
+    read_d(0, 0, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+
+    for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+        const int cur = (chunk & 1) * G::PATCH;
+        const int nb = G::PATCH - cur;
+        const int nxt = chunk + 1 < a.nchunks ? chunk + 1 : chunk;
+        stage_load(chunk + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // step (ks 0, f 0)
+        step(ucur, 0, false, 0, 0);
+        transform(unext);
+        interleave3<4>();
+        __builtin_amdgcn_sched_barrier(0);
+        read_d(cur, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ucur[j] = unext[j];
+        // step (0, 1): the last use of k-step 0's filter; reload k-step 1's
+        step(ucur, 1, true, chunk, 1);
+        transform(unext);
+        interleave3<4>();
+        __builtin_amdgcn_sched_barrier(0);
+        read_d(cur, 1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ucur[j] = unext[j];
+        // step (1, 0), with the next chunk's staging stores
+        step(ucur, 0, false, 0, 0);
+        transform(unext);
+        stage_store(nb);
+        interleave3<8>();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ucur[j] = unext[j];
+        __syncthreads();
+        read_d(nb, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        // step (1, 1): last use of k-step 1's filter; reload the next chunk's
+        // k-step 0
+        step(ucur, 1, true, nxt, 0);
+        transform(unext);
+        interleave3<4>();
+        __builtin_amdgcn_sched_barrier(0);
+        read_d(nb, 0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ucur[j] = unext[j];
+    }
+    __syncthreads();
+
+    // ---- output transform, one half of the channel fragments at a time:
+    // accumulator v of fragment (q, f, b) is Z[w][q] of tile slot
+    // 32f + 8(v/4) + 4h + v%4 and output channel 32b + m
+    float* Zs = reinterpret_cast<float*>(lds);
+    constexpr int GPR = TCB / 4;
+    const bool vec_ok = (a.OW % 8) == 0;
+    // whole-row runs: one column block spans the output width, the 2TR rows
+    // lie inside the output, and rows are whole 16-byte pieces
+    const bool runs = vec_ok && a.tbw == 1 && 2 * (tr0 + TR) <= a.OH;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+            for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int b = 2 * hb + bb;
+                    float z[8];
+#pragma unroll
+                    for (int vv = 0; vv < 4; ++vv) {
+                        z[2 * vv] = acc[0][f][b][4 * v4 + vv];
+                        z[2 * vv + 1] = acc[1][f][b][4 * v4 + vv];
+                    }
+                    const int s0 = 32 * f + 8 * v4 + 4 * h;
+                    float* dst = Zs + (wave * 64 + 32 * bb + m) * ZP + 2 * s0;
+                    *reinterpret_cast<float4*>(dst) = make_float4(z[0], z[1], z[2], z[3]);
+                    *reinterpret_cast<float4*>(dst + 4) = make_float4(z[4], z[5], z[6], z[7]);
+                }
+        __syncthreads();
+        if (runs) {
+            // the block covers whole output rows: each channel's 2TR rows are
+            // one contiguous run of 2TR * OW outputs, written as consecutive
+            // 16-byte pieces (8 columns of one row) by consecutive lanes
+            const int ppr = a.OW / 8;        // pieces per row
+            const int ppc = 2 * TR * ppr;    // pieces per channel
+            const int nk = min(64, a.K - (kt * KB2 + hb * 64));
+            uint16_t* ybase = a.y + n * a.y_img + static_cast<long long>(kt * KB2 + hb * 64) * a.OH * a.OW +
+                              static_cast<long long>(2 * tr0) * a.OW;
+            for (int job = tid; job < nk * ppc; job += NTHR) {
+                const int kl = job / ppc;
+                const int pc = job - kl * ppc;
+                const int row = pc / ppr;
+                const int g = pc - row * ppr;
+                const int tr = row >> 1, p = row & 1;
+                const int pos0 = tr * 2 * TCB + 8 * g;
+                float yv[8] = {};
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int co = f2.at[p][w];
+                    const float* src = Zs + (w * 64 + kl) * ZP + pos0;
+                    const float4 lo = *reinterpret_cast<const float4*>(src);
+                    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+                    const float zz[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (co > 0) yv[e] += zz[e];
+                        if (co < 0) yv[e] -= zz[e];
+                    }
+                }
+                const u32x4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                                 pack_bf16x2(yv[6], yv[7])};
+                __builtin_nontemporal_store(
+                    o, reinterpret_cast<u32x4*>(ybase + static_cast<long long>(kl) * a.OH * a.OW + pc * 8));
+            }
+            __syncthreads();
+            continue;
+        }
+        for (int job = tid; job < 64 * TR * GPR; job += NTHR) {
+            const int g = job % GPR;
+            const int rest = job / GPR;
+            const int tr = rest % TR;
+            const int kl = rest / TR;
+            const int k = kt * KB2 + hb * 64 + kl;
+            if (k >= a.K) continue;
+            const int pos0 = tr * 2 * TCB + 8 * g;
+            float z[4][8];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float* src = Zs + (w * 64 + kl) * ZP + pos0;
+                const float4 lo = *reinterpret_cast<const float4*>(src);
+                const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+                z[w][0] = lo.x; z[w][1] = lo.y; z[w][2] = lo.z; z[w][3] = lo.w;
+                z[w][4] = hi.x; z[w][5] = hi.y; z[w][6] = hi.z; z[w][7] = hi.w;
+            }
+            const int ow0 = 2 * tc0 + 8 * g;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int oh = 2 * (tr0 + tr) + p;
+                if (oh >= a.OH) continue;
+                float yv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float s = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int co = f2.at[p][w];
+                        if (co > 0) s += z[w][e];
+                        if (co < 0) s -= z[w][e];
+                    }
+                    yv[e] = s;
+                }
+                uint16_t* dst = a.y + n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
+                if (vec_ok && ow0 + 8 <= a.OW) {
+                    const u32x4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
+                                     pack_bf16x2(yv[6], yv[7])};
+                    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(dst));
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (ow0 + e < a.OW) dst[e] = float_to_bf16(yv[e]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- filter prepare
 // V[kt][chunk][xi = 4i + j][b][ks][m][h][8 fp16] = (G' g G'^T)[i][j] for output
-// channel kt*64 + 32b + m and input channel chunk*32 + 16ks + 8h + e; zero past
+// channel kt*KBT + 32b + m (KBT = 64 for config 1, 128 for config 2) and input channel chunk*32 + 16ks + 8h + e; zero past
 // K and C.
+template <int KBT>
 __global__ __launch_bounds__(256) void wf2_prepare_kernel(const uint16_t* __restrict__ w, _Float16* __restrict__ out,
                                                           int K, int C, int ntk, int nchunks) {
     constexpr F2 f2 = build_f2();
-    const long long total = static_cast<long long>(ntk) * KB * nchunks * CK;
+    const long long total = static_cast<long long>(ntk) * KBT * nchunks * CK;
     for (long long idx = blockIdx.x * 256LL + threadIdx.x; idx < total; idx += static_cast<long long>(gridDim.x) * 256) {
         const int c = static_cast<int>(idx % (nchunks * CK));
         const int k = static_cast<int>(idx / (nchunks * CK));
@@ -506,7 +886,7 @@ __global__ __launch_bounds__(256) void wf2_prepare_kernel(const uint16_t* __rest
                 for (int r = 0; r < 3; ++r) acc = fmaf(f2.gp[i][r], gg[r][s], acc);
                 tmp[i][s] = acc;
             }
-        const int kt = k / KB, kl = k % KB, b = kl / 32, mm = kl % 32;
+        const int kt = k / KBT, kl = k % KBT, b = kl / 32, mm = kl % 32;
         const int chunk = c / CK, cl = c % CK, ks = cl / 16, hh = (cl % 16) / 8, e = cl % 8;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -516,8 +896,8 @@ __global__ __launch_bounds__(256) void wf2_prepare_kernel(const uint16_t* __rest
 #pragma unroll
                 for (int s = 0; s < 3; ++s) acc = fmaf(tmp[i][s], f2.gp[j][s], acc);
                 const long long base =
-                    ((((((static_cast<long long>(kt) * nchunks + chunk) * 16 + (4 * i + j)) * 2 + b) * 2 + ks) * 32 + mm) * 2 +
-                     hh) * 8 + e;
+                    ((((((static_cast<long long>(kt) * nchunks + chunk) * 16 + (4 * i + j)) * (KBT / 32) + b) * 2 + ks) * 32 +
+                      mm) * 2 + hh) * 8 + e;
                 out[base] = static_cast<_Float16>(acc);
             }
     }
@@ -528,7 +908,7 @@ struct Plan {
     size_t v_bytes;
 };
 
-inline bool plan(const Prob& p, Plan* pl, std::string* why) {
+inline bool plan(const Prob& p, int kb, Plan* pl, std::string* why) {
     auto no = [&](const char* s) {
         if (why) *why = s;
         return false;
@@ -548,7 +928,7 @@ inline bool plan(const Prob& p, Plan* pl, std::string* why) {
     pl->tr = TBL / pl->tcb;
     pl->tbh = (pl->th + pl->tr - 1) / pl->tr;
     pl->tbw = (pl->tw + pl->tcb - 1) / pl->tcb;
-    pl->ntk = (p.k + KB - 1) / KB;
+    pl->ntk = (p.k + kb - 1) / kb;
     pl->nchunks = (p.c + CK - 1) / CK;
     const int pw_cols = 2 * pl->tcb + 2;
     const int first = (p.pw > 0) ? -1 : 0;  // floor(-pw / 8)
@@ -556,17 +936,18 @@ inline bool plan(const Prob& p, Plan* pl, std::string* why) {
     pl->nblk = last - first + 1;
     const long long blocks = static_cast<long long>(p.n) * pl->tbh * pl->tbw * pl->ntk;
     if (blocks > (1LL << 31) - 1) return no("winograd fused: too many workgroups");
-    pl->v_bytes = static_cast<size_t>(pl->ntk) * pl->nchunks * 65536;
+    pl->v_bytes = static_cast<size_t>(pl->ntk) * pl->nchunks * 16 * kb * CK * 2;
     return true;
 }
 
-template <int TCB, int PWO>
+template <int TCB, int PWO, bool FOLD>
 cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void* vp, void* y, hipStream_t st) {
     using G = Geo<TCB>;
     static_assert(G::LDS <= 160 * 1024, "LDS budget");
     if (pl.nblk > G::NBMAX) return set_error(CFWD_ERR_UNSUPPORTED, "winograd fused: patch wider than planned");
     static bool attr = false;
-    cfwd_status s = ig::allow_big_lds(wf2_kernel<TCB, PWO>, G::LDS, &attr);
+    auto kern = FOLD ? wf2f_kernel<TCB, PWO> : wf2_kernel<TCB, PWO>;
+    cfwd_status s = ig::allow_big_lds(kern, G::LDS, &attr);
     if (s != CFWD_OK) return s;
     Args a;
     a.x = static_cast<const uint16_t*>(x);
@@ -576,44 +957,58 @@ cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void*
     a.x_img = p.x_img; a.y_img = p.y_img;
     a.tbh = pl.tbh; a.tbw = pl.tbw; a.ntk = pl.ntk; a.nchunks = pl.nchunks; a.nblk = pl.nblk;
     const unsigned blocks = static_cast<unsigned>(static_cast<long long>(p.n) * pl.tbh * pl.tbw * pl.ntk);
-    wf2_kernel<TCB, PWO><<<blocks, NTHR, G::LDS, st>>>(a);
+    kern<<<blocks, NTHR, G::LDS, st>>>(a);
     return check_hip(hipGetLastError(), "winograd fused launch");
 }
 
+template <bool FOLD>
+cfwd_status launch_fold(const Prob& p, const Plan& pl, const void* x, const void* wp, void* y, hipStream_t st) {
+    const bool p1 = p.pw == 1;
+    switch (pl.tcb) {
+        case 32: return p1 ? launch_tcb<32, 1, FOLD>(p, pl, x, wp, y, st) : launch_tcb<32, 0, FOLD>(p, pl, x, wp, y, st);
+        case 16: return p1 ? launch_tcb<16, 1, FOLD>(p, pl, x, wp, y, st) : launch_tcb<16, 0, FOLD>(p, pl, x, wp, y, st);
+        default: return p1 ? launch_tcb<8, 1, FOLD>(p, pl, x, wp, y, st) : launch_tcb<8, 0, FOLD>(p, pl, x, wp, y, st);
+    }
+}
+
+inline int kb_of(int cfg) { return cfg == 2 ? KB2 : KB; }
+
 }  // namespace wf
 
-bool winograd_fused_supported(const Prob& p, std::string* why) {
+// cfg 1: the fused kernel (64 output channels per workgroup); cfg 2: the
+// folded form (128 output channels per workgroup).
+bool winograd_fused_supported(const Prob& p, int cfg, std::string* why) {
     wf::Plan pl;
-    return wf::plan(p, &pl, why);
+    return wf::plan(p, wf::kb_of(cfg), &pl, why);
 }
 
-size_t winograd_fused_filter_bytes(const Prob& p) {
+size_t winograd_fused_filter_bytes(const Prob& p, int cfg) {
     wf::Plan pl;
-    return wf::plan(p, &pl, nullptr) ? pl.v_bytes : 0;
+    return wf::plan(p, wf::kb_of(cfg), &pl, nullptr) ? pl.v_bytes : 0;
 }
 
-cfwd_status winograd_fused_prepare(const Prob& p, const void* w, void* wp, hipStream_t st) {
+cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
     wf::Plan pl;
     std::string why;
-    if (!wf::plan(p, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
-    const long long total = static_cast<long long>(pl.ntk) * wf::KB * pl.nchunks * wf::CK;
+    const int kb = wf::kb_of(cfg);
+    if (!wf::plan(p, kb, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    const long long total = static_cast<long long>(pl.ntk) * kb * pl.nchunks * wf::CK;
     const unsigned nb = static_cast<unsigned>(std::min<long long>((total + 255) / 256, 65536));
-    wf::wf2_prepare_kernel<<<nb, 256, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<_Float16*>(wp), p.k, p.c,
-                                                pl.ntk, pl.nchunks);
+    if (kb == wf::KB2)
+        wf::wf2_prepare_kernel<wf::KB2><<<nb, 256, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<_Float16*>(wp),
+                                                             p.k, p.c, pl.ntk, pl.nchunks);
+    else
+        wf::wf2_prepare_kernel<wf::KB><<<nb, 256, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<_Float16*>(wp),
+                                                            p.k, p.c, pl.ntk, pl.nchunks);
     return check_hip(hipGetLastError(), "winograd fused filter transform launch");
 }
 
-cfwd_status winograd_fused_launch(const Prob& p, const void* x, const void* wp, void* y, hipStream_t st) {
+cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, hipStream_t st) {
     wf::Plan pl;
     std::string why;
-    if (!wf::plan(p, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    if (!wf::plan(p, wf::kb_of(cfg), &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (wp == nullptr) return set_error(CFWD_ERR_WORKSPACE, "winograd fused: prepared filter is required");
-    const bool p1 = p.pw == 1;
-    switch (pl.tcb) {
-        case 32: return p1 ? wf::launch_tcb<32, 1>(p, pl, x, wp, y, st) : wf::launch_tcb<32, 0>(p, pl, x, wp, y, st);
-        case 16: return p1 ? wf::launch_tcb<16, 1>(p, pl, x, wp, y, st) : wf::launch_tcb<16, 0>(p, pl, x, wp, y, st);
-        default: return p1 ? wf::launch_tcb<8, 1>(p, pl, x, wp, y, st) : wf::launch_tcb<8, 0>(p, pl, x, wp, y, st);
-    }
+    return cfg == 2 ? wf::launch_fold<true>(p, pl, x, wp, y, st) : wf::launch_fold<false>(p, pl, x, wp, y, st);
 }
 
 }  // namespace cfwd
