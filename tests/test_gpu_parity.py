@@ -61,6 +61,9 @@ SMALL = [
     # ragged channel chunk and output-channel block
     ("wino_p0_w16", 2, 48, 16, 16, 64, 3, 3, 1, 0, 1, 1),
     ("wino_w72", 1, 33, 10, 72, 70, 3, 3, 1, 1, 1, 1),
+    # deep 7x7 layer: int8 has four 64-channel chunks, so every split of the
+    # reduction over workgroups runs (ragged last split with 3 of 4)
+    ("deep7x7_c256", 2, 256, 7, 7, 72, 3, 3, 1, 1, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
