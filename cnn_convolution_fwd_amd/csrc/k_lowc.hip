@@ -186,8 +186,8 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
     int st_n = 0, st_row0 = 0;
     if constexpr (STG) {
         const long long W0 = pg * wpix;
-        st_n = static_cast<int>(W0 / ohw);
-        st_row0 = static_cast<int>(W0 - static_cast<long long>(st_n) * ohw) / a.OW * a.sh - a.ph;
+        st_n = static_cast<int>(static_cast<unsigned>(W0) / static_cast<unsigned>(ohw));
+        st_row0 = static_cast<int>(static_cast<unsigned>(W0) - static_cast<unsigned>(st_n) * ohw) / a.OW * a.sh - a.ph;
         // 16-byte chunks of every staged row; chunks are wholly inside or
         // wholly outside the image (W and padL are multiples of a chunk)
         constexpr int CE = 16 / static_cast<int>(sizeof(G));  // gather elements per chunk
@@ -219,11 +219,13 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
     bool pok[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        const long long G0 = P0 + cb * 32 + j;
-        pok[cb] = G0 < a.npix;
-        const long long Gc = pok[cb] ? G0 : 0;
-        const int n = static_cast<int>(Gc / ohw);
-        const int pix = static_cast<int>(Gc - static_cast<long long>(n) * ohw);
+        // pixel indices fit in 31 bits (checked on the host): 32-bit
+        // divisions, which are several times cheaper than 64-bit ones
+        const unsigned G0 = static_cast<unsigned>(P0) + cb * 32 + j;
+        pok[cb] = G0 < static_cast<unsigned>(a.npix);
+        const unsigned Gc = pok[cb] ? G0 : 0u;
+        const int n = static_cast<int>(Gc / static_cast<unsigned>(ohw));
+        const int pix = static_cast<int>(Gc - static_cast<unsigned>(n) * ohw);
         const int oh = pix / a.OW, ow = pix - (pix / a.OW) * a.OW;
         ih0[cb] = oh * a.sh - a.ph;
         iw0[cb] = ow * a.sw - a.pw;
@@ -324,8 +326,8 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             if (k >= a.K) continue;
             const long long G0 = W0 + pc * PE;
             if (G0 >= a.npix) continue;
-            const int n = static_cast<int>(G0 / ohw);
-            const int pix = static_cast<int>(G0 - static_cast<long long>(n) * ohw);
+            const int n = static_cast<int>(static_cast<unsigned>(G0) / static_cast<unsigned>(ohw));
+            const int pix = static_cast<int>(static_cast<unsigned>(G0) - static_cast<unsigned>(n) * ohw);
             const uint8_t* src = otile + cl * pitch + pc * 16;
             T* dst = y + n * a.y_img + static_cast<long long>(k) * ohw + pix;
             if (a.vec_ok && G0 + PE <= a.npix && pix + PE <= ohw) {
@@ -338,8 +340,8 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                 for (int e = 0; e < PE; ++e) {
                     long long Ge = G0 + e;
                     if (Ge >= a.npix) break;
-                    const int ne = static_cast<int>(Ge / ohw);
-                    const int pe = static_cast<int>(Ge - static_cast<long long>(ne) * ohw);
+                    const int ne = static_cast<int>(static_cast<unsigned>(Ge) / static_cast<unsigned>(ohw));
+                    const int pe = static_cast<int>(static_cast<unsigned>(Ge) - static_cast<unsigned>(ne) * ohw);
                     T* de = y + ne * a.y_img + static_cast<long long>(k) * ohw + pe;
                     if constexpr (sizeof(T) == 4)
                         *de = *reinterpret_cast<const float*>(src + e * E);
@@ -356,9 +358,9 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         if (!pok[cb]) continue;
-        const long long G0 = P0 + cb * 32 + j;
-        const int n = static_cast<int>(G0 / ohw);
-        const int pix = static_cast<int>(G0 - static_cast<long long>(n) * ohw);
+        const unsigned G0 = static_cast<unsigned>(P0) + cb * 32 + j;
+        const int n = static_cast<int>(G0 / static_cast<unsigned>(ohw));
+        const int pix = static_cast<int>(G0 - static_cast<unsigned>(n) * ohw);
         const int oh = pix / a.OW, ow = pix - (pix / a.OW) * a.OW;
 #pragma unroll
         for (int b = 0; b < KBW; ++b) {
@@ -439,6 +441,7 @@ bool lc_geometry(const Prob& p, int cfg, LcArgs* a, std::string* why) {
     a->KW = kwaves >= 4 ? 4 : (kwaves >= 2 ? 2 : 1);
     a->ngk = (kwaves + a->KW - 1) / a->KW;
     a->npix = static_cast<long long>(p.n) * p.oh * p.ow;
+    if (a->npix + 1024 >= (1LL << 31)) return fail("implicit GEMM (gather): more than 2^31 output pixels");
     const long long per_wg = static_cast<long long>(4 / a->KW) * lc.ncb * 32;
     const long long pgroups = (a->npix + per_wg - 1) / per_wg;
     if (pgroups * a->ngk >= (1LL << 31)) return fail("implicit GEMM (gather): grid too large");
