@@ -115,11 +115,12 @@ __global__ __launch_bounds__(256) void pw_kernel(const T* __restrict__ x, const 
     const int kb0 = (kg * KW + wk) * KBW;
     if (kb0 >= nkb) return;  // no barrier in this kernel: idle waves may leave
     const long long P0 = (pg * (4 / KW) + wpx) * kWavePix;
-    const long long G = P0 + kPPL * lrow;  // this lane's first pixel (npix % 4 == 0)
-    const bool pix_ok = G < npix;
-    const long long Gc = pix_ok ? G : npix - kPPL;
-    const long long n = Gc / HW;
-    const int p = static_cast<int>(Gc - n * HW);
+    // pixel indices fit in 31 bits (checked on the host): a 32-bit division
+    const unsigned G = static_cast<unsigned>(P0) + kPPL * lrow;  // this lane's first pixel (npix % 4 == 0)
+    const bool pix_ok = G < static_cast<unsigned>(npix);
+    const unsigned Gc = pix_ok ? G : static_cast<unsigned>(npix) - kPPL;
+    const long long n = Gc / static_cast<unsigned>(HW);
+    const int p = static_cast<int>(Gc - static_cast<unsigned>(n) * HW);
     const T* xb = x + n * x_img + p;
     T* yb = y + n * y_img + p;
 
@@ -217,6 +218,7 @@ bool geometry(const Prob& p, int cfg, PwGeo* g, std::string* why) {
     g->KW = kwaves >= 4 ? 4 : (kwaves >= 2 ? 2 : 1);
     g->ngk = (kwaves + g->KW - 1) / g->KW;
     g->npix = hw * p.n;
+    if (g->npix + 1024 >= (1LL << 31)) return fail("pointwise: more than 2^31 pixels");
     const long long pix_per_wg = static_cast<long long>(4 / g->KW) * kWavePix;
     g->pgroups = (g->npix + pix_per_wg - 1) / pix_per_wg;
     if (g->pgroups * g->ngk >= (1LL << 31)) return fail("pointwise: grid too large");
