@@ -139,8 +139,9 @@ def copy_calibration():
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU: this library has no multi-GPU path (batch sharding is described in "
-              "DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: this library has no multi-GPU path (images are independent, so the "
+              "path would shard along the batch with replicated weights and no collective); run with --gpus 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
