@@ -64,6 +64,9 @@ SMALL = [
     # deep 7x7 layer: int8 has four 64-channel chunks, so every split of the
     # reduction over workgroups runs (ragged last split with 3 of 4)
     ("deep7x7_c256", 2, 256, 7, 7, 72, 3, 3, 1, 1, 1, 1),
+    # 3x3 with no vertical and one column of horizontal padding (Winograd
+    # tile blocks with different row and column offsets)
+    ("asym_pad_3x3", 2, 24, 12, 16, 40, 3, 3, 1, (0, 1), 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
