@@ -158,6 +158,24 @@ __device__ __forceinline__ int8_t requant_i8(int acc, float scale) {
     return static_cast<int8_t>(static_cast<int>(q));
 }
 
+// The same value as requant_i8, in the low byte of the result (the other
+// bytes are not defined), in four branch-free instructions: the clamp comes
+// before the rounding, which gives the same result because both bounds are
+// integers; adding 1.5 * 2^23 then rounds to the nearest integer (ties to
+// even, the default rounding) and leaves it, in two's complement, in the low
+// mantissa bits.
+__device__ __forceinline__ uint32_t requant_i8_bits(int acc, float scale) {
+    const float q = __builtin_amdgcn_fmed3f(__fmul_rn(static_cast<float>(acc), scale), -127.0f, 127.0f);
+    return __float_as_uint(__fadd_rn(q, 12582912.0f));
+}
+
+// Low bytes of four words -> one word, b0 in the lowest byte.
+__device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     static __device__ __forceinline__ float to_f(float v) { return v; }

@@ -167,7 +167,11 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
         Tap t;
         t.dr = -(1 << 28);  // padding unit: always out of range -> 0
         t.ds = 0;
-        t.off = STG ? -1 : 0;
+        // staged int8 reads a padding unit from the pixel's own first tap: its
+        // prepared weights are zero and int8 products are finite, so no select
+        // is needed; float types read zeros instead (an Inf in the input would
+        // otherwise give NaN)
+        t.off = (STG && sizeof(T) != 1) ? -1 : 0;
         const int nu = (sizeof(T) == 1) ? RS : a.units;
         if (u < nu) {
             const int c = (sizeof(T) == 1) ? 0 : u / RS;
@@ -194,14 +198,33 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
         const int cpr = a.RW / CE;
         const int nch = (sizeof(T) == 1) ? 1 : a.C;
         const G* xg = reinterpret_cast<const G*>(x) + static_cast<long long>(st_n) * (sizeof(T) == 1 ? a.x_img / 4 : a.x_img);
-        for (int q = tid; q < nch * a.ROWS * cpr; q += 256) {
-            const int col = q % cpr, t2 = q / cpr;
-            const int rr = t2 % a.ROWS, c = t2 / a.ROWS;
-            const int ih = st_row0 + rr, iw = col * CE - a.padL;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) && iw >= 0 && iw < a.W)
-                v = *reinterpret_cast<const uint4*>(xg + (static_cast<long long>(c) * a.H + ih) * a.W + iw);
-            *reinterpret_cast<uint4*>(lds_dyn + ((static_cast<long long>(c) * a.ROWS + rr) * a.RW + col * CE) * sizeof(G)) = v;
+        // chunk q = (c * ROWS + rr) * cpr + col, stepped by 256 without
+        // divisions inside the loop, four chunks per thread at a time: the
+        // four loads (from a clamped, always valid address; zeros outside the
+        // image) are all in flight before the first LDS write
+        int col = tid % cpr, rr = tid / cpr, c = 0;
+        while (rr >= a.ROWS) rr -= a.ROWS, ++c;
+        const int dcol = 256 % cpr, drow = 256 / cpr;
+        constexpr int NB = 4;
+        while (c < nch) {
+            uint4 v[NB];
+            int dst[NB];
+#pragma unroll
+            for (int i = 0; i < NB; ++i) {
+                const bool live = c < nch;
+                const int ih = st_row0 + rr, iw = col * CE - a.padL;
+                const bool in = live && static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) && iw >= 0 && iw < a.W;
+                const uint4 t = *reinterpret_cast<const uint4*>(xg + (in ? (static_cast<long long>(c) * a.H + ih) * a.W + iw : 0));
+                v[i] = in ? t : make_uint4(0, 0, 0, 0);
+                dst[i] = live ? ((c * a.ROWS + rr) * a.RW + col * CE) * static_cast<int>(sizeof(G)) : -1;
+                col += dcol;
+                rr += drow;
+                if (col >= cpr) col -= cpr, ++rr;
+                while (rr >= a.ROWS) rr -= a.ROWS, ++c;
+            }
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+                if (dst[i] >= 0) *reinterpret_cast<uint4*>(lds_dyn + dst[i]) = v[i];
         }
     }
     __syncthreads();
@@ -215,7 +238,7 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
 
     // this lane's pixel in each column block
     long long xbase[NCB];
-    int ih0[NCB], iw0[NCB], lbase[NCB];
+    int ih0[NCB], iw0[NCB], lbase[NCB], pn[NCB], ppix[NCB];
     bool pok[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
@@ -226,6 +249,8 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
         const unsigned Gc = pok[cb] ? G0 : 0u;
         const int n = static_cast<int>(Gc / static_cast<unsigned>(ohw));
         const int pix = static_cast<int>(Gc - static_cast<unsigned>(n) * ohw);
+        pn[cb] = n;
+        ppix[cb] = pix;
         const int oh = pix / a.OW, ow = pix - (pix / a.OW) * a.OW;
         ih0[cb] = oh * a.sh - a.ph;
         iw0[cb] = ow * a.sw - a.pw;
@@ -247,7 +272,10 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             const Tap t = tab[ss * L::SSU + L::unit(g, h)];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                if constexpr (STG) {
+                if constexpr (STG && sizeof(T) == 1) {
+                    v[cb][g] = lx[lbase[cb] + t.off];
+                    continue;
+                } else if constexpr (STG) {
                     const bool ok = t.off >= 0;
                     const G val = lx[ok ? lbase[cb] + t.off : 0];
                     v[cb][g] = ok ? val : G{};
@@ -355,30 +383,52 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
 
     // D[row = channel][col = pixel]: lane (j, hh), element v -> channel
     // 8 (v / 4) + 4 hh + v % 4 of the block
+    // int8: requantisation scales of this lane's 16 channels of each k block
+    // (channel 8 (v / 4) + 4 h + v % 4, as the accumulator holds them), all
+    // requested at once, at constant offsets from one address where the
+    // block lies inside K; channels past K get scale 0, which requantises to
+    // the zero bytes that NCHW4 keeps in its padding channels
+    float sc[KBW][16];
+    if constexpr (sizeof(T) == 1) {
+#pragma unroll
+        for (int b = 0; b < KBW; ++b) {
+            const int kb = (kb0 + b) * 32 + 4 * h;
+            if ((kb0 + b) * 32 + 32 <= a.K) {
+                const float* sp = scale + kb;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sc[b][v] = sp[8 * (v / 4) + (v % 4)];
+            } else {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int k = kb + 8 * (v / 4) + (v % 4);
+                    const float t = scale[min(k, a.K - 1)];
+                    sc[b][v] = k < a.K ? t : 0.0f;
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
         if (!pok[cb]) continue;
-        const unsigned G0 = static_cast<unsigned>(P0) + cb * 32 + j;
-        const int n = static_cast<int>(G0 / static_cast<unsigned>(ohw));
-        const int pix = static_cast<int>(G0 - static_cast<unsigned>(n) * ohw);
+        const int n = pn[cb], pix = ppix[cb];
         const int oh = pix / a.OW, ow = pix - (pix / a.OW) * a.OW;
 #pragma unroll
         for (int b = 0; b < KBW; ++b) {
             if constexpr (sizeof(T) == 1) {
-                // four consecutive channels of one pixel -> one NCHW4 dword
+                // four consecutive channels of one pixel -> one NCHW4 dword, at
+                // a wave-uniform offset from this lane's first one
+                const long long ohw4 = static_cast<long long>(ohw) * 4;
+                uint8_t* yb = reinterpret_cast<uint8_t*>(y) + n * a.y_img + static_cast<long long>(pix) * 4 +
+                              static_cast<long long>(kb0 * 8 + h) * ohw4;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int k0 = (kb0 + b) * 32 + 8 * q + 4 * h;
                     if (k0 >= a.K) continue;
-                    uint32_t word = 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int k = k0 + e;
-                        const int8_t r8 = (k < a.K) ? requant_i8(acc[b][cb][4 * q + e], scale[k]) : int8_t(0);
-                        word |= static_cast<uint32_t>(static_cast<uint8_t>(r8)) << (8 * e);
-                    }
-                    uint8_t* yb = reinterpret_cast<uint8_t*>(y) + n * a.y_img;
-                    *reinterpret_cast<uint32_t*>(yb + (static_cast<long long>(k0 / 4) * ohw + pix) * 4) = word;
+                    const typename L::Acc& ac = acc[b][cb];
+                    const uint32_t word = pack_low_bytes(
+                        requant_i8_bits(ac[4 * q], sc[b][4 * q]), requant_i8_bits(ac[4 * q + 1], sc[b][4 * q + 1]),
+                        requant_i8_bits(ac[4 * q + 2], sc[b][4 * q + 2]), requant_i8_bits(ac[4 * q + 3], sc[b][4 * q + 3]));
+                    *reinterpret_cast<uint32_t*>(yb + (b * 8 + 2 * q) * ohw4) = word;
                 }
             } else {
 #pragma unroll
