@@ -48,6 +48,9 @@ struct LcArgs {
     // into LDS, [channel][ROWS][RW] gather elements, the image columns at
     // padL .. padL + W - 1 and zeros around them
     int ROWS, RW, padL, st_bytes;
+    // staged fp32/bf16: element offset of a zero-filled region of ROWS * RW
+    // elements after the staged rows, read by the reduction's padding units
+    int zoff;
 };
 
 struct Tap {
@@ -144,12 +147,12 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
     using L = Lc<T>;
     using G = typename L::G;
     constexpr int TILE = lc_tile_bytes<T, XB, NCB, KBW>();
-    // dynamic LDS (sized by lc_lds_bytes): [staged input rows (STG)][unit
-    // table] while gathering, then, after a barrier, the transposed output
-    // tile in the same bytes
+    // dynamic LDS (sized by lc_lds_bytes): [staged input rows and zero
+    // region (STG)][unit table] while gathering, then, after a barrier, the
+    // transposed output tile in the same bytes
     extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-    const G* lx = reinterpret_cast<const G*>(lds_dyn);
     Tap* tab = reinterpret_cast<Tap*>(lds_dyn + (STG ? a.st_bytes : 0));
+    int* toff = reinterpret_cast<int*>(lds_dyn + a.st_bytes);  // STG's table
     uint8_t* otile = lds_dyn;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int j = lane & 31, h = lane >> 5;
@@ -159,19 +162,35 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
     const long long pg = static_cast<long long>(blockIdx.x) / a.ngk;
     const int wpix = (4 / a.KW) * NCB * 32;  // pixels of this workgroup (all in one image when STG)
 
-    // reduction unit -> (row delta, column delta, channel offset); staged:
-    // off = the unit's LDS element offset from a pixel's base, -1 = padding
+    // reduction unit -> (row delta, column delta, channel offset)
     const int RS = a.R * a.S;
     const int ntab = a.nss * L::SSU;
-    for (int u = tid; u < ntab; u += 256) {
+    if constexpr (STG) {
+        // staged: byte offset of each unit's element from a pixel's base in
+        // LDS, ordered [step][lane half][gather] so that a lane reads a
+        // step's offsets with 16-byte loads.  Padding units read zeros from
+        // the zero region (fp32/bf16: an Inf times a zero weight would be
+        // NaN), or, for int8, the pixel's own first tap: their weights are
+        // zero and int8 products are finite.
+        for (int i = tid; i < ntab; i += 256) {
+            const int ss = i / L::SSU, rem = i % L::SSU;
+            const int u = ss * L::SSU + L::unit(rem % L::NG, rem / L::NG);
+            int off = (sizeof(T) == 1) ? 0 : a.zoff;
+            const int nu = (sizeof(T) == 1) ? RS : a.units;
+            if (u < nu) {
+                const int c = (sizeof(T) == 1) ? 0 : u / RS;
+                const int tap = (sizeof(T) == 1) ? u : u % RS;
+                const int r = tap / a.S, s = tap % a.S;
+                off = (c * a.ROWS + r * a.dh) * a.RW + s * a.dw;
+            }
+            toff[i] = off * static_cast<int>(sizeof(G));
+        }
+    }
+    for (int u = tid; u < (STG ? 0 : ntab); u += 256) {
         Tap t;
         t.dr = -(1 << 28);  // padding unit: always out of range -> 0
         t.ds = 0;
-        // staged int8 reads a padding unit from the pixel's own first tap: its
-        // prepared weights are zero and int8 products are finite, so no select
-        // is needed; float types read zeros instead (an Inf in the input would
-        // otherwise give NaN)
-        t.off = (STG && sizeof(T) != 1) ? -1 : 0;
+        t.off = 0;
         const int nu = (sizeof(T) == 1) ? RS : a.units;
         if (u < nu) {
             const int c = (sizeof(T) == 1) ? 0 : u / RS;
@@ -179,19 +198,17 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             const int r = tap / a.S, s = tap % a.S;
             t.dr = r * a.dh;
             t.ds = s * a.dw;
-            if (STG)
-                t.off = (c * a.ROWS + r * a.dh) * a.RW + s * a.dw;
-            else if (sizeof(T) != 1)
-                t.off = (XB == 1) ? c * a.H * a.W : (c / XB) * a.H * a.W * XB + c % XB;
+            if (sizeof(T) != 1) t.off = (XB == 1) ? c * a.H * a.W : (c / XB) * a.H * a.W * XB + c % XB;
         }
         tab[u] = t;
     }
     // staged: first input row of this workgroup and its image
-    int st_n = 0, st_row0 = 0;
+    int st_n = 0, st_row0 = 0, st_pix0 = 0;
     if constexpr (STG) {
         const long long W0 = pg * wpix;
         st_n = static_cast<int>(static_cast<unsigned>(W0) / static_cast<unsigned>(ohw));
-        st_row0 = static_cast<int>(static_cast<unsigned>(W0) - static_cast<unsigned>(st_n) * ohw) / a.OW * a.sh - a.ph;
+        st_pix0 = static_cast<int>(static_cast<unsigned>(W0) - static_cast<unsigned>(st_n) * ohw);
+        st_row0 = st_pix0 / a.OW * a.sh - a.ph;
         // 16-byte chunks of every staged row; chunks are wholly inside or
         // wholly outside the image (W and padL are multiples of a chunk)
         constexpr int CE = 16 / static_cast<int>(sizeof(G));  // gather elements per chunk
@@ -226,6 +243,9 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             for (int i = 0; i < NB; ++i)
                 if (dst[i] >= 0) *reinterpret_cast<uint4*>(lds_dyn + dst[i]) = v[i];
         }
+        if constexpr (sizeof(T) != 1)
+            for (int q = tid; q < a.ROWS * cpr; q += 256)
+                *reinterpret_cast<uint4*>(lds_dyn + (a.zoff + q * CE) * sizeof(G)) = make_uint4(0, 0, 0, 0);
     }
     __syncthreads();
 
@@ -255,9 +275,14 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
         ih0[cb] = oh * a.sh - a.ph;
         iw0[cb] = ow * a.sw - a.pw;
         xbase[cb] = (sizeof(T) == 1) ? n * (a.x_img / 4) : n * a.x_img;
-        // staged: element of tap (0, 0), channel 0 of this pixel in LDS
-        lbase[cb] = pok[cb] ? (ih0[cb] - st_row0) * a.RW + iw0[cb] + a.padL : 0;
+        // staged: byte offset of tap (0, 0), channel 0 of this pixel in LDS
+        lbase[cb] = pok[cb] ? ((ih0[cb] - st_row0) * a.RW + iw0[cb] + a.padL) * static_cast<int>(sizeof(G)) : 0;
     }
+
+    // staged: this lane's pixel in LDS, one address per column block
+    const uint8_t* lpix[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) lpix[cb] = lds_dyn + lbase[cb];
 
     typename L::Acc acc[KBW][NCB];
 #pragma unroll
@@ -267,20 +292,23 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
 
     const G* xg = reinterpret_cast<const G*>(x);
     auto gather = [&](int ss, G (*v)[L::NG], uint4* wv) {
+        if constexpr (STG) {
+            int4 o[L::NG / 4];
 #pragma unroll
-        for (int g = 0; g < L::NG; ++g) {
+            for (int i = 0; i < L::NG / 4; ++i)
+                o[i] = *reinterpret_cast<const int4*>(toff + (ss * 2 + h) * L::NG + 4 * i);
+#pragma unroll
+            for (int g = 0; g < L::NG; ++g) {
+                const int og = (g % 4 == 0) ? o[g / 4].x : (g % 4 == 1) ? o[g / 4].y : (g % 4 == 2) ? o[g / 4].z : o[g / 4].w;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) v[cb][g] = *reinterpret_cast<const G*>(lpix[cb] + og);
+            }
+        }
+#pragma unroll
+        for (int g = 0; g < (STG ? 0 : L::NG); ++g) {
             const Tap t = tab[ss * L::SSU + L::unit(g, h)];
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
-                if constexpr (STG && sizeof(T) == 1) {
-                    v[cb][g] = lx[lbase[cb] + t.off];
-                    continue;
-                } else if constexpr (STG) {
-                    const bool ok = t.off >= 0;
-                    const G val = lx[ok ? lbase[cb] + t.off : 0];
-                    v[cb][g] = ok ? val : G{};
-                    continue;
-                }
                 const int ih = ih0[cb] + t.dr, iw = iw0[cb] + t.ds;
                 const bool ok = static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) &&
                                 static_cast<unsigned>(iw) < static_cast<unsigned>(a.W);
@@ -348,14 +376,23 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
         const int pieces = wpix / PE;
         const long long W0 = pg * wpix;  // first pixel of this workgroup
         const int kbase = kg * a.KW * KBW * 32;
-        for (int q = tid; q < wch * pieces; q += 256) {
-            const int cl = q / pieces, pc = q - (q / pieces) * pieces;
+        // piece (cl, pc) = channel row cl, pixels pc * PE ..; stepped by 256
+        // pieces without divisions; staged workgroups lie in one image
+        int cl = tid / pieces, pc = tid - (tid / pieces) * pieces;
+        const int dcl = 256 / pieces, dpc = 256 - (256 / pieces) * pieces;
+        for (; cl < wch; pc += dpc, cl += dcl, cl += (pc >= pieces), pc -= (pc >= pieces) ? pieces : 0) {
             const int k = kbase + cl;
             if (k >= a.K) continue;
             const long long G0 = W0 + pc * PE;
             if (G0 >= a.npix) continue;
-            const int n = static_cast<int>(static_cast<unsigned>(G0) / static_cast<unsigned>(ohw));
-            const int pix = static_cast<int>(static_cast<unsigned>(G0) - static_cast<unsigned>(n) * ohw);
+            int n, pix;
+            if constexpr (STG) {
+                n = st_n;
+                pix = st_pix0 + pc * PE;
+            } else {
+                n = static_cast<int>(static_cast<unsigned>(G0) / static_cast<unsigned>(ohw));
+                pix = static_cast<int>(static_cast<unsigned>(G0) - static_cast<unsigned>(n) * ohw);
+            }
             const uint8_t* src = otile + cl * pitch + pc * 16;
             T* dst = y + n * a.y_img + static_cast<long long>(k) * ohw + pix;
             if (a.vec_ok && G0 + PE <= a.npix && pix + PE <= ohw) {
@@ -495,7 +532,7 @@ bool lc_geometry(const Prob& p, int cfg, LcArgs* a, std::string* why) {
     const long long per_wg = static_cast<long long>(4 / a->KW) * lc.ncb * 32;
     const long long pgroups = (a->npix + per_wg - 1) / per_wg;
     if (pgroups * a->ngk >= (1LL << 31)) return fail("implicit GEMM (gather): grid too large");
-    a->ROWS = a->RW = a->padL = a->st_bytes = 0;
+    a->ROWS = a->RW = a->padL = a->st_bytes = a->zoff = 0;
     if (staged) {
         // gather element: the dtype's element, or an NCHW4 int8 pixel's dword
         const int gsz = (p.dtype == CFWD_I8) ? 4 : p.esize;
@@ -510,13 +547,16 @@ bool lc_geometry(const Prob& p, int cfg, LcArgs* a, std::string* why) {
         long long rw = std::max<long long>(ce + p.w, need);
         rw = (rw + ce - 1) / ce * ce;
         const long long nch = (p.dtype == CFWD_I8) ? 1 : p.c;
-        const long long sb = (nch * rows * rw * gsz + 15) / 16 * 16;
+        // fp32/bf16: a zero region of one channel's rows after the staged rows
+        const long long zrows = (p.dtype == CFWD_I8) ? 0 : rows;
+        const long long sb = ((nch * rows + zrows) * rw * gsz + 15) / 16 * 16;
         if (sb + static_cast<long long>(nss) * ssu * static_cast<long long>(sizeof(Tap)) > static_cast<long long>(kLcStageMax))
             return fail("implicit GEMM (gather, staged): input rows of a workgroup exceed the LDS budget");
         a->ROWS = static_cast<int>(rows);
         a->RW = static_cast<int>(rw);
         a->padL = ce;
         a->st_bytes = static_cast<int>(sb);
+        a->zoff = static_cast<int>(nch * rows * rw);
     }
     return true;
 }
