@@ -150,6 +150,26 @@ template <> struct RawVec<2> {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
+// Division of numerators below 2^31 by a divisor d >= 1 fixed at launch, as
+// a multiply-high and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, theorem 4.2 with N = 31):
+// with l = ceil(log2 d) and m = ceil(2^(31 + l) / d), which is below 2^32,
+// n / d = (n * m) >> (31 + l).  m = 0 stands for d = 1.
+struct FastDiv {
+    uint32_t m;
+    int sh;  // l - 1, the shift applied to the high word of n * m
+};
+FastDiv make_fastdiv(uint32_t d) {
+    if (d <= 1) return FastDiv{0u, 0};
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    const unsigned long long m = ((1ull << (31 + l)) + d - 1) / d;
+    return FastDiv{static_cast<uint32_t>(m), l - 1};
+}
+__device__ __forceinline__ int fast_div(int n, FastDiv f) {
+    return f.m ? static_cast<int>(__umulhi(static_cast<uint32_t>(n), f.m) >> f.sh) : n;
+}
+
 template <typename T, int NW> constexpr int dw_vpt() { return NW * Words<T>::PER_WORD; }
 
 // Workgroup = SPB whole strips (a strip = one plane n*C + c and one band of
@@ -163,13 +183,15 @@ template <typename T, int NW> constexpr int dw_vpt() { return NW * Words<T>::PER
 template <typename T, int RB, int NW>
 __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, const T* __restrict__ w,
                                                        T* __restrict__ y, int C, int H, int W, long long x_img,
-                                                       long long y_img, int cols, int bands, int strips) {
+                                                       long long y_img, int cols, int bands, int strips, int spb,
+                                                       FastDiv fd_cols, FastDiv fd_bands, FastDiv fd_c) {
     using WD = Words<T>;
     constexpr int V = dw_vpt<T, NW>();
     __shared__ uint32_t first_w[RB + 2][256], last_w[RB + 2][256];
     const int tid = threadIdx.x;
-    const int spb = 256 / cols;
-    const int sl = tid / cols;
+    // spb = 256 / cols whole strips per workgroup; the divisions by cols,
+    // bands and C are multiply-high reciprocals computed on the host
+    const int sl = fast_div(tid, fd_cols);
     const int cg = tid - sl * cols;
     // plain dispatch order: at any moment the chip streams one contiguous
     // region of the input (measured faster here than an XCD-aware order; the
@@ -177,10 +199,10 @@ __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, 
     const int strip_raw = static_cast<int>(blockIdx.x) * spb + sl;
     const bool valid = sl < spb && strip_raw < strips;
     const int strip = min(strip_raw, strips - 1);
-    const int band = strip % bands;
-    const int plane = strip / bands;
-    const int c = plane % C;
-    const int n = plane / C;
+    const int plane = fast_div(strip, fd_bands);
+    const int band = strip - plane * bands;
+    const int n = fast_div(plane, fd_c);
+    const int c = plane - n * C;
     const long long plane_off = static_cast<long long>(c) * H * W;
     const T* xp = x + n * x_img + plane_off;
     T* yp = y + n * y_img + plane_off;
@@ -332,7 +354,8 @@ cfwd_status launch_dw(const Prob& p, const void* x, const void* w, void* y, hipS
     const unsigned blocks = static_cast<unsigned>((strips + spb - 1) / spb);
     depthwise3x3_s1<T, RB, NW><<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const T*>(w),
                                                      static_cast<T*>(y), p.c, p.h, p.w, p.x_img, p.y_img, cols,
-                                                     bands, static_cast<int>(strips));
+                                                     bands, static_cast<int>(strips), spb, make_fastdiv(cols),
+                                                     make_fastdiv(bands), make_fastdiv(p.c));
     return check_hip(hipGetLastError(), "depthwise3x3_s1 launch");
 }
 
