@@ -215,7 +215,7 @@ template <> __device__ __forceinline__ void store_out<bf16_t>(bf16_t* y, long lo
 }
 template <> __device__ __forceinline__ void store_out<int8_t>(int8_t* y, long long off, i32x4 acc, int v,
                                                               float scale) {
-    y[off] = requant_i8(acc[v], scale);
+    y[off] = static_cast<int8_t>(requant_i8_bits(acc[v], scale));
 }
 
 // Four consecutive output pixels of one channel (NCHW, 4-aligned).
@@ -230,10 +230,9 @@ template <> __device__ __forceinline__ void store_out4<bf16_t>(bf16_t* y, long l
     *reinterpret_cast<uint2*>(y + off) = make_uint2(lo, hi);
 }
 template <> __device__ __forceinline__ void store_out4<int8_t>(int8_t* y, long long off, i32x4 acc, float scale) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v |= static_cast<uint32_t>(static_cast<uint8_t>(requant_i8(acc[i], scale))) << (8 * i);
-    *reinterpret_cast<uint32_t*>(y + off) = v;
+    *reinterpret_cast<uint32_t*>(y + off) =
+        pack_low_bytes(requant_i8_bits(acc[0], scale), requant_i8_bits(acc[1], scale), requant_i8_bits(acc[2], scale),
+                       requant_i8_bits(acc[3], scale));
 }
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
@@ -830,7 +829,8 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 const int kk = (wn * FN + nf) * FR + lrow;  // channel within the tile
                 const int k = kt0 + kk;
                 const bool kval = kt * NT + kk < a.Kg;
-                const float sc = kval ? a.scale[k] : 0.0f;
+                const float sc0 = a.scale[kval ? k : 0];  // no branch around the load
+                const float sc = kval ? sc0 : 0.0f;
                 uint8_t* lrow_base = lds + (kk >> 2) * pitch + (kk & 3);
 #pragma unroll
                 for (int f = 0; f < FM; ++f)
@@ -840,7 +840,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                         if (p0 < tile_pix) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
-                                lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(requant_i8(acc[f][nf][grp * 4 + v], sc));
+                                lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(requant_i8_bits(acc[f][nf][grp * 4 + v], sc));
                         }
                     }
             }
