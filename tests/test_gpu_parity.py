@@ -67,6 +67,13 @@ SMALL = [
     # 3x3 with no vertical and one column of horizontal padding (Winograd
     # tile blocks with different row and column offsets)
     ("asym_pad_3x3", 2, 24, 12, 16, 40, 3, 3, 1, (0, 1), 1, 1),
+    # few input channels, K = 37: a second k block whose last NCHW4 word holds
+    # one real channel (staged gather form: padding channels must be zero)
+    ("stem_k37_s2", 2, 3, 32, 32, 37, 3, 3, 2, 1, 1, 1),
+    ("c4_k37_s1", 1, 4, 16, 16, 37, 3, 3, 1, 1, 1, 1),
+    # depthwise with 96 channels and 20 rows: strip, band and channel indices
+    # through divisions by 96 and by the band count
+    ("dw_c96", 3, 96, 20, 32, 96, 3, 3, 1, 1, 1, 96),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
