@@ -15,6 +15,10 @@
 //   * a per-workgroup LDS table maps u to (row delta, column delta, channel
 //     offset); each lane adds its own pixel's origin, tests the bounds (zero
 //     padding) and loads with a clamped, always-valid address -- no branches;
+//   * staged variants first copy the input rows their pixels read into LDS,
+//     zero-padded around the image, and keep only each unit's byte offset
+//     from a pixel's base there: every gather is then one unconditional LDS
+//     load;
 //   * gathers of the next step are in flight while the current one is on the
 //     matrix cores (two-deep pipeline, last pair peeled);
 //   * the epilogue writes D[k][pixel] in the caller's layout; for int8 NCHW4
@@ -162,7 +166,6 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
     const long long pg = static_cast<long long>(blockIdx.x) / a.ngk;
     const int wpix = (4 / a.KW) * NCB * 32;  // pixels of this workgroup (all in one image when STG)
 
-    // reduction unit -> (row delta, column delta, channel offset)
     const int RS = a.R * a.S;
     const int ntab = a.nss * L::SSU;
     if constexpr (STG) {
@@ -186,6 +189,8 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
             toff[i] = off * static_cast<int>(sizeof(G));
         }
     }
+    // gathers from global memory: reduction unit -> (row delta, column
+    // delta, channel offset)
     for (int u = tid; u < (STG ? 0 : ntab); u += 256) {
         Tap t;
         t.dr = -(1 << 28);  // padding unit: always out of range -> 0
