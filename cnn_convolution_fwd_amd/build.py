@@ -38,6 +38,15 @@ COMMON = [
 ]
 
 
+# Per-source extra flags.  The gather-form stem kernels are bound by vector
+# ALU issue; keeping MFMA results in ordinary VGPRs instead of accumulation
+# registers removes the register moves around their epilogues (about a tenth
+# of their vector instructions) without raising register use.
+EXTRA = {
+    "k_lowc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(SRC_DIR, f) for f in os.listdir(SRC_DIR)
                   if f.endswith((".hip", ".cpp")))
@@ -45,7 +54,7 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
