@@ -233,13 +233,22 @@ def conv2d_int8_points(*a, **k):
 
 
 def normalised_error(y_hat, y, den):
-    """max_i |y_hat_i - y_i| / den_i; where den_i == 0, y_hat_i must be exactly 0.
+    """Pass/fail metric of the float parity tests: max_i |y_hat_i - y_i| / den_i.
 
-    Returns +inf when an output with den == 0 is not exactly zero.
+    ``den_i`` is the sum of |x * w| over output i's terms (as returned by
+    ``conv2d``).  Each output's deviation is divided by its own ``den_i``.
+    Outputs with ``den_i == 0`` have only zero terms, so the exact result is 0:
+    they are left out of the maximum and must be exactly zero, else the error
+    is +inf.  Any NaN or infinity in ``y_hat`` also gives +inf.  With every
+    ``den_i == 0`` (and ``y_hat`` all zero) the error is 0.
     """
     y_hat = np.asarray(y_hat, dtype=np.float64)
     y = np.asarray(y, dtype=np.float64)
     den = np.asarray(den, dtype=np.float64)
+    if y_hat.shape != y.shape or y.shape != den.shape:
+        raise ValueError("shapes differ: %s, %s, %s" % (y_hat.shape, y.shape, den.shape))
+    if not np.all(np.isfinite(y_hat)):
+        return float("inf")
     zero = den == 0
     if np.any(y_hat[zero] != 0):
         return float("inf")
