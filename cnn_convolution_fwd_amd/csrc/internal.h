@@ -96,6 +96,10 @@ cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const v
 // Writes 0 to the NCHWX output channels past K (no-op unless K % xb != 0).
 cfwd_status zero_output_channel_padding(const Prob& p, void* y, hipStream_t st);
 
+// Overwrites `bytes` of buf (16-byte aligned) with plain stores, so that the
+// caches no longer hold what earlier launches touched (k_util.hip).
+cfwd_status evict_caches(void* buf, size_t bytes, unsigned salt, hipStream_t st);
+
 // Fast-Run accuracy gate helpers (k_util.hip).
 cfwd_status abs_copy(const Prob& p, const void* src, void* dst, long long count, hipStream_t st);
 // stats[0] = bit pattern of max |cand - ref| / den (float dtypes), stats[1] =

@@ -35,13 +35,19 @@ __global__ __launch_bounds__(256) void gate_float(const T* __restrict__ cand, co
         const float c = Elem<T>::to_f(cand[i]);
         const float r = Elem<T>::to_f(ref[i]);
         const float d = Elem<T>::to_f(den[i]);
-        if (!(c == c)) {
-            ++bad;
-        } else if (d == 0.0f) {
-            if (c != 0.0f) ++bad;
+        if (!(fabsf(c) <= 3.402823466e38f)) {
+            ++bad;  // NaN or infinity
+        } else if (!(d > 0.0f)) {
+            // den is a sum of absolute values: 0 means every term is zero, so
+            // the output must be exactly 0.  Anything else (negative, NaN) is
+            // not a valid normaliser and fails rather than passing silently.
+            if (c != 0.0f || d != 0.0f) ++bad;
         } else {
             const float e = fabsf(c - r) / d;
-            worst = max(worst, __float_as_uint(e));  // non-negative floats order as unsigned ints
+            if (!(e <= 3.402823466e38f))
+                ++bad;
+            else
+                worst = max(worst, __float_as_uint(e));  // non-negative floats order as unsigned ints
         }
     }
     for (int off = 32; off > 0; off >>= 1) {
@@ -63,6 +69,15 @@ __global__ __launch_bounds__(256) void gate_i8(const int8_t* __restrict__ cand, 
     if ((threadIdx.x & 63) == 0) atomicAdd(stats + 1, bad);
 }
 
+// Plain (cache-allocating) 16-byte stores over the whole buffer: afterwards
+// the Infinity Cache and every L2 hold this buffer's lines, not the ones a
+// previous run left behind.
+__global__ __launch_bounds__(256) void evict_kernel(uint4* __restrict__ buf, long long n16, unsigned salt) {
+    const uint4 v = make_uint4(salt, salt, salt, salt);
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n16; i += static_cast<long long>(gridDim.x) * 256)
+        buf[i] = v;
+}
+
 unsigned blocks_for(long long n) {
     long long b = (n + 255) / 256;
     return static_cast<unsigned>(b > 8192 ? 8192 : (b < 1 ? 1 : b));
@@ -80,6 +95,13 @@ cfwd_status abs_copy(const Prob& p, const void* src, void* dst, long long count,
     else
         return set_error(CFWD_ERR_UNSUPPORTED, "abs_copy: float dtypes only");
     return check_hip(hipGetLastError(), "abs_kernel launch");
+}
+
+cfwd_status evict_caches(void* buf, size_t bytes, unsigned salt, hipStream_t st) {
+    const long long n16 = static_cast<long long>(bytes / 16);
+    if (n16 == 0) return CFWD_OK;
+    evict_kernel<<<4096, 256, 0, st>>>(static_cast<uint4*>(buf), n16, salt);
+    return check_hip(hipGetLastError(), "evict_kernel launch");
 }
 
 cfwd_status gate_compare(const Prob& p, const void* cand, const void* ref, const void* den, unsigned* stats,

@@ -152,19 +152,22 @@ cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc *desc, cfwd_algo algo, const vo
 
 /* Fast-Run selection phase (MegEngine inference article, section "Fast-Run"):
  * time every candidate of cfwd_list_candidates on this device with these
- * buffers (median of >= 5 runs after 2 warm-ups), reject any whose output
- * fails the accuracy gate against the IMPLICIT_GEMM or DIRECT result on the
- * same data (bit-identical for int8; normalised error <= 1e-5 fp32 direct
- * families, 1e-3 fp32 Winograd, 1e-2 bf16), keep the fastest (times within 1%
- * count as equal and the earlier candidate wins), record it in the map and
- * return it in *best.  Synchronises `stream`; overwrites y.  workspace must
- * hold cfwd_fastrun_workspace_size bytes. */
+ * buffers (median of 7 runs after 2 warm-ups; before each run the Infinity
+ * Cache and L2 are flushed by overwriting a 512 MiB region of the workspace
+ * unless x and y together already exceed that, so candidates are timed from
+ * HBM), reject any whose output fails the accuracy gate against the generic
+ * DIRECT kernel's result on the same data (bit-identical for int8;
+ * normalised error <= 1e-5 fp32 except Winograd F(6x6), 1e-3 fp32 F(6x6),
+ * 1e-2 bf16; NaN or infinity fails), keep the fastest (times within 1% count
+ * as equal and the earlier candidate wins), record it in the map and return
+ * it in *best.  Synchronises `stream`; overwrites y.  workspace must hold
+ * cfwd_fastrun_workspace_size bytes. */
 cfwd_status cfwd_fastrun_select(const cfwd_conv_desc *desc, const void *x, const void *w_kcrs,
                                 const float *requant_scale, void *y, void *workspace,
                                 size_t ws_bytes, void *stream, cfwd_algo *best);
 
-/* Workspace for cfwd_fastrun_select: the largest candidate workspace plus a
- * reference output copy. */
+/* Workspace for cfwd_fastrun_select: the largest candidate workspace, the
+ * reference output and error normaliser, and the cache-flush region. */
 cfwd_status cfwd_fastrun_workspace_size(const cfwd_conv_desc *desc, size_t *bytes);
 
 /* Fast-Run execution-phase map (host memory, process-wide, thread-safe).
