@@ -327,17 +327,89 @@ def conv2d_fwd(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", c
 
 
 def fastrun_select(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", channels=None,
-                   requant_scale=None, out=None) -> Tuple[Algo, object]:
-    """Run the Fast-Run selection for this problem; returns (best algo, output)."""
+                   requant_scale=None, out=None, workspace=None) -> Tuple[Algo, object]:
+    """Run the Fast-Run selection for this problem; returns (best algo, output).
+
+    ``workspace`` (uint8 device tensor of at least ``fastrun_workspace_size``
+    bytes) is allocated here when not given.
+    """
     torch = _torch()
-    _check_dev(x, w, requant_scale, out)
+    _check_dev(x, w, requant_scale, out, workspace)
     desc = desc_for(x, w, stride, padding, dilation, groups, layout, channels)
     if out is None:
         out = torch.empty(_out_shape(desc), dtype=x.dtype, device=x.device)
     nbytes = fastrun_workspace_size(desc)
-    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=x.device)
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
     best = Algo()
     _check(_lib().cfwd_fastrun_select(ctypes.byref(desc), x.data_ptr(), w.data_ptr(),
                                       requant_scale.data_ptr() if requant_scale is not None else None,
-                                      out.data_ptr(), ws.data_ptr(), nbytes, _stream(), ctypes.byref(best)))
+                                      out.data_ptr(), workspace.data_ptr(), nbytes, _stream(),
+                                      ctypes.byref(best)))
     return best, out
+
+
+class LayerPlan:
+    """One conv layer set up the way an inference step runs it.
+
+    ``algo="auto"``: the Fast-Run selection phase runs once on (x, w) and
+    records its choice in the map; launches then pass AUTO, so the library
+    dispatches from the map (execution phase).  Otherwise the named family
+    (and config, "family/cfg") is resolved once and passed explicitly.  The
+    filter is prepared once (constant weights) and the algorithm's scratch is
+    allocated once; ``prepare_ms`` is the prepare step's device time.
+    """
+
+    def __init__(self, x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", channels=None,
+                 requant_scale=None, algo_spec="auto"):
+        torch = _torch()
+        _check_dev(x, w, requant_scale)
+        self.w, self.scale = w, requant_scale
+        self.desc = desc_for(x, w, stride, padding, dilation, groups, layout, channels)
+        self.out_shape = _out_shape(self.desc)
+        self.dtype, self.device = x.dtype, x.device
+        if algo_spec == "auto":
+            best, _ = fastrun_select(x, w, stride, padding, dilation, groups, layout, channels,
+                                     requant_scale=requant_scale)
+            self.chosen = resolve_algo(self.desc, algo())
+            if self.chosen.key() != best.key():
+                raise RuntimeError("AUTO resolves to %s, Fast-Run chose %s" % (algo_name(self.chosen),
+                                                                               algo_name(best)))
+            self.chosen.median_ms = best.median_ms
+            self.algo_arg = algo()
+        else:
+            fam, _, cid = algo_spec.partition("/")
+            self.chosen = resolve_algo(self.desc, algo(fam, int(cid) if cid else -1))
+            self.algo_arg = self.chosen
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        self.wp = prepare_filter(w, self.desc, self.chosen)
+        e1.record()
+        torch.cuda.synchronize()
+        self.prepare_ms = e0.elapsed_time(e1) if self.wp is not None else 0.0
+        self.scratch_bytes = scratch_size(self.desc, self.chosen)
+        self.scratch = torch.empty(max(self.scratch_bytes, 16), dtype=torch.uint8, device=x.device)
+
+    @property
+    def name(self) -> str:
+        return algo_name(self.chosen)
+
+    def new_output(self):
+        return _torch().empty(self.out_shape, dtype=self.dtype, device=self.device)
+
+    def launch_raw(self, x_ptr: int, y_ptr: int, stream: int) -> int:
+        """Enqueue the layer on ``stream`` with raw device pointers; returns the status."""
+        return conv2d_fwd_raw(self.desc, self.algo_arg, x_ptr, self.w.data_ptr(),
+                              self.wp.data_ptr() if self.wp is not None else 0,
+                              self.scale.data_ptr() if self.scale is not None else 0, y_ptr,
+                              self.scratch.data_ptr() if self.scratch_bytes else 0, self.scratch_bytes, stream)
+
+    def __call__(self, x, out=None):
+        """y = conv(x) on the current stream (x shaped and typed like the set-up input)."""
+        _check_dev(x, out)
+        if out is None:
+            out = self.new_output()
+        _check(self.launch_raw(x.data_ptr(), out.data_ptr(), _stream()))
+        return out

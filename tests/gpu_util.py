@@ -1,7 +1,11 @@
 """Helpers shared by the GPU parity tests: move seeded numpy problems to the
 device, run the HIP library through its C ABI, and bring results back."""
+import functools
+
 import numpy as np
 import pytest
+
+import oracle
 
 from cnn_convolution_fwd_amd import binding as B
 from cnn_convolution_fwd_amd.workloads import bf16_bits, bf16_to_f32, pack_nchwx, unpack_nchwx
@@ -67,3 +71,33 @@ def candidates_for(shape, dtype, stride=1, padding=0, dilation=1, groups=1, layo
     N, C, H, W, K, R, S = shape
     d = B.make_desc(N, C, H, W, K, R, S, stride, padding, dilation, groups, layout, xb, dtype)
     return [(B.algo_name(a).split("/")[0], a.config_id) for a in B.list_candidates(d)]
+
+
+def output_to_host(y, dtype, layout, K):
+    """Device output -> logical-NCHW numpy; NCHWX channels past K must be 0."""
+    out = from_device(y, dtype)
+    if layout == "NCHWX":
+        full = out.transpose(0, 1, 4, 2, 3).reshape(out.shape[0], -1, out.shape[2], out.shape[3])
+        assert np.all(full[:, K:] == 0), "padded output channels are not zero"
+        out = unpack_nchwx(out, K)
+    return out
+
+
+@functools.lru_cache(maxsize=4)
+def float_reference(config, layer_idx, n, dtype):
+    """(problem, y, den) of a float workload layer at batch n: the whole tensor from the oracle."""
+    from cnn_convolution_fwd_amd.workloads import float_problem
+    pr = float_problem(config, layer_idx, n=n, dtype=dtype)
+    L = pr.layer
+    y, den = oracle.conv2d(pr.x, pr.w, L.stride, L.pad, L.dil, L.groups)
+    return pr, y, den
+
+
+@functools.lru_cache(maxsize=4)
+def int8_reference(config, layer_idx, n):
+    """(problem, y) of an int8 workload layer at batch n: the whole tensor from the oracle."""
+    from cnn_convolution_fwd_amd.workloads import int8_problem
+    pr = int8_problem(config, layer_idx, n=n)
+    L = pr.layer
+    y, _ = oracle.conv2d_int8_requant(pr.x, pr.w, pr.scale, L.stride, L.pad, L.dil, L.groups)
+    return pr, y

@@ -8,7 +8,7 @@ Blog "卷积总结": the naive conv of its example layer runs ~85.16 M inner
 iterations, ~170 MFLOP.  MegEngine inference article, section "Winograd":
 F(2x2,3x3) and F(6x6,3x3) cut multiplies 2.25x and 5.06x.
 """
-from cnn_convolution_fwd_amd.roofline import bound, conv_bytes, conv_flops, gemm_flops_bytes
+from cnn_convolution_fwd_amd.roofline import bound, conv_bytes, conv_flops, gemm_flops_bytes, winograd_flops
 from cnn_convolution_fwd_amd.workloads import CONFIGS, resnet18_layers
 
 
@@ -60,3 +60,18 @@ def test_resnet18_int8_totals():
     macs = sum(conv_flops(1, L.c, L.h, L.w, L.k, L.r, L.s, L.stride, L.pad) for L in resnet18_layers()) // 2
     assert round(macs / 1e9, 4) == 1.8136
     assert len(resnet18_layers()) == 20
+
+
+def test_winograd_product_counts():
+    # F(2x2,3x3): 16 products per 2x2 tile instead of 36 -> 2.25x on a 56x56 map
+    d = conv_flops(1, 1, 56, 56, 1, 3, 3, 1, 1)
+    assert winograd_flops(1, 1, 56, 56, 1, 2) == 2 * 16 * 28 * 28
+    assert d / winograd_flops(1, 1, 56, 56, 1, 2) == 2.25
+    # F(6x6,3x3): 64 instead of 324 per tile (5.0625x), but 56 is not a
+    # multiple of 6: ceil(56/6)^2 = 100 tiles cover 60x60 outputs -> 4.41x
+    assert winograd_flops(1, 1, 56, 56, 1, 6) == 2 * 64 * 100
+    assert abs(d / winograd_flops(1, 1, 56, 56, 1, 6) - 4.41) < 0.01
+    assert conv_flops(1, 1, 60, 60, 1, 3, 3, 1, 1) / winograd_flops(1, 1, 60, 60, 1, 6) == 324 / 64
+    # the headline layer: 52.6 GFLOP (F(2x2)) and 26.8 GFLOP (F(6x6)) at N=32, C=K=256
+    assert round(winograd_flops(32, 256, 56, 56, 256, 2) / 1e9, 1) == 52.6
+    assert round(winograd_flops(32, 256, 56, 56, 256, 6) / 1e9, 1) == 26.8
