@@ -21,9 +21,13 @@ clock the GPU holds under sustained load rather than one still ramping up
 from idle (this matters for a fixed ``--algo``, where no Fast-Run search has
 run first).
 
-Prints ONE JSON line: whole-step throughput, the roofline of the dominant
-kernel (HIP events around every launch, on the stream the kernel runs on),
-and the CPU oracle timed on a bounded sample of the same workload.
+Prints ONE JSON line: whole-step throughput (direct-equivalent FLOPs), the
+roofline of the dominant kernel (HIP events around every launch, on the
+stream the kernel runs on; FLOPs its algorithm performs, so Winograd is held
+to its own element-wise products), the filter prepare time (once per layer,
+outside the step), the shader clock and board power sampled while the same
+steps run, and the CPU oracle timed on a bounded sample of the same workload
+(threads used, host CPU model).
 
     python bench.py [--workload NAME] [--n N] [--dtype bf16|f32|i8] [--algo auto|family[/cfg]]
                     [--steps K] [--warmup W]
@@ -77,6 +81,8 @@ def parse():
     ap.add_argument("--algo", default="auto", help="auto (Fast-Run) or family[/config], e.g. implicit_gemm/7")
     ap.add_argument("--settle", type=float, default=0.3, help="seconds of untimed launches before the warm-up steps")
     ap.add_argument("--sets", type=int, default=0, help="rotated buffer sets (0: enough for > 512 MB)")
+    ap.add_argument("--telemetry-window", type=float, default=0.3,
+                    help="seconds of further untimed steps while clock and power are sampled")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle CPU work at most")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -155,7 +161,8 @@ def main():
         return
 
     from cnn_convolution_fwd_amd import binding as B
-    from cnn_convolution_fwd_amd.roofline import PEAK, bound, layer_bytes, layer_flops
+    from cnn_convolution_fwd_amd import telemetry
+    from cnn_convolution_fwd_amd.roofline import PEAK, bound, layer_algo_flops, layer_bytes, layer_flops
     from cnn_convolution_fwd_amd.workloads import CONFIGS, bf16_bits, float_problem, int8_problem, pack_nchwx
 
     base = ALIASES.get(a.workload, a.workload)
@@ -181,7 +188,8 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(arr, np.int8)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
 
-    # ---- per-layer set-up: inputs, algorithm (Fast-Run), prepared filter, scratch
+    # ---- per-layer set-up: inputs, algorithm (Fast-Run), prepared filter, scratch.
+    # LayerPlan is the same sequence of library calls the parity tests run.
     layers = []
     for li in layer_ids:
         L = cfg.layers[li]
@@ -194,23 +202,9 @@ def main():
             x0 = to_dev(pr.x)
             scale = None
         w = to_dev(pr.w)
-        desc = B.desc_for(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c)
-        y0 = torch.empty(B._out_shape(desc), dtype=x0.dtype, device=dev)
-        if a.algo == "auto":
-            best, _ = B.fastrun_select(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c,
-                                       requant_scale=scale, out=y0)
-            chosen = B.resolve_algo(desc, B.algo())
-            assert chosen.key() == best.key()
-            algo_arg = B.algo()  # AUTO: dispatch from the Fast-Run map
-        else:
-            fam, _, cid = a.algo.partition("/")
-            chosen = B.resolve_algo(desc, B.algo(fam, int(cid) if cid else -1))
-            algo_arg = chosen
-        wp = B.prepare_filter(w, desc, chosen)
-        sbytes = B.scratch_size(desc, chosen)
-        layers.append(dict(L=L, pr=pr, x0=x0, y0=y0, w=w, scale=scale, desc=desc, chosen=chosen,
-                           algo_arg=algo_arg, wp=wp, sbytes=sbytes,
-                           scratch=torch.empty(max(sbytes, 1), dtype=torch.uint8, device=dev)))
+        plan = B.LayerPlan(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c, requant_scale=scale,
+                           algo_spec=a.algo)
+        layers.append(dict(L=L, pr=pr, x0=x0, y0=plan.new_output(), plan=plan))
 
     # every layer rotates over its own buffer sets, > 512 MB per layer, so a
     # layer timed alone (per-kernel figures) cannot read from the cache either
@@ -225,14 +219,11 @@ def main():
 
     def launch(l, i):
         ns = l["nsets"]
-        st = B.conv2d_fwd_raw(l["desc"], l["algo_arg"], l["xs"][i % ns].data_ptr(), l["w"].data_ptr(),
-                              l["wp"].data_ptr() if l["wp"] is not None else 0,
-                              l["scale"].data_ptr() if l["scale"] is not None else 0,
-                              l["ys"][i % ns].data_ptr(), l["scratch"].data_ptr() if l["sbytes"] else 0,
-                              l["sbytes"], sptr)
+        st = l["plan"].launch_raw(l["xs"][i % ns].data_ptr(), l["ys"][i % ns].data_ptr(), sptr)
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
 
+    sampler = telemetry.Sampler(torch.cuda.current_device()).start()
     t_end = time.perf_counter() + a.settle
     i = 0
     while time.perf_counter() < t_end:
@@ -268,6 +259,18 @@ def main():
     else:
         layer_avg = [timed(lambda i, l=l: launch(l, i), a.steps) for l in layers]
 
+    # clock and power under the same load: keep launching whole steps for a
+    # while after the timed region, so the sampler sees a sustained window
+    t_end = time.perf_counter() + a.telemetry_window
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(8):
+            for l in layers:
+                launch(l, i)
+            i += 1
+        torch.cuda.synchronize()
+    gpu_telemetry = sampler.stop()
+
     # warm (same buffers every step) secondary figure
     for _ in range(3):
         for l in layers:
@@ -280,16 +283,19 @@ def main():
     per_layer = []
     for l, t in zip(layers, layer_avg):
         L = l["L"]
-        fl = layer_flops(L, N)
+        name = l["plan"].name
+        fl = layer_flops(L, N)               # direct-equivalent (the metric)
+        afl = layer_algo_flops(L, N, name)   # what the chosen algorithm performs
         by = layer_bytes(L, N, dtype)
-        kind, _ = bound(fl, by, peak_key)
+        kind, _ = bound(afl, by, peak_key)
         total_flops += fl
         if kind == "hbm":
             ach, pk, u = by / (t * 1e-3) / 1e9, PEAK["hbm_bytes_per_s"] / 1e9, "GB/s"
         else:
-            ach, pk, u = fl / (t * 1e-3) / 1e12, PEAK[peak_key] / 1e12, unit
-        per_layer.append(dict(name=L.name, algo=B.algo_name(l["chosen"]), ms=round(t, 5), bound=kind,
-                              achieved=round(ach, 2), peak=pk, unit=u, frac=round(ach / pk, 4), flops=fl, bytes=by))
+            ach, pk, u = afl / (t * 1e-3) / 1e12, PEAK[peak_key] / 1e12, unit
+        per_layer.append(dict(name=L.name, algo=name, ms=round(t, 5), bound=kind, achieved=round(ach, 2), peak=pk,
+                              unit=u, frac=round(ach / pk, 4), flops=fl, algo_flops=afl, bytes=by,
+                              prepare_ms=round(l["plan"].prepare_ms, 5)))
     dom = max(range(nl), key=lambda j: layer_avg[j])
     d = per_layer[dom]
     value = total_flops / (ms_per_step * 1e-3) / 1e12
@@ -314,7 +320,9 @@ def main():
             "gflop_per_step": round(total_flops / 1e9, 3),
             "mb_per_step": round(sum(p["bytes"] for p in per_layer) / 1e6, 2),
             "warm_ms_per_step": round(warm_ms, 5),
+            "filter_prepare_ms": round(sum(p["prepare_ms"] for p in per_layer), 5),
         },
+        "gpu_telemetry": gpu_telemetry,
         "roofline": {
             "bound": d["bound"],
             "achieved": d["achieved"],
@@ -325,11 +333,12 @@ def main():
             "kernel": "%s (%s)" % (d["name"], d["algo"]),
             "kernel_avg_ms": d["ms"],
             "algorithmic_bytes": d["bytes"],
-            "algorithmic_flops": d["flops"],
+            "algorithmic_flops": d["algo_flops"],
+            "direct_equivalent_flops": d["flops"],
         },
     }
     if nl > 1:
-        out["layers"] = [{k: p[k] for k in ("name", "algo", "ms", "bound", "achieved", "unit", "frac")}
+        out["layers"] = [{k: p[k] for k in ("name", "algo", "ms", "bound", "achieved", "unit", "frac", "prepare_ms")}
                          for p in per_layer]
 
     if not a.no_cpu:
@@ -357,6 +366,8 @@ def main():
             "value": round(sflops / t1 / 1e12, 6),
             "unit": unit,
             "cores": oracle.max_threads(),
+            "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu_model": telemetry.cpu_model(),
             "kind": "oracle",
             "sample": "%d of %d images through %d layer(s) (%.2f G%s, %s loop nest, %.1f s)" % (
                 nimg, N, nl, sflops / 1e9, "OP" if int8 else "FLOP", "int64" if int8 else "fp64", t1),

@@ -67,13 +67,36 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(jobs: int = 0, verbose: bool = False) -> str:
-    """Compile every source and link libcfwd.so; returns the library path."""
+def _stale(src: str) -> bool:
+    """True when src's object is missing or older than src or any header."""
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    headers = [os.path.join(SRC_DIR, f) for f in os.listdir(SRC_DIR) if f.endswith(".h")]
+    headers.append(os.path.join(INCLUDE, "cfwd.h"))
+    return any(os.path.getmtime(f) > t for f in [src, *headers, os.path.abspath(__file__)])
+
+
+def build(jobs: int = 0, verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source (only stale ones when ``incremental``) and link
+    libcfwd.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
+    if incremental:
+        stale = [s for s in srcs if _stale(s)]
+        if stale:
+            with cf.ThreadPoolExecutor(max_workers=jobs or min(len(stale), 16)) as ex:
+                list(ex.map(lambda s: _compile(s, verbose), stale))
+        objs = [os.path.join(BUILD_DIR, os.path.basename(s) + ".o") for s in srcs]
+        return _link(objs, verbose)
     jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    return _link(objs, verbose)
+
+
+def _link(objs, verbose: bool) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -89,8 +112,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--incremental", action="store_true", help="recompile only sources newer than their objects")
     a = ap.parse_args(argv)
-    print(build(a.jobs, a.verbose))
+    print(build(a.jobs, a.verbose, a.incremental))
 
 
 if __name__ == "__main__":

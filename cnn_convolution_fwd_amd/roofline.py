@@ -6,7 +6,9 @@ counts as 2 FLOPs; the memory traffic of a layer is the size of all its
 inputs, its parameters and its outputs, each counted once (caches ignored);
 arithmetic intensity = FLOPs / bytes; a kernel is bound by compute when its
 intensity exceeds the ridge point peak_flops / bandwidth, else by memory.
-Winograd layers are credited with the FLOPs of direct convolution.
+Throughput is quoted in direct-equivalent FLOPs for every algorithm (Winograd
+layers are credited with the FLOPs of direct convolution); a kernel's roofline
+fraction uses the FLOPs its algorithm performs (``layer_algo_flops``).
 
 Peaks are AMD's published MI355X figures (dense, no sparsity).
 """
@@ -43,6 +45,28 @@ def layer_flops(L, n) -> int:
 
 def layer_bytes(L, n, dtype) -> int:
     return conv_bytes(n, L.c, L.h, L.w, L.k, L.r, L.s, L.stride, L.pad, L.dil, L.groups, ESIZE[dtype])
+
+
+def winograd_flops(n, c, h, w, k, m, pad=1, groups=1) -> int:
+    """FLOPs of Winograd F(m x m, 3 x 3)'s element-wise products, the part the
+    matrix cores execute: every output tile of m x m (edge tiles included,
+    cropped afterwards) takes alpha^2 = (m + 2)^2 products per (input channel,
+    output channel) pair, 2 FLOPs each (MegEngine inference article, section
+    "Winograd": 16 instead of 36 multiplies for F(2x2,3x3))."""
+    oh, ow = out_hw(h, w, 3, 3, 1, pad, 1)
+    tiles = n * (-(-oh // m)) * (-(-ow // m))
+    return 2 * (m + 2) ** 2 * tiles * k * (c // groups)
+
+
+def layer_algo_flops(L, n, algo_name: str) -> int:
+    """FLOPs the named algorithm performs for the layer: Winograd's
+    element-wise products for the Winograd families, the direct count for
+    every other family (implicit GEMM, direct, pointwise perform exactly it)."""
+    if algo_name.startswith("winograd_f2x2"):
+        return winograd_flops(n, L.c, L.h, L.w, L.k, 2, L.pad, L.groups)
+    if algo_name.startswith("winograd_f6x6"):
+        return winograd_flops(n, L.c, L.h, L.w, L.k, 6, L.pad, L.groups)
+    return layer_flops(L, n)
 
 
 def gemm_flops_bytes(m, n, k, esize=4):
