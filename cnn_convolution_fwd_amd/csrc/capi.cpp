@@ -197,6 +197,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Device scratch an algorithm needs besides its prepared filter.
 size_t scratch_bytes(const Prob& p, const cfwd_algo& a) {
     switch (a.kind) {
+        case CFWD_ALGO_IMPLICIT_GEMM: return igemm_scratch_bytes(p, a.config_id);
         case CFWD_ALGO_WINOGRAD_F2X2_3X3: return winograd_scratch_bytes(p, 2, a.config_id);
         case CFWD_ALGO_WINOGRAD_F6X6_3X3: return winograd_scratch_bytes(p, 6, a.config_id);
         default: return 0;
@@ -354,7 +355,7 @@ cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w,
                 const float* scale, void* y, void* scratch, hipStream_t st) {
     cfwd_status s;
     switch (a.kind) {
-        case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, st); break;
+        case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, scratch, st); break;
         case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, st); break;
         case CFWD_ALGO_DIRECT: s = direct_launch(p, a.config_id, x, w, scale, y, st); break;
         case CFWD_ALGO_WINOGRAD_F2X2_3X3: s = winograd_launch(p, 2, a.config_id, x, wp, scratch, y, st); break;

@@ -51,6 +51,11 @@ struct Args {
     int TN, TH, TW, PH, PW, npix;  // output tile and its input patch
     int tiles_w, tiles_h, tiles_n;
     int nchunks, ntk;              // channel chunks, output-channel tiles
+    // split reduction (SPLIT kernels only): workgroup split s of a tile sums
+    // channel chunks [s*cps, min((s+1)*cps, nchunks)) and writes its int32
+    // partial tile to part + s * N * y_img, in the output's NCHW4 order
+    int cps;
+    int32_t* part;
 };
 
 template <typename T> struct Mma;
@@ -312,7 +317,7 @@ template <typename T> struct Frag<T, 32> {
     static constexpr int NACC = 16;
 };
 
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV>
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false>
 __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
     constexpr int NT = WN * FN * FR;
@@ -341,6 +346,19 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     // XCD's L2) and consecutive pixel tiles are spatial neighbours (they share
     // halo rows).
     int lin = xcd_linear(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
+    // split reduction: the split index is outermost in the work order, so the
+    // workgroups running together on one XCD share a chunk range (and its
+    // input channels and weights)
+    int cb = 0;             // first channel chunk of this workgroup
+    int nch = a.nchunks;    // chunks it sums
+    int split = 0;
+    if constexpr (SPLIT) {
+        const int per = static_cast<int>(gridDim.x) / ((a.nchunks + a.cps - 1) / a.cps);
+        split = lin / per;
+        lin -= split * per;
+        cb = split * a.cps;
+        nch = min(a.cps, a.nchunks - cb);
+    }
     const int kt = lin % a.ntk;
     lin /= a.ntk;
     const int ntm = a.tiles_w * a.tiles_h * a.tiles_n;
@@ -430,7 +448,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
             for (int l = 0; l < PP; ++l) dst[i][l] = make_uint4(0, 0, 0, 0);
             if (u_sp[i] < 0) continue;
-            const int cl = chunk * CK + u_j[i] * E16;
+            const int cl = (chunk + cb) * CK + u_j[i] * E16;
             const int nval = a.Cg - cl;
             if (nval <= 0) continue;
             const int c0 = g * a.Cg + cl;
@@ -483,7 +501,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     auto stage_piece = [&](int chunk, int l) {
         using R = typename Raw<T>::type;
         const int i = l / PP, ld = l % PP;
-        const int cl = chunk * CK + (u_j[i] < 0 ? 0 : u_j[i]) * E16;
+        const int cl = (chunk + cb) * CK + (u_j[i] < 0 ? 0 : u_j[i]) * E16;
         const int nval = a.Cg - cl;
         const bool valid = (u_sp[i] >= 0) && (XB == 1 ? ld < nval : ld * XB < nval);
         const int c0 = g * a.Cg + cl;
@@ -518,8 +536,8 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     // of 64 bytes, laid out so that each fragment piece is 1 KB contiguous:
     // FR=16: [NT][64 B] (lane reads row lrow, slot lgrp);
     // FR=32: [NT/32][piece][32 rows][half][16 B].
-    const uint8_t* __restrict__ wtile =
-        static_cast<const uint8_t*>(a.wp) + static_cast<long long>(g * a.ntk + kt) * a.nchunks * RS * NT * 64;
+    const uint8_t* __restrict__ wtile = static_cast<const uint8_t*>(a.wp) +
+                                        (static_cast<long long>(g * a.ntk + kt) * a.nchunks + cb) * RS * NT * 64;
     const int boff = (FR == 16) ? (wn * FN * 16 + lrow) * 64 + lgrp * 16 : (wn * FN * 2 * 32 + lrow) * 32 + lgrp * 16;
     auto load_b = [&](uint4 (*b)[NP], int it) {
         const uint8_t* p = wtile + static_cast<long long>(it) * NT * 64 + boff;
@@ -564,7 +582,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         __syncthreads();
     }
 
-    const int total_it = a.nchunks * RS;
+    const int total_it = nch * RS;
     int it = 0;
     if constexpr (RSV == 9 && FR == 32) {
         // 3x3 (nine-tap) filters, 32x32 fragments, wide staging: the nine taps
@@ -620,7 +638,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
             for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(lds + abase[f] + i * PSTEP);
         int bc = 0;  // buffer of chunk c
-        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+        for (int chunk = 0; chunk < nch; ++chunk) {
             const int bnext = TB ? ((bc == 2) ? 0 : bc + 1) : (bc ^ 1);
             const int bfar = (bnext == 2) ? 0 : bnext + 1;
             const uint8_t* pb = lds + bc * patch_bytes;
@@ -642,7 +660,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 }
             }
             if constexpr (TB) {
-                if (chunk + 2 < a.nchunks) stage_store(bfar, stg);
+                if (chunk + 2 < nch) stage_store(bfar, stg);
                 __syncthreads();
             } else {
                 stage_store(bnext, stg);  // zeros past the last chunk: harmless
@@ -684,9 +702,9 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         __syncthreads();
 #pragma unroll
         for (int f = 0; f < FM; ++f) ra[f] = *reinterpret_cast<const uint4*>(lds + abase[f]);
-        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+        for (int chunk = 0; chunk < nch; ++chunk) {
             const int buf = chunk & 1;
-            const bool more = chunk + 1 < a.nchunks;
+            const bool more = chunk + 1 < nch;
             const uint8_t* pb = lds + buf * patch_bytes;
             const int itn = (chunk + 1) * 9;  // first tap of the next chunk
             if constexpr (STG == 0) {
@@ -737,9 +755,9 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
         load_b(bnxt, total_it > 1 ? 1 : 0);
         read_a(lds, 0);
         const int last_it = total_it - 1;
-        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+        for (int chunk = 0; chunk < nch; ++chunk) {
             const int buf = chunk & 1;
-            const bool more = chunk + 1 < a.nchunks;
+            const bool more = chunk + 1 < nch;
             const uint8_t* pb = lds + buf * patch_bytes;
             if (more) stage_load(chunk + 1, stg);
             int r = 0, s = 0;
@@ -786,9 +804,9 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             if (more) read_a(lds + (buf ^ 1) * patch_bytes, 0);
         }
     } else {
-        for (int chunk = 0; chunk < a.nchunks; ++chunk) {
+        for (int chunk = 0; chunk < nch; ++chunk) {
             const int buf = chunk & 1;
-            const bool more = chunk + 1 < a.nchunks;
+            const bool more = chunk + 1 < nch;
             const uint8_t* pb = lds + buf * patch_bytes;
             if (more) stage_load(chunk + 1, stg);
             int r = 0, s = 0;
@@ -807,6 +825,53 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             if (more) stage_store(buf ^ 1, stg);
             __syncthreads();
         }
+    }
+
+    // ---- split reduction: the int32 partial tile of this workgroup's chunk
+    // range goes to its split's partial buffer in the output's NCHW4 order
+    // (one pixel's four channels = 16 bytes), where the reduce kernel sums the
+    // splits and requantises (int32 addition is exact in any order, so the
+    // result is the same bit for bit).  A lane holds one channel of four pixel
+    // rows; the tile is transposed through LDS as [channel block][tile
+    // pixel][4 channels] so that each lane then stores one pixel's 16 bytes
+    // and consecutive lanes store consecutive pixels of a channel block.
+    if constexpr (SPLIT) {
+        static_assert(sizeof(T) == 1 && XB == 4, "split reduction: int8 NCHW4 only");
+        // bytes per channel block in LDS; the 64-byte pad takes the up to three
+        // rows past tile_pix of a register tile's last 4-row group
+        const int pitch = tile_pix * 16 + 64;
+        constexpr int NG = FT::NACC / 4;
+#pragma unroll
+        for (int nf = 0; nf < FN; ++nf) {
+            const int kk = (wn * FN + nf) * FR + lrow;  // channel within the tile
+            int32_t* cbase = reinterpret_cast<int32_t*>(lds + (kk >> 2) * pitch) + (kk & 3);
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int grp = 0; grp < NG; ++grp) {
+                    const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
+                    if (p0 < tile_pix) {
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) cbase[(p0 + v) * 4] = acc[f][nf][grp * 4 + v];
+                    }
+                }
+        }
+        __syncthreads();
+        const int OHW = a.OH * a.OW;
+        int32_t* pbase = a.part + static_cast<long long>(split) * a.N * a.y_img;
+        const int kb0 = kt * NT / 4;                          // first channel block of the tile
+        const int nkb4 = (min(NT, a.Kg - kt * NT) + 3) / 4;   // channel blocks it writes
+        const int nimg = min(a.TN, a.N - n0);
+        for (int q = tid; q < nkb4 * tile_pix; q += NTHR) {
+            const int kb = q / tile_pix, pp = q - (q / tile_pix) * tile_pix;
+            const int tn = pp / thw, rem = pp - (pp / thw) * thw;
+            const int ohl = rem / a.TW, owl = rem - (rem / a.TW) * a.TW;
+            const int oh = oh0 + ohl, ow = ow0 + owl;
+            if (tn >= nimg || oh >= a.OH || ow >= a.OW) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(lds + kb * pitch + pp * 16);
+            *reinterpret_cast<uint4*>(pbase + (n0 + tn) * a.y_img + ((kb0 + kb) * OHW + oh * a.OW + ow) * 4) = v;
+        }
+        return;
     }
 
     // ---- epilogue for int8 NCHW4 outputs of tiles of whole output rows (or
@@ -1092,6 +1157,25 @@ constexpr int kNumCfgs = sizeof(kCfgs) / sizeof(kCfgs[0]);
 
 constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one CU (gfx950)
 
+// Split reduction (int8 NCHW4, groups 1): the channel-chunk reduction of a
+// base tile config is divided among `splits` workgroups per tile, which
+// write int32 partial tiles; a second kernel sums them and requantises.  For
+// deep layers with few output pixels (ResNet-18's 14x14 and 7x7 stages) the
+// base tiles alone are too few to fill the 256 CUs, and each would walk the
+// whole reduction (up to 8 chunks x 9 taps) by itself.
+struct SplitCfg {
+    int base, splits;
+};
+constexpr SplitCfg kSplitCfgs[] = {
+    {10, 2}, {10, 4}, {10, 8},  // 256 px x 128 ch, 32x32 fragments
+    {9, 2},  {9, 4},  {9, 8},   // 128 px x 256 ch, 32x32 fragments
+    {11, 2}, {11, 4}, {11, 8},  // 128 px x 128 ch, 32x32 fragments
+    {13, 2}, {13, 4}, {13, 8},  // 256 px x  64 ch, 32x32 fragments
+    {2, 2},  {2, 4},  {2, 8},   // 128 px x  64 ch, 16x16 fragments
+    {16, 2}, {16, 4}, {16, 8},  // 256 px x  64 ch, 16x16 fragments, eight waves
+};
+constexpr int kNumSplitCfgs = sizeof(kSplitCfgs) / sizeof(kSplitCfgs[0]);
+
 struct Geo {
     int TN, TH, TW, PH, PW, npix, tiles_n, tiles_h, tiles_w, nchunks, ntk;
     int stg;  // 0: per-pixel gathers, 1: wide row-block loads
@@ -1205,6 +1289,46 @@ inline bool geometry(const Prob& p, const Cfg& c, Geo* g, std::string* why) {
     return tile_geometry(p, c, TN, TH, TW, g, why);
 }
 
+// Geometry of split config `sc`: the base config's tiles, the chunks per
+// split (*cps) and the LDS of the partial-tile epilogue.  Rejected when the
+// splits would not all be non-empty or distinct from a smaller split count.
+inline bool split_geometry(const Prob& p, int sc, Geo* g, int* cps, std::string* why) {
+    if (sc < 0 || sc >= kNumSplitCfgs) {
+        if (why) *why = "implicit GEMM: no such split config";
+        return false;
+    }
+    const SplitCfg s = kSplitCfgs[sc];
+    if (p.dtype != CFWD_I8 || p.layout != CFWD_LAYOUT_NCHWX || p.xb != 4 || p.g != 1) {
+        if (why) *why = "implicit GEMM split reduction: int8 NCHW4 with groups 1 only";
+        return false;
+    }
+    if (!geometry(p, kCfgs[s.base], g, why)) return false;
+    const int c = (g->nchunks + s.splits - 1) / s.splits;
+    if (g->nchunks < s.splits || (g->nchunks + c - 1) / c != s.splits) {
+        if (why) *why = "implicit GEMM split reduction: the channel chunks do not divide into that many splits";
+        return false;
+    }
+    *cps = c;
+    const size_t tile_pix = static_cast<size_t>(g->TN) * g->TH * g->TW;
+    g->lds_bytes = std::max(g->lds_bytes, static_cast<size_t>(kCfgs[s.base].nt() / 4) * (tile_pix * 16 + 64));
+    if (g->lds_bytes > kLdsBytes) {
+        if (why) *why = "implicit GEMM split reduction: the partial tile needs more LDS than a CU has";
+        return false;
+    }
+    // the reduce kernel indexes pixel-channel-blocks of all images in 32 bits
+    if (static_cast<long long>(p.n) * p.y_img / 4 >= (1LL << 31) ||
+        static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk * s.splits > 0x7fffffffLL) {
+        if (why) *why = "implicit GEMM split reduction: problem too large";
+        return false;
+    }
+    return true;
+}
+
+// Partial tiles of every split: splits x N x y_img int32.
+inline size_t split_scratch_bytes(const Prob& p, int sc) {
+    return static_cast<size_t>(kSplitCfgs[sc].splits) * p.n * static_cast<size_t>(p.y_img) * 4;
+}
+
 inline size_t filter_bytes(const Prob& p, const Cfg& c, const Geo& g) {
     return static_cast<size_t>(p.g) * g.ntk * g.nchunks * p.r * p.s * c.nt() * 64;
 }
@@ -1222,6 +1346,8 @@ inline Args make_args(const Prob& p, const Geo& g, const void* x, const void* wp
     a.TN = g.TN; a.TH = g.TH; a.TW = g.TW; a.PH = g.PH; a.PW = g.PW; a.npix = g.npix;
     a.tiles_w = g.tiles_w; a.tiles_h = g.tiles_h; a.tiles_n = g.tiles_n;
     a.nchunks = g.nchunks; a.ntk = g.ntk;
+    a.cps = g.nchunks;
+    a.part = nullptr;
     return a;
 }
 
@@ -1239,15 +1365,21 @@ template <typename K> cfwd_status allow_big_lds(K kern, size_t lds_bytes, bool* 
     return CFWD_OK;
 }
 
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV>
+// One launch of a tile config.  SPLIT: `nsplit` workgroups per tile, each
+// summing `cps` channel chunks into its partial tile in `part`.
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false>
 cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
-                       hipStream_t st) {
-    const Args a = make_args(p, g, x, wp, scale, y);
-    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV>;
+                       hipStream_t st, int cps = 0, int nsplit = 1, int32_t* part = nullptr) {
+    Args a = make_args(p, g, x, wp, scale, y);
+    if constexpr (SPLIT) {
+        a.cps = cps;
+        a.part = part;
+    }
+    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV, SPLIT>;
     static bool attr_done = false;
     const cfwd_status s = allow_big_lds(kern, g.lds_bytes, &attr_done);
     if (s != CFWD_OK) return s;
-    const dim3 grid(static_cast<unsigned>(tile_count(p, g)));
+    const dim3 grid(static_cast<unsigned>(tile_count(p, g) * (SPLIT ? nsplit : 1)));
     kern<<<grid, WM * WN * 64, g.lds_bytes, st>>>(a);
     return check_hip(hipGetLastError(), "igemm_kernel launch");
 }
@@ -1348,5 +1480,9 @@ cfwd_status igemm_launch_i8(int cfg, const Prob& p, const ig::Geo& g, const void
 cfwd_status igemm_prepare_f32(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st);
 cfwd_status igemm_prepare_bf16(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st);
 cfwd_status igemm_prepare_i8(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st);
+// Split config sc (k_igemm_i8_split.hip): the split kernel, then the reduce
+// kernel that sums the partial tiles in `part` and requantises into y.
+cfwd_status igemm_launch_i8_split(int sc, const Prob& p, const ig::Geo& g, int cps, const void* x, const void* wp,
+                                  const float* scale, void* y, void* part, hipStream_t st);
 
 }  // namespace cfwd

@@ -57,8 +57,9 @@ int igemm_num_configs();
 bool igemm_supported(const Prob& p, int cfg, std::string* why);
 size_t igemm_filter_bytes(const Prob& p, int cfg);
 cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
+size_t igemm_scratch_bytes(const Prob& p, int cfg);  // partial tiles of split configs
 cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp,
-                         const float* scale, void* y, hipStream_t st);
+                         const float* scale, void* y, void* scratch, hipStream_t st);
 int igemm_default_config(const Prob& p);
 // gather form of implicit GEMM for few input channels (implicit-GEMM configs
 // after the tiled ones)

@@ -5,28 +5,47 @@
 namespace cfwd {
 
 // Configs 0 .. kNumCfgs-1: the tiled kernel of igemm_impl.h; the next
-// lowc_num_configs(): the gather form for few input channels (k_lowc.hip).
-int igemm_num_configs() { return ig::kNumCfgs + lowc_num_configs(); }
+// lowc_num_configs(): the gather form for few input channels (k_lowc.hip);
+// the next kNumSplitCfgs: the tiled kernel with a split reduction
+// (k_igemm_i8_split.hip), whose partial tiles live in the scratch.
+namespace {
+int split_first() { return ig::kNumCfgs + lowc_num_configs(); }
+bool is_lowc(int cfg) { return cfg >= ig::kNumCfgs && cfg < split_first(); }
+bool is_split(int cfg) { return cfg >= split_first() && cfg < split_first() + ig::kNumSplitCfgs; }
+// base tile config of a tiled or split config
+int base_of(int cfg) { return is_split(cfg) ? ig::kSplitCfgs[cfg - split_first()].base : cfg; }
+}  // namespace
+
+int igemm_num_configs() { return split_first() + ig::kNumSplitCfgs; }
 
 bool igemm_supported(const Prob& p, int cfg, std::string* why) {
-    if (cfg >= ig::kNumCfgs && cfg < igemm_num_configs()) return lowc_supported(p, cfg - ig::kNumCfgs, why);
+    if (is_lowc(cfg)) return lowc_supported(p, cfg - ig::kNumCfgs, why);
+    ig::Geo g;
+    if (is_split(cfg)) {
+        int cps;
+        return ig::split_geometry(p, cfg - split_first(), &g, &cps, why);
+    }
     if (cfg < 0 || cfg >= ig::kNumCfgs) {
         if (why) *why = "implicit GEMM: no such config";
         return false;
     }
-    ig::Geo g;
     return ig::geometry(p, ig::kCfgs[cfg], &g, why);
 }
 
 size_t igemm_filter_bytes(const Prob& p, int cfg) {
-    if (cfg >= ig::kNumCfgs) return lowc_filter_bytes(p, cfg - ig::kNumCfgs);
+    if (is_lowc(cfg)) return lowc_filter_bytes(p, cfg - ig::kNumCfgs);
     ig::Geo g;
-    if (!ig::geometry(p, ig::kCfgs[cfg], &g, nullptr)) return 0;
-    return ig::filter_bytes(p, ig::kCfgs[cfg], g);
+    if (!ig::geometry(p, ig::kCfgs[base_of(cfg)], &g, nullptr)) return 0;
+    return ig::filter_bytes(p, ig::kCfgs[base_of(cfg)], g);
+}
+
+size_t igemm_scratch_bytes(const Prob& p, int cfg) {
+    return is_split(cfg) ? ig::split_scratch_bytes(p, cfg - split_first()) : 0;
 }
 
 cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
-    if (cfg >= ig::kNumCfgs) return lowc_prepare(p, cfg - ig::kNumCfgs, w, wp, st);
+    if (is_lowc(cfg)) return lowc_prepare(p, cfg - ig::kNumCfgs, w, wp, st);
+    cfg = base_of(cfg);  // a split config reads its base config's prepared filter
     ig::Geo g;
     std::string why;
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
@@ -38,10 +57,16 @@ cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipSt
 }
 
 cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp, const float* scale, void* y,
-                         hipStream_t st) {
-    if (cfg >= ig::kNumCfgs) return lowc_launch(p, cfg - ig::kNumCfgs, x, wp, scale, y, st);
+                         void* scratch, hipStream_t st) {
+    if (is_lowc(cfg)) return lowc_launch(p, cfg - ig::kNumCfgs, x, wp, scale, y, st);
     ig::Geo g;
     std::string why;
+    if (is_split(cfg)) {
+        int cps;
+        if (!ig::split_geometry(p, cfg - split_first(), &g, &cps, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+        if (scratch == nullptr) return set_error(CFWD_ERR_WORKSPACE, "implicit GEMM split reduction needs scratch");
+        return igemm_launch_i8_split(cfg - split_first(), p, g, cps, x, wp, scale, y, scratch, st);
+    }
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     switch (p.dtype) {
         case CFWD_F32: return igemm_launch_f32(cfg, p, g, x, wp, scale, y, st);

@@ -73,6 +73,12 @@ SMALL = [
     # depthwise with 96 channels and 20 rows: strip, band and channel indices
     # through divisions by 96 and by the band count
     ("dw_c96", 3, 96, 20, 32, 96, 3, 3, 1, 1, 1, 96),
+    # int8 split reductions: four chunks with a ragged last one and K = 37
+    # (partial tiles of padded channel blocks); three chunks in two splits
+    # of two and one; a 1x1 stride-2 layer with four chunks
+    ("split_c200_k37", 2, 200, 9, 11, 37, 3, 3, 1, 1, 1, 1),
+    ("split_c130_3chunks", 3, 130, 7, 7, 72, 3, 3, 1, 1, 1, 1),
+    ("split_1x1_s2_c256", 2, 256, 14, 14, 64, 1, 1, 2, 0, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
