@@ -30,7 +30,9 @@ EXPORTED = [
     "cfwd_prepare_filter", "cfwd_workspace_size", "cfwd_scratch_size", "cfwd_conv2d_fwd", "cfwd_fastrun_select",
     "cfwd_fastrun_workspace_size", "cfwd_fastrun_lookup", "cfwd_fastrun_load", "cfwd_fastrun_save",
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
+    "cfwd_conv2d_fwd_noalloc",
 ]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CFWD_NOALLOC_SCRATCH_BYTES
 
 
 class ConvDesc(ctypes.Structure):
@@ -82,6 +84,7 @@ def _lib():
             "cfwd_workspace_size": [dp, Algo, P(sz)],
             "cfwd_scratch_size": [dp, Algo, P(sz)],
             "cfwd_conv2d_fwd": [dp, Algo, vp, vp, vp, vp, vp, vp, sz, vp],
+            "cfwd_conv2d_fwd_noalloc": [dp, Algo, vp, vp, vp, vp, vp, vp],
             "cfwd_fastrun_select": [dp, vp, vp, vp, vp, vp, sz, vp, P(Algo)],
             "cfwd_fastrun_workspace_size": [dp, P(sz)],
             "cfwd_fastrun_lookup": [dp, P(Algo)],
@@ -221,6 +224,13 @@ def conv2d_fwd_raw(desc: ConvDesc, a: Algo, x: int, w: int, w_prepared: int, sca
     """cfwd_conv2d_fwd with integer device pointers; returns the status."""
     return _lib().cfwd_conv2d_fwd(ctypes.byref(desc), a, x or None, w or None, w_prepared or None, scale or None,
                                   y or None, ws or None, ws_bytes, stream or None)
+
+
+def conv2d_fwd_noalloc_raw(desc: ConvDesc, a: Algo, x: int, w: int, w_prepared: int, scale: int, y: int,
+                           stream: int) -> int:
+    """cfwd_conv2d_fwd_noalloc with integer device pointers; returns the status."""
+    return _lib().cfwd_conv2d_fwd_noalloc(ctypes.byref(desc), a, x or None, w or None, w_prepared or None,
+                                          scale or None, y or None, stream or None)
 
 
 def prepare_filter_raw(desc: ConvDesc, a: Algo, w: int, wp: int, nbytes: int, stream: int) -> int:

@@ -398,6 +398,36 @@ cfwd_status conv_impl(const Prob& p, const cfwd_algo& a, const void* x, const vo
     return run(p, a, x, w, wp, scale, y, scratch, st);
 }
 
+// ------------------------------------------------------------- allocation-free entry point
+
+// Scratch of cfwd_conv2d_fwd_noalloc: one array per device, holding what a
+// call would otherwise take from the caller's workspace (the prepared filter
+// when none is passed, and the algorithm's scratch).  Each device holds its
+// own copy until the process ends.  `scratch` names a host-side stand-in;
+// kernels get the device address hipGetSymbolAddress returns for the
+// current device, cached per device on the first call there.
+static __device__ __align__(256) uint8_t scratch[CFWD_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+cfwd_status static_scratch(void** out) {
+    int dev = 0;
+    cfwd_status s = check_hip(hipGetDevice(&dev), "hipGetDevice");
+    if (s != CFWD_OK) return s;
+    if (dev < 0 || dev >= kMaxDevices) return set_error(CFWD_ERR_UNSUPPORTED, "device index out of range");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        s = check_hip(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        if (s != CFWD_OK) return s;
+        if (ptr == nullptr) return set_error(CFWD_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return CFWD_OK;
+}
+
 // ------------------------------------------------------------- Fast-Run selection
 
 constexpr int kWarmup = 2;
@@ -756,6 +786,30 @@ cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc* desc, cfwd_algo algo, const vo
         if (s != CFWD_OK) return s;
     }
     return conv_impl(p, a, x, w_kcrs, w_prepared, requant_scale, y, workspace, ws_bytes, st);
+}
+
+cfwd_status cfwd_conv2d_fwd_noalloc(const cfwd_conv_desc* desc, cfwd_algo algo, const void* x, const void* w_kcrs,
+                                    const void* w_prepared, const float* requant_scale, void* y, void* stream) {
+    Prob p;
+    std::string why;
+    cfwd_status s = make_prob(desc, &p, &why);
+    if (s != CFWD_OK) return set_error(s, why);
+    cfwd_algo a;
+    s = resolve(p, algo, &a);  // AUTO: the Fast-Run map, else the fixed preference (never a search)
+    if (s != CFWD_OK) return s;
+    const size_t need = w_prepared ? scratch_bytes(p, a) : workspace_bytes(p, a);
+    if (need > CFWD_NOALLOC_SCRATCH_BYTES)
+        return set_error(CFWD_ERR_WORKSPACE, std::string(cfwd_algo_name(a)) + " needs " + std::to_string(need) +
+                                                 " bytes of scratch; the allocation-free entry point has " +
+                                                 std::to_string(static_cast<size_t>(CFWD_NOALLOC_SCRATCH_BYTES)) +
+                                                 (w_prepared ? "" : " (pass a prepared filter to need less)"));
+    void* ws = nullptr;
+    if (need > 0) {
+        s = static_scratch(&ws);
+        if (s != CFWD_OK) return s;
+    }
+    return conv_impl(p, a, x, w_kcrs, w_prepared, requant_scale, y, ws, ws ? CFWD_NOALLOC_SCRATCH_BYTES : 0,
+                     static_cast<hipStream_t>(stream));
 }
 
 cfwd_status cfwd_fastrun_lookup(const cfwd_conv_desc* desc, cfwd_algo* algo) {

@@ -150,6 +150,29 @@ cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc *desc, cfwd_algo algo, const vo
                             const float *requant_scale, void *y, void *workspace,
                             size_t ws_bytes, void *stream);
 
+/* Scratch capacity of cfwd_conv2d_fwd_noalloc, per device (64 MiB). */
+#define CFWD_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* Allocation-free variant of cfwd_conv2d_fwd, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and result as
+ * cfwd_conv2d_fwd without the workspace: what that call takes from the
+ * workspace (the prepared filter when w_prepared is NULL, plus the
+ * algorithm's scratch -- split-reduction partial tiles, Winograd transformed
+ * input) lives instead in a library-owned device array of
+ * CFWD_NOALLOC_SCRATCH_BYTES, one per device, held until the process ends.
+ * Returns CFWD_ERR_WORKSPACE, enqueuing nothing, when the resolved algorithm
+ * needs more than that (cfwd_scratch_size / cfwd_workspace_size tell in
+ * advance).  AUTO resolves from the Fast-Run map or the fixed preference,
+ * never by a search.  Every call on one device shares that device's array:
+ * calls that overlap on one GPU (other streams, other host threads) race on
+ * it; calls in one stream are ordered.  No kernel needs the array zeroed --
+ * each overwrites what it reads -- so the previous call's contents are
+ * harmless.  Allocates nothing, frees nothing. */
+cfwd_status cfwd_conv2d_fwd_noalloc(const cfwd_conv_desc *desc, cfwd_algo algo, const void *x,
+                                    const void *w_kcrs, const void *w_prepared,
+                                    const float *requant_scale, void *y, void *stream);
+
 /* Fast-Run selection phase (MegEngine inference article, section "Fast-Run"):
  * time every candidate of cfwd_list_candidates on this device with these
  * buffers (median of 7 runs after 2 warm-ups; before each run the Infinity
