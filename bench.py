@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--algo", default="auto", help="auto (Fast-Run) or family[/config], e.g. implicit_gemm/7")
     ap.add_argument("--settle", type=float, default=0.3, help="seconds of untimed launches before the warm-up steps")
     ap.add_argument("--sets", type=int, default=0, help="rotated buffer sets (0: enough for > 512 MB)")
-    ap.add_argument("--telemetry-window", type=float, default=0.3,
+    ap.add_argument("--telemetry-window", type=float, default=0.5,
                     help="seconds of further untimed steps while clock and power are sampled")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle CPU work at most")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
@@ -223,7 +223,7 @@ def main():
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
 
-    sampler = telemetry.Sampler(torch.cuda.current_device()).start()
+    sampler = telemetry.Sampler(torch.cuda.current_device())
     t_end = time.perf_counter() + a.settle
     i = 0
     while time.perf_counter() < t_end:
@@ -260,7 +260,8 @@ def main():
         layer_avg = [timed(lambda i, l=l: launch(l, i), a.steps) for l in layers]
 
     # clock and power under the same load: keep launching whole steps for a
-    # while after the timed region, so the sampler sees a sustained window
+    # while after the timed region, sampled only while those launches run
+    sampler.start()
     t_end = time.perf_counter() + a.telemetry_window
     i = 0
     while time.perf_counter() < t_end:
