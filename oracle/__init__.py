@@ -71,6 +71,14 @@ class Oracle:
         lib.oracle_conv2d_f64_points.restype = ctypes.c_int
         lib.oracle_conv2d_i8_points.argtypes = [vp, vp, i32p, ctypes.c_long, vp, vp]
         lib.oracle_conv2d_i8_points.restype = ctypes.c_int
+        lib.oracle_epilogue_f64.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long]
+        lib.oracle_epilogue_f64.restype = ctypes.c_int
+        lib.oracle_requant_epi_one.argtypes = [ctypes.c_int64, ctypes.c_float, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_int8, ctypes.c_int]
+        lib.oracle_requant_epi_one.restype = ctypes.c_int8
+        lib.oracle_requant_epi_i8.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_long,
+                                              vp]
+        lib.oracle_requant_epi_i8.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -149,6 +157,67 @@ class Oracle:
         """int8 convolution followed by the requantisation rule; returns (y_int8, acc_int64)."""
         acc = self.conv2d_int8(x, w, stride, padding, dilation, groups)
         return self.requant(acc, scale), acc
+
+    # ---- fused epilogue (reading in oracle.c): bias, then residual, then ReLU
+
+    def epilogue(self, y, den, bias=None, residual=None, relu=False):
+        """(y', den') = the fused epilogue applied to fp64 conv outputs [N, K, ...].
+
+        y' = act(y + bias[k] + residual); den' = den + |bias[k]| + |residual|.
+        """
+        y = np.array(y, dtype=np.float64, order="C")
+        den = np.array(den, dtype=np.float64, order="C")
+        N, K = y.shape[0], y.shape[1]
+        hw = int(np.prod(y.shape[2:], dtype=np.int64)) if y.ndim > 2 else 1
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float64)
+        r = None if residual is None else np.ascontiguousarray(residual, dtype=np.float64)
+        if b is not None and b.shape != (K,):
+            raise ValueError("bias must have shape [K]")
+        if r is not None and r.shape != y.shape:
+            raise ValueError("residual must have the output's shape")
+        self.lib.oracle_epilogue_f64(y.ctypes.data, den.ctypes.data, None if b is None else b.ctypes.data,
+                                     None if r is None else r.ctypes.data, int(bool(relu)), N, K, hw)
+        return y, den
+
+    def conv2d_fused(self, x, w, bias=None, residual=None, relu=False, stride=1, padding=0, dilation=1, groups=1):
+        """fp64 (y, den') of conv followed by the fused epilogue."""
+        y, den = self.conv2d(x, w, stride, padding, dilation, groups)
+        return self.epilogue(y, den, bias, residual, relu)
+
+    def requant_epi(self, acc, scale, bias=None, residual=None, relu=False):
+        """int8 outputs of the fused int8 epilogue over [N, K, ...] accumulators."""
+        acc = np.ascontiguousarray(acc, dtype=np.int64)
+        scale = np.ascontiguousarray(scale, dtype=np.float32)
+        N, K = acc.shape[0], acc.shape[1]
+        hw = int(np.prod(acc.shape[2:], dtype=np.int64)) if acc.ndim > 2 else 1
+        if scale.shape != (K,):
+            raise ValueError("scale must have shape [K]")
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.int32)
+        r = None if residual is None else np.ascontiguousarray(residual, dtype=np.int8)
+        if b is not None and b.shape != (K,):
+            raise ValueError("bias must have shape [K]")
+        if r is not None and r.shape != acc.shape:
+            raise ValueError("residual must have the output's shape")
+        y = np.empty(acc.shape, dtype=np.int8)
+        if self.lib.oracle_requant_epi_i8(acc.ctypes.data, scale.ctypes.data, None if b is None else b.ctypes.data,
+                                          None if r is None else r.ctypes.data, int(bool(relu)), N, K, hw,
+                                          y.ctypes.data):
+            raise OverflowError("an accumulator plus its bias does not fit in int32")
+        return y
+
+    def requant_epi_one(self, acc: int, scale: float, bias: int = 0, residual=None, relu: bool = False) -> int:
+        """The fused int8 epilogue for a single accumulator value."""
+        if not (-2**31 <= int(acc) + int(bias) < 2**31):
+            raise OverflowError("accumulator plus bias outside int32")
+        return int(self.lib.oracle_requant_epi_one(int(acc), float(np.float32(scale)), int(bias),
+                                                   int(residual is not None),
+                                                   int(residual) if residual is not None else 0, int(bool(relu))))
+
+    def conv2d_int8_requant_fused(self, x, w, scale, bias=None, residual=None, relu=False, stride=1, padding=0,
+                                  dilation=1, groups=1):
+        """int8 conv followed by the fused int8 epilogue; returns (y_int8, acc_int64)."""
+        acc = self.conv2d_int8(x, w, stride, padding, dilation, groups)
+        return self.requant_epi(acc, scale, bias, residual, relu), acc
 
     @staticmethod
     def _points_idx(idx):
@@ -230,6 +299,26 @@ def conv2d_points(*a, **k):
 
 def conv2d_int8_points(*a, **k):
     return default().conv2d_int8_points(*a, **k)
+
+
+def epilogue(*a, **k):
+    return default().epilogue(*a, **k)
+
+
+def conv2d_fused(*a, **k):
+    return default().conv2d_fused(*a, **k)
+
+
+def requant_epi(*a, **k):
+    return default().requant_epi(*a, **k)
+
+
+def requant_epi_one(*a, **k):
+    return default().requant_epi_one(*a, **k)
+
+
+def conv2d_int8_requant_fused(*a, **k):
+    return default().conv2d_int8_requant_fused(*a, **k)
 
 
 def normalised_error(y_hat, y, den):

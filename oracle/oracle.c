@@ -316,3 +316,89 @@ int oracle_conv2d_i8_points(const int8_t *x, const int8_t *w, const int *p,
     }
     return 0;
 }
+
+/*
+ * Fused epilogue.  The Momenta talk (section "Graph層面") folds the bias add
+ * and the ReLU that follow a convolution into the convolution itself, so the
+ * output is written once.  What is computed is the tail of a ResNet block in
+ * inference: a per-output-channel bias (the folded batch norm), then the
+ * skip connection (a residual tensor of the output's shape), then the
+ * activation.  Reading taken (the pages give no formula):
+ *
+ *   float: y = act(conv + bias[k] + residual), every step in fp64, and the
+ *          error normaliser grows by the absolute values of the added
+ *          terms: den' = den + |bias[k]| + |residual|.
+ *   int8:  y = clamp(rne(fp32(acc + bias[k]) * scale[k] + fp32(residual)), lo, 127)
+ *          with acc + bias an exact integer sum (it must fit in int32), the
+ *          IEEE int32 -> fp32 conversion, one fp32 multiply, one fp32 add
+ *          (no contraction), ties to even, lo = 0 with ReLU and -127 without.
+ *
+ * bias / residual may be NULL (absent); act is 0 (none) or 1 (ReLU).
+ */
+
+/* In place on y and den, both [N][K][HW]; bias [K], residual [N][K][HW]. */
+int oracle_epilogue_f64(double *y, double *den, const double *bias, const double *res, int relu,
+                        int N, int K, long HW)
+{
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            for (long i = 0; i < HW; ++i) {
+                const size_t o = ((size_t)n * K + k) * HW + i;
+                double v = y[o];
+                double d = den[o];
+                if (bias) {
+                    v += bias[k];
+                    d += fabs(bias[k]);
+                }
+                if (res) {
+                    v += res[o];
+                    d += fabs(res[o]);
+                }
+                if (relu && v < 0.0)
+                    v = 0.0;
+                y[o] = v;
+                den[o] = d;
+            }
+    return 0;
+}
+
+/* One int8 output of the fused epilogue (see above).  acc + bias must fit in
+ * int32 (the caller checks). */
+int8_t oracle_requant_epi_one(int64_t acc, float scale, int64_t bias, int has_res, int8_t res, int relu)
+{
+    const float a = (float)(int32_t)(acc + bias);
+    float q = a * scale; /* one IEEE fp32 multiply */
+    if (has_res)
+        q = q + (float)res; /* one IEEE fp32 add */
+    q = rintf(q);
+    const float lo = relu ? 0.0f : -127.0f;
+    if (q > 127.0f)
+        return 127;
+    if (q < lo)
+        return (int8_t)lo;
+    return (int8_t)q;
+}
+
+/* Whole tensors: acc and res [N][K][HW], scale [K], bias [K] (int32, or
+ * NULL), res (or NULL).  Returns -1, writing nothing, if any acc + bias is
+ * outside int32. */
+int oracle_requant_epi_i8(const int64_t *acc, const float *scale, const int32_t *bias, const int8_t *res,
+                          int relu, int N, int K, long HW, int8_t *y)
+{
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            for (long i = 0; i < HW; ++i) {
+                const size_t o = ((size_t)n * K + k) * HW + i;
+                const int64_t s = acc[o] + (bias ? bias[k] : 0);
+                if (s > INT32_MAX || s < INT32_MIN)
+                    return -1;
+            }
+    for (int n = 0; n < N; ++n)
+        for (int k = 0; k < K; ++k)
+            for (long i = 0; i < HW; ++i) {
+                const size_t o = ((size_t)n * K + k) * HW + i;
+                y[o] = oracle_requant_epi_one(acc[o], scale[k], bias ? bias[k] : 0, res != NULL,
+                                              res ? res[o] : 0, relu);
+            }
+    return 0;
+}

@@ -12,6 +12,7 @@ import os
 import pytest
 
 import oracle
+import tests.test_oracle_epilogue as epi_pins
 import tests.test_oracle_pins as pins
 
 MUTATIONS = {
@@ -26,6 +27,23 @@ MUTATIONS = {
     "round_half_away": ("rintf(prod)", "roundf(prod)"),
     "asymmetric_clamp": ("if (q < -127.0f)\n        return -127;", "if (q < -128.0f)\n        return -128;"),
     "exact_product": ("const float prod = a * scale;", "const float prod = (float)((double)acc * (double)scale); (void)a;"),
+    # fused epilogue
+    "epi_bias_dropped": ("v += bias[k];", "v += 0.0 * bias[k];"),
+    "epi_bias_indexed_by_image": ("v += bias[k];", "v += bias[n % K];"),
+    "epi_den_without_bias": ("d += fabs(bias[k]);", "d += 0.0;"),
+    "epi_den_without_residual": ("d += fabs(res[o]);", "d += 0.0;"),
+    "epi_relu_ignored": ("if (relu && v < 0.0)", "if (relu < 0 && v < 0.0)"),
+    "epi_relu_before_residual": (
+        "if (res) {\n                    v += res[o];\n                    d += fabs(res[o]);\n                }\n"
+        "                if (relu && v < 0.0)\n                    v = 0.0;",
+        "if (relu && v < 0.0)\n                    v = 0.0;\n                if (res) {\n"
+        "                    v += res[o];\n                    d += fabs(res[o]);\n                }"),
+    "epi_int8_bias_after_scale": ("const float a = (float)(int32_t)(acc + bias);\n    float q = a * scale;",
+                                  "const float a = (float)(int32_t)acc;\n    float q = a * scale + (float)bias;"),
+    "epi_int8_residual_before_scale": ("q = q + (float)res; /* one IEEE fp32 add */",
+                                       "q = (a + (float)res) * scale;"),
+    "epi_int8_relu_floor_ignored": ("const float lo = relu ? 0.0f : -127.0f;",
+                                    "const float lo = -127.0f;\n    (void)relu;"),
 }
 
 
@@ -42,6 +60,8 @@ def pin_checks():
     yield "saturate", pins.test_requant_saturates_symmetrically
     yield "fp32_first", pins.test_requant_converts_acc_to_fp32_first
     yield "delta", lambda: pins.test_delta_kernel_is_identity(3, 3)
+    for pin in epi_pins.PINS:
+        yield pin.__name__, pin
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
