@@ -30,8 +30,9 @@ EXPORTED = [
     "cfwd_prepare_filter", "cfwd_workspace_size", "cfwd_scratch_size", "cfwd_conv2d_fwd", "cfwd_fastrun_select",
     "cfwd_fastrun_workspace_size", "cfwd_fastrun_lookup", "cfwd_fastrun_load", "cfwd_fastrun_save",
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
-    "cfwd_conv2d_fwd_noalloc",
+    "cfwd_conv2d_fwd_noalloc", "cfwd_conv2d_fwd_ex",
 ]
+ACT_NONE, ACT_RELU = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CFWD_NOALLOC_SCRATCH_BYTES
 
 
@@ -39,6 +40,11 @@ class ConvDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in ("n", "c", "h", "w", "k", "r", "s", "stride_h", "stride_w", "pad_h",
                                             "pad_w", "dil_h", "dil_w", "groups")] + \
                [("layout", ctypes.c_int), ("x", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
+class Epilogue(ctypes.Structure):
+    """cfwd_epilogue: bias [K] (fp32, or int32 for int8), residual (y's shape / layout / dtype), activation."""
+    _fields_ = [("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p), ("act", ctypes.c_int)]
 
 
 class Algo(ctypes.Structure):
@@ -85,6 +91,7 @@ def _lib():
             "cfwd_scratch_size": [dp, Algo, P(sz)],
             "cfwd_conv2d_fwd": [dp, Algo, vp, vp, vp, vp, vp, vp, sz, vp],
             "cfwd_conv2d_fwd_noalloc": [dp, Algo, vp, vp, vp, vp, vp, vp],
+            "cfwd_conv2d_fwd_ex": [dp, Algo, vp, vp, vp, vp, P(Epilogue), vp, vp, sz, vp],
             "cfwd_fastrun_select": [dp, vp, vp, vp, vp, vp, sz, vp, P(Algo)],
             "cfwd_fastrun_workspace_size": [dp, P(sz)],
             "cfwd_fastrun_lookup": [dp, P(Algo)],
@@ -226,6 +233,21 @@ def conv2d_fwd_raw(desc: ConvDesc, a: Algo, x: int, w: int, w_prepared: int, sca
                                   y or None, ws or None, ws_bytes, stream or None)
 
 
+def epilogue_of(bias: int = 0, residual: int = 0, relu: bool = False) -> Optional[Epilogue]:
+    """cfwd_epilogue from device pointers, or None when there is nothing to fuse."""
+    if not bias and not residual and not relu:
+        return None
+    return Epilogue(bias or None, residual or None, ACT_RELU if relu else ACT_NONE)
+
+
+def conv2d_fwd_ex_raw(desc: ConvDesc, a: Algo, x: int, w: int, w_prepared: int, scale: int, ep: Optional[Epilogue],
+                      y: int, ws: int, ws_bytes: int, stream: int) -> int:
+    """cfwd_conv2d_fwd_ex with integer device pointers; returns the status."""
+    return _lib().cfwd_conv2d_fwd_ex(ctypes.byref(desc), a, x or None, w or None, w_prepared or None, scale or None,
+                                     ctypes.byref(ep) if ep is not None else None, y or None, ws or None, ws_bytes,
+                                     stream or None)
+
+
 def conv2d_fwd_noalloc_raw(desc: ConvDesc, a: Algo, x: int, w: int, w_prepared: int, scale: int, y: int,
                            stream: int) -> int:
     """cfwd_conv2d_fwd_noalloc with integer device pointers; returns the status."""
@@ -310,16 +332,18 @@ def prepare_filter(w, desc: ConvDesc, a: Algo):
 
 
 def conv2d_fwd(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", channels=None, algo_kind="auto",
-               config_id=-1, requant_scale=None, out=None, w_prepared=None, workspace=None):
+               config_id=-1, requant_scale=None, out=None, w_prepared=None, workspace=None, bias=None, residual=None,
+               relu=False):
     """y = conv(x, w) on the current stream.  Tensors on the GPU, contiguous.
 
     ``algo_kind`` is one of auto, implicit_gemm, winograd_f2x2_3x3,
     winograd_f6x6_3x3, direct, pointwise; ``requant_scale`` (float32 [K]) is
     required for int8.  ``w_prepared`` is the output of ``prepare_filter`` for
-    the same resolved algorithm.
+    the same resolved algorithm.  ``bias`` (float32 [K], int32 for int8),
+    ``residual`` (shaped like the output) and ``relu`` are the fused epilogue.
     """
     torch = _torch()
-    _check_dev(x, w, requant_scale, out, w_prepared, workspace)
+    _check_dev(x, w, requant_scale, out, w_prepared, workspace, bias, residual)
     desc = desc_for(x, w, stride, padding, dilation, groups, layout, channels)
     a = resolve_algo(desc, algo(algo_kind, config_id))
     if out is None:
@@ -329,9 +353,12 @@ def conv2d_fwd(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", c
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=x.device)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
-    st = conv2d_fwd_raw(desc, a, x.data_ptr(), w.data_ptr(), w_prepared.data_ptr() if w_prepared is not None else 0,
-                        requant_scale.data_ptr() if requant_scale is not None else 0, out.data_ptr(),
-                        workspace.data_ptr() if workspace is not None else 0, ws_bytes, _stream())
+    ep = epilogue_of(bias.data_ptr() if bias is not None else 0,
+                     residual.data_ptr() if residual is not None else 0, relu)
+    st = conv2d_fwd_ex_raw(desc, a, x.data_ptr(), w.data_ptr(),
+                           w_prepared.data_ptr() if w_prepared is not None else 0,
+                           requant_scale.data_ptr() if requant_scale is not None else 0, ep, out.data_ptr(),
+                           workspace.data_ptr() if workspace is not None else 0, ws_bytes, _stream())
     _check(st)
     return out
 
@@ -373,10 +400,11 @@ class LayerPlan:
     """
 
     def __init__(self, x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", channels=None,
-                 requant_scale=None, algo_spec="auto"):
+                 requant_scale=None, algo_spec="auto", bias=None, relu=False):
         torch = _torch()
-        _check_dev(x, w, requant_scale)
+        _check_dev(x, w, requant_scale, bias)
         self.w, self.scale = w, requant_scale
+        self.bias, self.relu = bias, relu  # fused epilogue (a residual is given per launch)
         self.desc = desc_for(x, w, stride, padding, dilation, groups, layout, channels)
         self.out_shape = _out_shape(self.desc)
         self.dtype, self.device = x.dtype, x.device
@@ -409,17 +437,19 @@ class LayerPlan:
     def new_output(self):
         return _torch().empty(self.out_shape, dtype=self.dtype, device=self.device)
 
-    def launch_raw(self, x_ptr: int, y_ptr: int, stream: int) -> int:
+    def launch_raw(self, x_ptr: int, y_ptr: int, stream: int, residual_ptr: int = 0) -> int:
         """Enqueue the layer on ``stream`` with raw device pointers; returns the status."""
-        return conv2d_fwd_raw(self.desc, self.algo_arg, x_ptr, self.w.data_ptr(),
-                              self.wp.data_ptr() if self.wp is not None else 0,
-                              self.scale.data_ptr() if self.scale is not None else 0, y_ptr,
-                              self.scratch.data_ptr() if self.scratch_bytes else 0, self.scratch_bytes, stream)
+        ep = epilogue_of(self.bias.data_ptr() if self.bias is not None else 0, residual_ptr, self.relu)
+        return conv2d_fwd_ex_raw(self.desc, self.algo_arg, x_ptr, self.w.data_ptr(),
+                                 self.wp.data_ptr() if self.wp is not None else 0,
+                                 self.scale.data_ptr() if self.scale is not None else 0, ep, y_ptr,
+                                 self.scratch.data_ptr() if self.scratch_bytes else 0, self.scratch_bytes, stream)
 
-    def __call__(self, x, out=None):
-        """y = conv(x) on the current stream (x shaped and typed like the set-up input)."""
-        _check_dev(x, out)
+    def __call__(self, x, out=None, residual=None):
+        """y = conv(x) (+ the fused epilogue) on the current stream (x shaped and typed like the set-up input)."""
+        _check_dev(x, out, residual)
         if out is None:
             out = self.new_output()
-        _check(self.launch_raw(x.data_ptr(), out.data_ptr(), _stream()))
+        _check(self.launch_raw(x.data_ptr(), out.data_ptr(), _stream(),
+                               residual.data_ptr() if residual is not None else 0))
         return out

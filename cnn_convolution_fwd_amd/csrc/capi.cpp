@@ -352,14 +352,14 @@ cfwd_status prepare(const Prob& p, const cfwd_algo& a, const void* w, void* wp, 
 }
 
 cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w, const void* wp,
-                const float* scale, void* y, void* scratch, hipStream_t st) {
+                const float* scale, void* y, void* scratch, const Epi& e, hipStream_t st) {
     cfwd_status s;
     switch (a.kind) {
-        case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, scratch, st); break;
-        case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, st); break;
-        case CFWD_ALGO_DIRECT: s = direct_launch(p, a.config_id, x, w, scale, y, st); break;
-        case CFWD_ALGO_WINOGRAD_F2X2_3X3: s = winograd_launch(p, 2, a.config_id, x, wp, scratch, y, st); break;
-        case CFWD_ALGO_WINOGRAD_F6X6_3X3: s = winograd_launch(p, 6, a.config_id, x, wp, scratch, y, st); break;
+        case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, scratch, e, st); break;
+        case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, e, st); break;
+        case CFWD_ALGO_DIRECT: s = direct_launch(p, a.config_id, x, w, scale, y, e, st); break;
+        case CFWD_ALGO_WINOGRAD_F2X2_3X3: s = winograd_launch(p, 2, a.config_id, x, wp, scratch, y, e, st); break;
+        case CFWD_ALGO_WINOGRAD_F6X6_3X3: s = winograd_launch(p, 6, a.config_id, x, wp, scratch, y, e, st); break;
         default: return set_error(CFWD_ERR_INVALID_ARG, "unknown algorithm kind");
     }
     if (s != CFWD_OK) return s;
@@ -368,7 +368,7 @@ cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w,
 
 // Full conv: validation of pointers and sizes, optional on-the-fly prepare.
 cfwd_status conv_impl(const Prob& p, const cfwd_algo& a, const void* x, const void* w, const void* wp,
-                      const float* scale, void* y, void* ws, size_t ws_bytes, hipStream_t st) {
+                      const float* scale, void* y, void* ws, size_t ws_bytes, hipStream_t st, const Epi& e = Epi{}) {
     if (!x || !w || !y) return set_error(CFWD_ERR_INVALID_ARG, "x, w and y must not be NULL");
     if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (wp && !aligned16(wp)) || (ws && !aligned16(ws)))
         return set_error(CFWD_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
@@ -395,7 +395,27 @@ cfwd_status conv_impl(const Prob& p, const cfwd_algo& a, const void* x, const vo
                                                      cfwd_algo_name(a));
         scratch = ws;
     }
-    return run(p, a, x, w, wp, scale, y, scratch, st);
+    return run(p, a, x, w, wp, scale, y, scratch, e, st);
+}
+
+// Checks a C-ABI epilogue and turns it into an Epi.
+cfwd_status make_epi(const Prob& p, const cfwd_epilogue* ep, const void* y, Epi* out) {
+    *out = Epi{};
+    if (ep == nullptr) return CFWD_OK;
+    if (ep->act != CFWD_ACT_NONE && ep->act != CFWD_ACT_RELU) return set_error(CFWD_ERR_INVALID_ARG, "unknown activation");
+    if (ep->bias && (reinterpret_cast<uintptr_t>(ep->bias) & 3u))
+        return set_error(CFWD_ERR_INVALID_ARG, "bias must be 4-byte aligned");
+    if (ep->residual) {
+        if (!aligned16(ep->residual)) return set_error(CFWD_ERR_INVALID_ARG, "residual must be 16-byte aligned");
+        const uintptr_t r0 = reinterpret_cast<uintptr_t>(ep->residual);
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(y);
+        const uintptr_t bytes = static_cast<uintptr_t>(p.y_img) * p.n * p.esize;
+        if (r0 < y0 + bytes && y0 < r0 + bytes) return set_error(CFWD_ERR_INVALID_ARG, "residual must not overlap y");
+    }
+    out->bias = ep->bias;
+    out->res = ep->residual;
+    out->relu = ep->act == CFWD_ACT_RELU ? 1 : 0;
+    return CFWD_OK;
 }
 
 // ------------------------------------------------------------- allocation-free entry point
@@ -674,7 +694,7 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
     // Reference output: the generic direct kernel (exact integer arithmetic
     // for int8; fp32 accumulation for float).  For float dtypes the error
     // normaliser den = conv(|x|, |w|) is computed the same way.
-    s = direct_launch(p, 0, x, w_kcrs, requant_scale, ref, st);
+    s = direct_launch(p, 0, x, w_kcrs, requant_scale, ref, Epi{}, st);
     if (s != CFWD_OK) return s;
     s = zero_output_channel_padding(p, ref, st);
     if (s != CFWD_OK) return s;
@@ -683,7 +703,7 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
         if (s != CFWD_OK) return s;
         s = abs_copy(p, w_kcrs, ws + L.wabs, static_cast<long long>(p.k) * p.cg * p.r * p.s, st);
         if (s != CFWD_OK) return s;
-        s = direct_launch(p, 0, ws + L.xabs, ws + L.wabs, nullptr, ws + L.den, st);
+        s = direct_launch(p, 0, ws + L.xabs, ws + L.wabs, nullptr, ws + L.den, Epi{}, st);
         if (s != CFWD_OK) return s;
         // NCHWX channels past K: the direct kernel does not write them; den
         // there must be 0 like the candidate's and the reference's outputs
@@ -714,7 +734,7 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
         for (int rep = 0; rep < kWarmup + kReps && s == CFWD_OK; ++rep) {
             if (L.evict_bytes) s = evict_caches(ws + L.evict, L.evict_bytes, static_cast<unsigned>(rep), st);
             if (s == CFWD_OK) s = check_hip(hipEventRecord(e0, st), "hipEventRecord");
-            if (s == CFWD_OK) s = run(p, a, x, w_kcrs, wp, requant_scale, y, scr, st);
+            if (s == CFWD_OK) s = run(p, a, x, w_kcrs, wp, requant_scale, y, scr, Epi{}, st);
             if (s == CFWD_OK) s = check_hip(hipEventRecord(e1, st), "hipEventRecord");
             if (s == CFWD_OK) s = check_hip(hipEventSynchronize(e1), "hipEventSynchronize");
             float ms = 0.0f;
@@ -748,7 +768,7 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
             if (s != CFWD_OK) return s;
         }
         void* scr = scratch_bytes(p, chosen) ? static_cast<uint8_t*>(cand_ws) + round_up(fb, 256) : nullptr;
-        s = run(p, chosen, x, w_kcrs, fb > 0 ? cand_ws : nullptr, requant_scale, y, scr, st);
+        s = run(p, chosen, x, w_kcrs, fb > 0 ? cand_ws : nullptr, requant_scale, y, scr, Epi{}, st);
         if (s != CFWD_OK) return s;
         s = check_hip(hipStreamSynchronize(st), "hipStreamSynchronize");
         if (s != CFWD_OK) return s;
@@ -765,16 +785,27 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
 cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc* desc, cfwd_algo algo, const void* x, const void* w_kcrs,
                             const void* w_prepared, const float* requant_scale, void* y, void* workspace,
                             size_t ws_bytes, void* stream) {
+    return cfwd_conv2d_fwd_ex(desc, algo, x, w_kcrs, w_prepared, requant_scale, nullptr, y, workspace, ws_bytes,
+                              stream);
+}
+
+cfwd_status cfwd_conv2d_fwd_ex(const cfwd_conv_desc* desc, cfwd_algo algo, const void* x, const void* w_kcrs,
+                               const void* w_prepared, const float* requant_scale, const cfwd_epilogue* epilogue,
+                               void* y, void* workspace, size_t ws_bytes, void* stream) {
     Prob p;
     std::string why;
     cfwd_status s = make_prob(desc, &p, &why);
     if (s != CFWD_OK) return set_error(s, why);
+    Epi e;
+    s = make_epi(p, epilogue, y, &e);
+    if (s != CFWD_OK) return s;
+    const bool has_epi = e.bias || e.res || e.relu;
     hipStream_t st = static_cast<hipStream_t>(stream);
     cfwd_algo a;
     if (algo.kind == CFWD_ALGO_AUTO) {
         if (!map_lookup(p, &a)) {
             const char* mode = std::getenv("CFWD_FASTRUN_MODE");
-            if (mode && std::strcmp(mode, "search") == 0 && workspace) {
+            if (mode && std::strcmp(mode, "search") == 0 && workspace && !has_epi) {
                 size_t need = fastrun_layout(p, candidates(p)).total;
                 if (ws_bytes >= need)
                     return cfwd_fastrun_select(desc, x, w_kcrs, requant_scale, y, workspace, ws_bytes, stream, &a);
@@ -785,7 +816,7 @@ cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc* desc, cfwd_algo algo, const vo
         s = resolve(p, algo, &a);
         if (s != CFWD_OK) return s;
     }
-    return conv_impl(p, a, x, w_kcrs, w_prepared, requant_scale, y, workspace, ws_bytes, st);
+    return conv_impl(p, a, x, w_kcrs, w_prepared, requant_scale, y, workspace, ws_bytes, st, e);
 }
 
 cfwd_status cfwd_conv2d_fwd_noalloc(const cfwd_conv_desc* desc, cfwd_algo algo, const void* x, const void* w_kcrs,

@@ -56,6 +56,7 @@ struct Args {
     // partial tile to part + s * N * y_img, in the output's NCHW4 order
     int cps;
     int32_t* part;
+    Epi e;  // fused epilogue
 };
 
 template <typename T> struct Mma;
@@ -240,6 +241,39 @@ template <> __device__ __forceinline__ void store_out4<int8_t>(int8_t* y, long l
                        requant_i8_bits(acc[3], scale));
 }
 
+// The same stores with the fused epilogue (bias, residual, ReLU) applied
+// first; channel k < K, `off` the output element's offset.
+template <typename T, bool EPI>
+__device__ __forceinline__ void store_out_epi(T* y, long long off, typename Mma<T>::acc_t acc, int v, float scale,
+                                              const Epi& e, int k) {
+    if constexpr (!EPI) {
+        store_out<T>(y, off, acc, v, scale);
+    } else if constexpr (sizeof(T) == 1) {
+        y[off] = static_cast<int8_t>(requant_i8_epi_bits(acc[v], scale, e, k, off));
+    } else {
+        f32x4 q;
+        q[v] = epi_float<T>(acc[v], e, k, off);
+        store_out<T>(y, off, q, v, scale);
+    }
+}
+template <typename T, bool EPI>
+__device__ __forceinline__ void store_out4_epi(T* y, long long off, typename Mma<T>::acc_t acc, float scale,
+                                               const Epi& e, int k) {
+    if constexpr (!EPI) {
+        store_out4<T>(y, off, acc, scale);
+    } else if constexpr (sizeof(T) == 1) {
+        *reinterpret_cast<uint32_t*>(y + off) =
+            pack_low_bytes(requant_i8_epi_bits(acc[0], scale, e, k, off), requant_i8_epi_bits(acc[1], scale, e, k, off + 1),
+                           requant_i8_epi_bits(acc[2], scale, e, k, off + 2),
+                           requant_i8_epi_bits(acc[3], scale, e, k, off + 3));
+    } else {
+        f32x4 q;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) q[v] = epi_float<T>(acc[v], e, k, off + v);
+        store_out4<T>(y, off, q, scale);
+    }
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxUnitsPerThread = 8;
@@ -317,7 +351,11 @@ template <typename T> struct Frag<T, 32> {
     static constexpr int NACC = 16;
 };
 
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false>
+// EPI: the fused epilogue (bias, residual, ReLU) is applied as outputs are
+// converted; a separate instantiation, so the plain kernels carry none of
+// its registers.
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false,
+          bool EPI = false>
 __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
     constexpr int NT = WN * FN * FR;
@@ -897,6 +935,13 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 const float sc0 = a.scale[kval ? k : 0];  // no branch around the load
                 const float sc = kval ? sc0 : 0.0f;
                 uint8_t* lrow_base = lds + (kk >> 2) * pitch + (kk & 3);
+                // fused epilogue: channels past K (scale 0) take the last real
+                // channel's bias; pixels of images past N read image N - 1
+                // (their bytes are never stored)
+                const int ke = EPI ? min(k, a.K - 1) : 0;
+                const long long kofs = EPI ? static_cast<long long>(k >> 2) * a.OH * a.OW * 4 + (k & 3) +
+                                                 static_cast<long long>(oh0) * a.OW * 4
+                                           : 0;
 #pragma unroll
                 for (int f = 0; f < FM; ++f)
 #pragma unroll
@@ -904,8 +949,18 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                         const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
                         if (p0 < tile_pix) {
 #pragma unroll
-                            for (int v = 0; v < 4; ++v)
-                                lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(requant_i8_bits(acc[f][nf][grp * 4 + v], sc));
+                            for (int v = 0; v < 4; ++v) {
+                                uint32_t q;
+                                if constexpr (EPI) {
+                                    const int pp = p0 + v, tn = pp / thw;
+                                    const long long o = static_cast<long long>(min(n0 + tn, a.N - 1)) * a.y_img + kofs +
+                                                        static_cast<long long>(pp - tn * thw) * 4;
+                                    q = requant_i8_epi_bits(acc[f][nf][grp * 4 + v], sc, a.e, ke, o);
+                                } else {
+                                    q = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
+                                }
+                                lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(q);
+                            }
                         }
                     }
             }
@@ -953,14 +1008,27 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
             for (int nf = 0; nf < FN; ++nf) {
                 const int kk = (wn * FN + nf) * FR + lrow;  // channel within the tile
+                const int kl = kt * NT + kk;
+                // fused epilogue (whole output rows of one image): output
+                // offset of this channel's first tile pixel
+                const long long ko = EPI ? static_cast<long long>(n0) * a.y_img +
+                                               static_cast<long long>(g * a.Kg + kl) * a.OH * a.OW +
+                                               static_cast<long long>(oh0) * a.OW
+                                         : 0;
 #pragma unroll
                 for (int f = 0; f < FM; ++f)
 #pragma unroll
                     for (int grp = 0; grp < FT::NACC / 4; ++grp) {
                         const int p0 = (wm * FM + f) * FR + 8 * grp + 4 * lgrp;
                         if (p0 < tile_pix) {
-                            const uint2 q = make_uint2(pack_bf16x2(acc[f][nf][grp * 4 + 0], acc[f][nf][grp * 4 + 1]),
-                                                       pack_bf16x2(acc[f][nf][grp * 4 + 2], acc[f][nf][grp * 4 + 3]));
+                            float v4[4];
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) v4[v] = acc[f][nf][grp * 4 + v];
+                            if (EPI && kl < a.Kg) {
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) v4[v] = epi_float<T>(v4[v], a.e, g * a.Kg + kl, ko + p0 + v);
+                            }
+                            const uint2 q = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
                             *reinterpret_cast<uint2*>(lds + kk * pitch + p0 * 2) = q;
                         }
                     }
@@ -1033,7 +1101,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                     typename Mma<T>::acc_t quad;
 #pragma unroll
                     for (int v = 0; v < 4; ++v) quad[v] = acc[f][nf][grp * 4 + v];
-                    if (o[f][grp] >= 0) store_out4<T>(y, o[f][grp] + coff, quad, sc);
+                    if (o[f][grp] >= 0) store_out4_epi<T, EPI>(y, o[f][grp] + coff, quad, sc, a.e, k);
                 }
         }
         return;
@@ -1056,7 +1124,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const long long ov = otab[p0 + v];
-                    if (ov >= 0) store_out<T>(y, ov + coff, quad, v, sc);
+                    if (ov >= 0) store_out_epi<T, EPI>(y, ov + coff, quad, v, sc, a.e, k);
                 }
             }
         }
@@ -1367,15 +1435,17 @@ template <typename K> cfwd_status allow_big_lds(K kern, size_t lds_bytes, bool* 
 
 // One launch of a tile config.  SPLIT: `nsplit` workgroups per tile, each
 // summing `cps` channel chunks into its partial tile in `part`.
-template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false>
+template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false,
+          bool EPI = false>
 cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
-                       hipStream_t st, int cps = 0, int nsplit = 1, int32_t* part = nullptr) {
+                       const Epi& e, hipStream_t st, int cps = 0, int nsplit = 1, int32_t* part = nullptr) {
     Args a = make_args(p, g, x, wp, scale, y);
+    a.e = e;
     if constexpr (SPLIT) {
         a.cps = cps;
         a.part = part;
     }
-    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV, SPLIT>;
+    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV, SPLIT, EPI>;
     static bool attr_done = false;
     const cfwd_status s = allow_big_lds(kern, g.lds_bytes, &attr_done);
     if (s != CFWD_OK) return s;
@@ -1384,9 +1454,9 @@ cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* w
     return check_hip(hipGetLastError(), "igemm_kernel launch");
 }
 
-template <typename T, int XB>
+template <typename T, int XB, bool EPI>
 cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale,
-                       void* y, hipStream_t st) {
+                       void* y, const Epi& e, hipStream_t st) {
     switch (cfg) {
 #define CFWD_IG_CFG(ID)                                                                                    \
     case ID: {                                                                                             \
@@ -1394,14 +1464,14 @@ cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, cons
         if constexpr (Wide<T, XB>::ok) {                                                                   \
             if (g.stg == 1) {                                                                              \
                 if (p.r * p.s == 9)                                                                        \
-                    return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9>(p, g, x, wp, scale, y, st);   \
-                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 0>(p, g, x, wp, scale, y, st);   \
+                    return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9, false, EPI>(p, g, x, wp, scale, y, e, st);   \
+                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 0, false, EPI>(p, g, x, wp, scale, y, e, st);   \
             }                                                                                              \
         }                                                                                                  \
         if constexpr (c.fr == 16)                                                                          \
             if (p.r * p.s == 9)                                                                            \
-                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 9>(p, g, x, wp, scale, y, st);   \
-        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 0>(p, g, x, wp, scale, y, st);           \
+                return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 9, false, EPI>(p, g, x, wp, scale, y, e, st);   \
+        return launch_one<T, XB, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 0, false, EPI>(p, g, x, wp, scale, y, e, st);           \
     }
         CFWD_IG_CFG(0)
         CFWD_IG_CFG(1)
@@ -1426,13 +1496,13 @@ cfwd_status launch_cfg(int cfg, const Prob& p, const Geo& g, const void* x, cons
     }
 }
 
-template <typename T>
+template <typename T, bool EPI>
 cfwd_status launch_dtype(int cfg, const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale,
-                         void* y, hipStream_t st) {
+                         void* y, const Epi& e, hipStream_t st) {
     switch (p.xb) {
-        case 1: return launch_cfg<T, 1>(cfg, p, g, x, wp, scale, y, st);
-        case 4: return launch_cfg<T, 4>(cfg, p, g, x, wp, scale, y, st);
-        case 8: return launch_cfg<T, 8>(cfg, p, g, x, wp, scale, y, st);
+        case 1: return launch_cfg<T, 1, EPI>(cfg, p, g, x, wp, scale, y, e, st);
+        case 4: return launch_cfg<T, 4, EPI>(cfg, p, g, x, wp, scale, y, e, st);
+        case 8: return launch_cfg<T, 8, EPI>(cfg, p, g, x, wp, scale, y, e, st);
         default: return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM: channel block must be 1, 4 or 8");
     }
 }
@@ -1472,17 +1542,24 @@ cfwd_status prepare_dtype(int cfg, const Prob& p, const Geo& g, const void* w, v
 
 // Per-dtype entry points (defined in k_igemm_{f32,bf16,i8}.hip).
 cfwd_status igemm_launch_f32(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
-                             const float* scale, void* y, hipStream_t st);
+                             const float* scale, void* y, const Epi& e, hipStream_t st);
 cfwd_status igemm_launch_bf16(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
-                              const float* scale, void* y, hipStream_t st);
+                              const float* scale, void* y, const Epi& e, hipStream_t st);
 cfwd_status igemm_launch_i8(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
-                            const float* scale, void* y, hipStream_t st);
+                            const float* scale, void* y, const Epi& e, hipStream_t st);
 cfwd_status igemm_prepare_f32(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st);
 cfwd_status igemm_prepare_bf16(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st);
 cfwd_status igemm_prepare_i8(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st);
+// The same with the fused epilogue compiled in (k_igemm_{f32,bf16,i8}_epi.hip).
+cfwd_status igemm_launch_f32_epi(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
+                                 const float* scale, void* y, const Epi& e, hipStream_t st);
+cfwd_status igemm_launch_bf16_epi(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
+                                  const float* scale, void* y, const Epi& e, hipStream_t st);
+cfwd_status igemm_launch_i8_epi(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
+                                const float* scale, void* y, const Epi& e, hipStream_t st);
 // Split config sc (k_igemm_i8_split.hip): the split kernel, then the reduce
 // kernel that sums the partial tiles in `part` and requantises into y.
 cfwd_status igemm_launch_i8_split(int sc, const Prob& p, const ig::Geo& g, int cps, const void* x, const void* wp,
-                                  const float* scale, void* y, void* part, hipStream_t st);
+                                  const float* scale, void* y, void* part, const Epi& e, hipStream_t st);
 
 }  // namespace cfwd

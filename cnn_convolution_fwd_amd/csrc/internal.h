@@ -30,6 +30,16 @@ struct Prob {
     bool pointwise() const { return r == 1 && s == 1 && ph == 0 && pw == 0; }
 };
 
+// Fused epilogue of one call (cfwd_epilogue): a per-output-channel bias
+// (fp32 for fp32 / bf16 outputs, int32 added to the accumulator for int8), a
+// residual in y's layout and dtype, and ReLU -- applied to each output before
+// it is converted and stored.  All null / 0: a plain convolution.
+struct Epi {
+    const void* bias = nullptr;
+    const void* res = nullptr;
+    int relu = 0;
+};
+
 // Fills *p from a descriptor; returns CFWD_OK or INVALID_ARG/UNSUPPORTED and a
 // reason in *why.
 cfwd_status make_prob(const cfwd_conv_desc* d, Prob* p, std::string* why);
@@ -50,7 +60,7 @@ int direct_num_configs();
 int direct_default_config(const Prob& p);  // fastest expected supported config
 bool direct_supported(const Prob& p, int cfg, std::string* why);
 cfwd_status direct_launch(const Prob& p, int cfg, const void* x, const void* w,
-                          const float* scale, void* y, hipStream_t st);
+                          const float* scale, void* y, const Epi& e, hipStream_t st);
 
 // Implicit GEMM on the matrix cores.
 int igemm_num_configs();
@@ -59,7 +69,7 @@ size_t igemm_filter_bytes(const Prob& p, int cfg);
 cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
 size_t igemm_scratch_bytes(const Prob& p, int cfg);  // partial tiles of split configs
 cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp,
-                         const float* scale, void* y, void* scratch, hipStream_t st);
+                         const float* scale, void* y, void* scratch, const Epi& e, hipStream_t st);
 int igemm_default_config(const Prob& p);
 // gather form of implicit GEMM for few input channels (implicit-GEMM configs
 // after the tiled ones)
@@ -68,7 +78,7 @@ bool lowc_supported(const Prob& p, int cfg, std::string* why);
 size_t lowc_filter_bytes(const Prob& p, int cfg);
 cfwd_status lowc_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
 cfwd_status lowc_launch(const Prob& p, int cfg, const void* x, const void* wp, const float* scale, void* y,
-                        hipStream_t st);
+                        const Epi& e, hipStream_t st);
 
 // Pointwise (1x1) path.
 int pointwise_num_configs();
@@ -76,7 +86,7 @@ bool pointwise_supported(const Prob& p, int cfg, std::string* why);
 size_t pointwise_filter_bytes(const Prob& p, int cfg);
 cfwd_status pointwise_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
 cfwd_status pointwise_launch(const Prob& p, int cfg, const void* x, const void* wp,
-                             const float* scale, void* y, hipStream_t st);
+                             const float* scale, void* y, const Epi& e, hipStream_t st);
 
 // Winograd F(m x m, 3 x 3), m = 2 or 6.
 int winograd_num_configs(int m);
@@ -85,14 +95,15 @@ size_t winograd_filter_bytes(const Prob& p, int m, int cfg);
 size_t winograd_scratch_bytes(const Prob& p, int m, int cfg);  // transformed input U
 cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st);
 cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch,
-                            void* y, hipStream_t st);
+                            void* y, const Epi& e, hipStream_t st);
 
 // Fused Winograd F(2x2,3x3) for bf16 NCHW (configs 1 and 2 of F(2x2)): the
 // transformed input stays on chip, no scratch.
 bool winograd_fused_supported(const Prob& p, int cfg, std::string* why);
 size_t winograd_fused_filter_bytes(const Prob& p, int cfg);
 cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
-cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, hipStream_t st);
+cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, const Epi& e,
+                                  hipStream_t st);
 
 // Writes 0 to the NCHWX output channels past K (no-op unless K % xb != 0).
 cfwd_status zero_output_channel_padding(const Prob& p, void* y, hipStream_t st);
@@ -181,6 +192,25 @@ __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uin
     return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
+// ---- fused epilogue, one output value (see Epi)
+
+// fp32 / bf16 outputs: act(v + bias[k] + residual[off]) in fp32, before the
+// single conversion to the output type.  k must be a real channel (< K).
+template <typename T>
+__device__ __forceinline__ float epi_float(float v, const Epi& e, int k, long long off);
+
+// int8 outputs: clamp(rne(fp32(acc + bias[k]) * scale + fp32(residual[off])),
+// lo, 127), lo = 0 under ReLU, else -127; the value in the low byte, as in
+// requant_i8_bits (which this equals with no bias, residual or ReLU).  k
+// must be a real channel (< K) when there is a bias.
+__device__ __forceinline__ uint32_t requant_i8_epi_bits(int acc, float scale, const Epi& e, int k, long long off) {
+    if (e.bias) acc += static_cast<const int32_t*>(e.bias)[k];
+    float q = __fmul_rn(static_cast<float>(acc), scale);
+    if (e.res) q = __fadd_rn(q, static_cast<float>(static_cast<const int8_t*>(e.res)[off]));
+    q = __builtin_amdgcn_fmed3f(q, e.relu ? 0.0f : -127.0f, 127.0f);
+    return __float_as_uint(__fadd_rn(q, 12582912.0f));
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
     static __device__ __forceinline__ float to_f(float v) { return v; }
@@ -191,6 +221,14 @@ template <> struct Elem<bf16_t> {
 template <> struct Elem<int8_t> {
     static __device__ __forceinline__ int to_f(int8_t v) { return v; }
 };
+
+template <typename T>
+__device__ __forceinline__ float epi_float(float v, const Epi& e, int k, long long off) {
+    if (e.bias) v += static_cast<const float*>(e.bias)[k];
+    if (e.res) v += static_cast<float>(Elem<T>::to_f(static_cast<const T*>(e.res)[off]));
+    if (e.relu) v = fmaxf(v, 0.0f);
+    return v;
+}
 
 // Offset of activation element (c, h, w) inside one image.
 template <int XB>

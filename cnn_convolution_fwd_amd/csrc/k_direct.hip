@@ -28,6 +28,7 @@ namespace {
 struct DirectArgs {
     int N, C, H, W, K, OH, OW, Cg, Kg, R, S, sh, sw, ph, pw, dh, dw;
     long long x_img, y_img;
+    Epi e;  // fused epilogue
 };
 
 template <typename T> __device__ __forceinline__ T store_cast(float v);
@@ -64,7 +65,8 @@ __global__ __launch_bounds__(256) void direct_generic(const T* __restrict__ x, c
                 }
             }
         }
-        y[n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW)] = store_cast<T>(acc);
+        const long long o = n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW);
+        y[o] = store_cast<T>(epi_float<T>(acc, a.e, k, o));
     }
 }
 
@@ -96,7 +98,8 @@ __global__ __launch_bounds__(256) void direct_generic_i8(const int8_t* __restric
                 }
             }
         }
-        y[n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW)] = requant_i8(acc, scale[k]);
+        const long long o = n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW);
+        y[o] = static_cast<int8_t>(requant_i8_epi_bits(acc, scale[k], a.e, k, o));
     }
 }
 
@@ -180,11 +183,13 @@ template <typename T, int NW> constexpr int dw_vpt() { return NW * Words<T>::PER
 // clamped (in bounds) and zeroed with selects; threads past the last strip
 // work on a clamped strip and store nothing.  Outputs are written with
 // streaming (non-temporal) stores.
-template <typename T, int RB, int NW>
+// EPI: the fused epilogue compiled in (a separate instantiation, so the
+// plain kernels carry none of its registers).
+template <typename T, int RB, int NW, bool EPI>
 __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, const T* __restrict__ w,
                                                        T* __restrict__ y, int C, int H, int W, long long x_img,
                                                        long long y_img, int cols, int bands, int strips, int spb,
-                                                       FastDiv fd_cols, FastDiv fd_bands, FastDiv fd_c) {
+                                                       FastDiv fd_cols, FastDiv fd_bands, FastDiv fd_c, Epi ep) {
     using WD = Words<T>;
     constexpr int V = dw_vpt<T, NW>();
     __shared__ uint32_t first_w[RB + 2][256], last_w[RB + 2][256];
@@ -294,6 +299,19 @@ __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, 
             }
         }
         if (valid && oh < H) {
+            // fused epilogue: bias, residual (the same vector of the
+            // residual tensor), ReLU, before the one conversion
+            if constexpr (EPI) {
+                uint32_t rr[NW];
+                if (ep.res) RawVec<NW>::load(static_cast<const T*>(ep.res) + (yp - y) + (oh * W + ow0), rr);
+                const float b = ep.bias ? static_cast<const float*>(ep.bias)[c] : 0.0f;
+#pragma unroll
+                for (int e = 0; e < V; ++e) {
+                    float v = out[e] + b;
+                    if (ep.res) v += WD::elem(rr, e);
+                    out[e] = ep.relu ? fmaxf(v, 0.0f) : v;
+                }
+            }
             uint32_t o[NW];
 #pragma unroll
             for (int q = 0; q < NW; ++q) o[q] = WD::pack(out, q);
@@ -302,8 +320,9 @@ __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, 
     }
 }
 
-DirectArgs make_args(const Prob& p) {
+DirectArgs make_args(const Prob& p, const Epi& e) {
     DirectArgs a;
+    a.e = e;
     a.N = p.n; a.C = p.c; a.H = p.h; a.W = p.w; a.K = p.k; a.OH = p.oh; a.OW = p.ow;
     a.Cg = p.cg; a.Kg = p.kg; a.R = p.r; a.S = p.s;
     a.sh = p.sh; a.sw = p.sw; a.ph = p.ph; a.pw = p.pw; a.dh = p.dh; a.dw = p.dw;
@@ -344,7 +363,8 @@ bool depthwise_fast_ok(const Prob& p, int cfg, std::string* why) {
 }
 
 template <typename T, int RB, int NW>
-cfwd_status launch_dw(const Prob& p, const void* x, const void* w, void* y, hipStream_t st) {
+cfwd_status launch_dw(const Prob& p, const void* x, const void* w, void* y, const Epi& e, hipStream_t st) {
+    const bool epi = e.bias || e.res || e.relu;
     constexpr int V = dw_vpt<T, NW>();
     const int cols = p.w / V;
     const int bands = (p.oh + RB - 1) / RB;
@@ -352,22 +372,23 @@ cfwd_status launch_dw(const Prob& p, const void* x, const void* w, void* y, hipS
     const int spb = 256 / cols;  // whole strips per workgroup (cols <= 256 is checked)
     if (strips >= (1LL << 31)) return set_error(CFWD_ERR_UNSUPPORTED, "depthwise: too many strips");
     const unsigned blocks = static_cast<unsigned>((strips + spb - 1) / spb);
-    depthwise3x3_s1<T, RB, NW><<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const T*>(w),
-                                                     static_cast<T*>(y), p.c, p.h, p.w, p.x_img, p.y_img, cols,
-                                                     bands, static_cast<int>(strips), spb, make_fastdiv(cols),
-                                                     make_fastdiv(bands), make_fastdiv(p.c));
+    auto kern = epi ? depthwise3x3_s1<T, RB, NW, true> : depthwise3x3_s1<T, RB, NW, false>;
+    kern<<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const T*>(w), static_cast<T*>(y), p.c, p.h,
+                                 p.w, p.x_img, p.y_img, cols, bands, static_cast<int>(strips), spb,
+                                 make_fastdiv(cols), make_fastdiv(bands), make_fastdiv(p.c), e);
     return check_hip(hipGetLastError(), "depthwise3x3_s1 launch");
 }
 
 template <typename T>
-cfwd_status launch_dw_cfg(const Prob& p, int cfg, const void* x, const void* w, void* y, hipStream_t st) {
+cfwd_status launch_dw_cfg(const Prob& p, int cfg, const void* x, const void* w, void* y, const Epi& e,
+                          hipStream_t st) {
     switch (cfg) {
-        case 1: return launch_dw<T, 1, 4>(p, x, w, y, st);
-        case 2: return launch_dw<T, 2, 4>(p, x, w, y, st);
-        case 3: return launch_dw<T, 4, 4>(p, x, w, y, st);
-        case 4: return launch_dw<T, 8, 4>(p, x, w, y, st);
-        case 5: return launch_dw<T, 2, 2>(p, x, w, y, st);
-        default: return launch_dw<T, 4, 2>(p, x, w, y, st);
+        case 1: return launch_dw<T, 1, 4>(p, x, w, y, e, st);
+        case 2: return launch_dw<T, 2, 4>(p, x, w, y, e, st);
+        case 3: return launch_dw<T, 4, 4>(p, x, w, y, e, st);
+        case 4: return launch_dw<T, 8, 4>(p, x, w, y, e, st);
+        case 5: return launch_dw<T, 2, 2>(p, x, w, y, e, st);
+        default: return launch_dw<T, 4, 2>(p, x, w, y, e, st);
     }
 }
 
@@ -389,11 +410,11 @@ bool direct_supported(const Prob& p, int cfg, std::string* why) {
 }
 
 cfwd_status direct_launch(const Prob& p, int cfg, const void* x, const void* w, const float* scale, void* y,
-                          hipStream_t st) {
-    const DirectArgs a = make_args(p);
+                          const Epi& e, hipStream_t st) {
+    const DirectArgs a = make_args(p, e);
     if (cfg >= 1 && cfg <= 6) {
-        if (p.dtype == CFWD_F32) return launch_dw_cfg<float>(p, cfg, x, w, y, st);
-        return launch_dw_cfg<bf16_t>(p, cfg, x, w, y, st);
+        if (p.dtype == CFWD_F32) return launch_dw_cfg<float>(p, cfg, x, w, y, e, st);
+        return launch_dw_cfg<bf16_t>(p, cfg, x, w, y, e, st);
     }
     const long long total = static_cast<long long>(p.n) * p.k * p.oh * p.ow;
     const unsigned blocks = grid_for(total);

@@ -57,21 +57,30 @@ cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipSt
 }
 
 cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp, const float* scale, void* y,
-                         void* scratch, hipStream_t st) {
-    if (is_lowc(cfg)) return lowc_launch(p, cfg - ig::kNumCfgs, x, wp, scale, y, st);
+                         void* scratch, const Epi& e, hipStream_t st) {
+    if (is_lowc(cfg)) return lowc_launch(p, cfg - ig::kNumCfgs, x, wp, scale, y, e, st);
     ig::Geo g;
     std::string why;
     if (is_split(cfg)) {
         int cps;
         if (!ig::split_geometry(p, cfg - split_first(), &g, &cps, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
         if (scratch == nullptr) return set_error(CFWD_ERR_WORKSPACE, "implicit GEMM split reduction needs scratch");
-        return igemm_launch_i8_split(cfg - split_first(), p, g, cps, x, wp, scale, y, scratch, st);
+        return igemm_launch_i8_split(cfg - split_first(), p, g, cps, x, wp, scale, y, scratch, e, st);
     }
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    // the fused epilogue has instantiations of its own (no registers of it
+    // in the plain kernels)
+    const bool epi = e.bias || e.res || e.relu;
     switch (p.dtype) {
-        case CFWD_F32: return igemm_launch_f32(cfg, p, g, x, wp, scale, y, st);
-        case CFWD_BF16: return igemm_launch_bf16(cfg, p, g, x, wp, scale, y, st);
-        default: return igemm_launch_i8(cfg, p, g, x, wp, scale, y, st);
+        case CFWD_F32:
+            return epi ? igemm_launch_f32_epi(cfg, p, g, x, wp, scale, y, e, st)
+                       : igemm_launch_f32(cfg, p, g, x, wp, scale, y, e, st);
+        case CFWD_BF16:
+            return epi ? igemm_launch_bf16_epi(cfg, p, g, x, wp, scale, y, e, st)
+                       : igemm_launch_bf16(cfg, p, g, x, wp, scale, y, e, st);
+        default:
+            return epi ? igemm_launch_i8_epi(cfg, p, g, x, wp, scale, y, e, st)
+                       : igemm_launch_i8(cfg, p, g, x, wp, scale, y, e, st);
     }
 }
 

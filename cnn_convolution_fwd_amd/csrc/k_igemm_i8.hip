@@ -4,8 +4,8 @@
 namespace cfwd {
 
 cfwd_status igemm_launch_i8(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
-                             const float* scale, void* y, hipStream_t st) {
-    return ig::launch_dtype<int8_t>(cfg, p, g, x, wp, scale, y, st);
+                             const float* scale, void* y, const Epi& e, hipStream_t st) {
+    return ig::launch_dtype<int8_t, false>(cfg, p, g, x, wp, scale, y, e, st);
 }
 
 cfwd_status igemm_prepare_i8(int cfg, const Prob& p, const ig::Geo& g, const void* w, void* wp, hipStream_t st) {

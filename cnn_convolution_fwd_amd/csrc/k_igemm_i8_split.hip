@@ -24,7 +24,7 @@ namespace {
 // take scale 0, which writes the zero bytes NCHW4 keeps in its padding.
 __global__ __launch_bounds__(256) void split_reduce_i8(const int4* __restrict__ part, const float* __restrict__ scale,
                                                        uint32_t* __restrict__ y, int n4, int S, int OHW, int KB,
-                                                       int K) {
+                                                       int K, Epi ep) {
     const int i = static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x);
     if (i >= n4) return;
     int4 acc = part[i];
@@ -44,6 +44,16 @@ __global__ __launch_bounds__(256) void split_reduce_i8(const int4* __restrict__ 
         const float v = scale[ok ? k0 + c : 0];  // no branch around the load
         sc[c] = ok ? v : 0.0f;
     }
+    if (ep.bias || ep.res || ep.relu) {
+        // fused epilogue; channels past K take the last real channel's bias
+        // (their scale is 0 and they are zeroed afterwards)
+        const long long o = 4LL * i;
+        y[i] = pack_low_bytes(requant_i8_epi_bits(acc.x, sc[0], ep, min(k0, K - 1), o),
+                              requant_i8_epi_bits(acc.y, sc[1], ep, min(k0 + 1, K - 1), o + 1),
+                              requant_i8_epi_bits(acc.z, sc[2], ep, min(k0 + 2, K - 1), o + 2),
+                              requant_i8_epi_bits(acc.w, sc[3], ep, min(k0 + 3, K - 1), o + 3));
+        return;
+    }
     y[i] = pack_low_bytes(requant_i8_bits(acc.x, sc[0]), requant_i8_bits(acc.y, sc[1]),
                           requant_i8_bits(acc.z, sc[2]), requant_i8_bits(acc.w, sc[3]));
 }
@@ -51,7 +61,7 @@ __global__ __launch_bounds__(256) void split_reduce_i8(const int4* __restrict__ 
 }  // namespace
 
 cfwd_status igemm_launch_i8_split(int sc, const Prob& p, const ig::Geo& g, int cps, const void* x, const void* wp,
-                                  const float* scale, void* y, void* part, hipStream_t st) {
+                                  const float* scale, void* y, void* part, const Epi& e, hipStream_t st) {
     using namespace ig;
     const int base = kSplitCfgs[sc].base;
     const int nsplit = kSplitCfgs[sc].splits;
@@ -63,16 +73,16 @@ cfwd_status igemm_launch_i8_split(int sc, const Prob& p, const ig::Geo& g, int c
         constexpr Cfg c = kCfgs[ID];                                                                             \
         if (g.stg == 1) {                                                                                        \
             if (p.r * p.s == 9)                                                                                  \
-                s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9, true>(p, g, x, wp, scale, y, st, cps, \
+                s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 9, true>(p, g, x, wp, scale, y, Epi{}, st, cps, \
                                                                                     nsplit, pt);                 \
             else                                                                                                 \
-                s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 0, true>(p, g, x, wp, scale, y, st, cps, \
+                s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 1, c.fr, 0, true>(p, g, x, wp, scale, y, Epi{}, st, cps, \
                                                                                     nsplit, pt);                 \
         } else if (c.fr == 16 && p.r * p.s == 9) {                                                               \
             s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 0, c.fr, (c.fr == 16 ? 9 : 0), true>(              \
-                p, g, x, wp, scale, y, st, cps, nsplit, pt);                                                     \
+                p, g, x, wp, scale, y, Epi{}, st, cps, nsplit, pt);                                                     \
         } else {                                                                                                 \
-            s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 0, true>(p, g, x, wp, scale, y, st, cps,  \
+            s = launch_one<int8_t, 4, c.wm, c.wn, c.fm, c.fn, 0, c.fr, 0, true>(p, g, x, wp, scale, y, Epi{}, st, cps,  \
                                                                                 nsplit, pt);                     \
         }                                                                                                        \
         break;                                                                                                   \
@@ -92,7 +102,7 @@ cfwd_status igemm_launch_i8_split(int sc, const Prob& p, const ig::Geo& g, int c
     const int KB = static_cast<int>(p.y_img / (4LL * OHW));
     const int n4 = static_cast<int>(static_cast<long long>(p.n) * p.y_img / 4);
     split_reduce_i8<<<(n4 + 255) / 256, 256, 0, st>>>(reinterpret_cast<const int4*>(pt), scale,
-                                                     static_cast<uint32_t*>(y), n4, nsplit, OHW, KB, p.k);
+                                                     static_cast<uint32_t*>(y), n4, nsplit, OHW, KB, p.k, e);
     return check_hip(hipGetLastError(), "split_reduce_i8 launch");
 }
 

@@ -55,6 +55,7 @@ struct LcArgs {
     // staged fp32/bf16: element offset of a zero-filled region of ROWS * RW
     // elements after the staged rows, read by the reduction's padding units
     int zoff;
+    Epi e;  // fused epilogue
 };
 
 struct Tap {
@@ -145,7 +146,9 @@ constexpr int lc_tile_bytes() {
 
 // Workgroup: 4 waves = (4 / KW) pixel groups x KW k groups; a wave owns NCB
 // columns blocks of 32 pixels x KBW blocks of 32 output channels.
-template <typename T, int XB, int NCB, int KBW, bool STG>
+// EPI: the fused epilogue compiled in (a separate instantiation, so the
+// plain kernels carry none of its registers).
+template <typename T, int XB, int NCB, int KBW, bool STG, bool EPI>
 __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const uint8_t* __restrict__ wp,
                                                  const float* __restrict__ scale, T* __restrict__ y, LcArgs a) {
     using L = Lc<T>;
@@ -369,10 +372,17 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                     for (int v = 0; v < 16; ++v) {
                         const int cl = (wk * KBW + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
                         uint8_t* d = otile + cl * pitch + pl * E;
+                        float val = acc[b][cb][v];
+                        if constexpr (EPI) {  // fused epilogue, before the conversion
+                            const int k = kg * a.KW * KBW * 32 + cl;
+                            if (k < a.K && pok[cb])
+                                val = epi_float<T>(val, a.e, k,
+                                                   pn[cb] * a.y_img + static_cast<long long>(k) * ohw + ppix[cb]);
+                        }
                         if constexpr (sizeof(T) == 4)
-                            *reinterpret_cast<float*>(d) = acc[b][cb][v];
+                            *reinterpret_cast<float*>(d) = val;
                         else
-                            *reinterpret_cast<uint16_t*>(d) = float_to_bf16(acc[b][cb][v]);
+                            *reinterpret_cast<uint16_t*>(d) = float_to_bf16(val);
                     }
                 }
         }
@@ -467,9 +477,23 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                     const int k0 = (kb0 + b) * 32 + 8 * q + 4 * h;
                     if (k0 >= a.K) continue;
                     const typename L::Acc& ac = acc[b][cb];
-                    const uint32_t word = pack_low_bytes(
-                        requant_i8_bits(ac[4 * q], sc[b][4 * q]), requant_i8_bits(ac[4 * q + 1], sc[b][4 * q + 1]),
-                        requant_i8_bits(ac[4 * q + 2], sc[b][4 * q + 2]), requant_i8_bits(ac[4 * q + 3], sc[b][4 * q + 3]));
+                    uint32_t word;
+                    if constexpr (EPI) {
+                        // fused epilogue; channels past K (scale 0, zeroed
+                        // afterwards) read the last real channel's bias
+                        const long long o0 = n * a.y_img + (static_cast<long long>(k0 / 4) * ohw + pix) * 4;
+                        uint32_t qb[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            qb[i] = requant_i8_epi_bits(ac[4 * q + i], sc[b][4 * q + i], a.e, min(k0 + i, a.K - 1),
+                                                        o0 + i);
+                        word = pack_low_bytes(qb[0], qb[1], qb[2], qb[3]);
+                    } else {
+                        word = pack_low_bytes(
+                            requant_i8_bits(ac[4 * q], sc[b][4 * q]), requant_i8_bits(ac[4 * q + 1], sc[b][4 * q + 1]),
+                            requant_i8_bits(ac[4 * q + 2], sc[b][4 * q + 2]),
+                            requant_i8_bits(ac[4 * q + 3], sc[b][4 * q + 3]));
+                    }
                     *reinterpret_cast<uint32_t*>(yb + (b * 8 + 2 * q) * ohw4) = word;
                 }
             } else {
@@ -477,11 +501,13 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                 for (int v = 0; v < 16; ++v) {
                     const int k = (kb0 + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
                     if (k >= a.K) continue;
-                    T* dst = y + n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW);
+                    const long long o = n * a.y_img + act_off<XB>(k, oh, ow, a.OH, a.OW);
+                    T* dst = y + o;
+                    const float val = EPI ? epi_float<T>(acc[b][cb][v], a.e, k, o) : acc[b][cb][v];
                     if constexpr (sizeof(T) == 4)
-                        *dst = acc[b][cb][v];
+                        *dst = val;
                     else
-                        dst->bits = float_to_bf16(acc[b][cb][v]);
+                        dst->bits = float_to_bf16(val);
                 }
             }
         }
@@ -581,18 +607,21 @@ template <typename T, int XB, int NCB, int KBW>
 void lc_launch_cfg(bool staged, unsigned blocks, const LcArgs& b, const T* xt, const uint8_t* w8, const float* scale,
                    T* yt, hipStream_t st) {
     const size_t lds = lc_lds_bytes<T, XB, NCB, KBW>(b);
+    const bool epi = b.e.bias || b.e.res || b.e.relu;
     if constexpr (sizeof(T) == 1 || XB == 1) {
         if (staged) {
-            lc_kernel<T, XB, NCB, KBW, true><<<blocks, 256, lds, st>>>(xt, w8, scale, yt, b);
+            auto kern = epi ? lc_kernel<T, XB, NCB, KBW, true, true> : lc_kernel<T, XB, NCB, KBW, true, false>;
+            kern<<<blocks, 256, lds, st>>>(xt, w8, scale, yt, b);
             return;
         }
     }
-    lc_kernel<T, XB, NCB, KBW, false><<<blocks, 256, lds, st>>>(xt, w8, scale, yt, b);
+    auto kern = epi ? lc_kernel<T, XB, NCB, KBW, false, true> : lc_kernel<T, XB, NCB, KBW, false, false>;
+    kern<<<blocks, 256, lds, st>>>(xt, w8, scale, yt, b);
 }
 
 template <typename T, int XB>
 cfwd_status lc_launch_t(int cfg, const LcArgs& a, const void* x, const void* wp, const float* scale, void* y,
-                        hipStream_t st) {
+                        const Epi& e, hipStream_t st) {
     const bool staged = cfg >= kLcBase;
     cfg %= kLcBase;
     const long long per_wg = static_cast<long long>(4 / a.KW) * kLc[cfg].ncb * 32;
@@ -603,6 +632,7 @@ cfwd_status lc_launch_t(int cfg, const LcArgs& a, const void* x, const void* wp,
     // 16-byte output pieces start at pixel multiples of 16 / sizeof(T) of a
     // channel plane: aligned when the planes and the tensor are
     LcArgs b = a;
+    b.e = e;
     const long long pe = 16 / static_cast<long long>(sizeof(T));
     b.vec_ok = (reinterpret_cast<uintptr_t>(y) % 16 == 0) && (static_cast<long long>(a.OH) * a.OW) % pe == 0 &&
                a.y_img % pe == 0;
@@ -619,11 +649,11 @@ cfwd_status lc_launch_t(int cfg, const LcArgs& a, const void* x, const void* wp,
 
 template <typename T>
 cfwd_status lc_launch_layout(const Prob& p, int cfg, const LcArgs& a, const void* x, const void* wp,
-                             const float* scale, void* y, hipStream_t st) {
+                             const float* scale, void* y, const Epi& e, hipStream_t st) {
     switch (p.xb) {
-        case 1: return lc_launch_t<T, 1>(cfg, a, x, wp, scale, y, st);
-        case 4: return lc_launch_t<T, 4>(cfg, a, x, wp, scale, y, st);
-        case 8: return lc_launch_t<T, 8>(cfg, a, x, wp, scale, y, st);
+        case 1: return lc_launch_t<T, 1>(cfg, a, x, wp, scale, y, e, st);
+        case 4: return lc_launch_t<T, 4>(cfg, a, x, wp, scale, y, e, st);
+        case 8: return lc_launch_t<T, 8>(cfg, a, x, wp, scale, y, e, st);
         default: return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM (gather): bad channel block");
     }
 }
@@ -664,14 +694,14 @@ cfwd_status lowc_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStr
 }
 
 cfwd_status lowc_launch(const Prob& p, int cfg, const void* x, const void* wp, const float* scale, void* y,
-                        hipStream_t st) {
+                        const Epi& e, hipStream_t st) {
     LcArgs a;
     std::string why;
     if (!lc_geometry(p, cfg, &a, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (wp == nullptr) return set_error(CFWD_ERR_WORKSPACE, "implicit GEMM (gather): prepared filter required");
-    if (p.dtype == CFWD_F32) return lc_launch_layout<float>(p, cfg, a, x, wp, scale, y, st);
-    if (p.dtype == CFWD_BF16) return lc_launch_layout<bf16_t>(p, cfg, a, x, wp, scale, y, st);
-    return lc_launch_t<int8_t, 4>(cfg, a, x, wp, scale, y, st);
+    if (p.dtype == CFWD_F32) return lc_launch_layout<float>(p, cfg, a, x, wp, scale, y, e, st);
+    if (p.dtype == CFWD_BF16) return lc_launch_layout<bf16_t>(p, cfg, a, x, wp, scale, y, e, st);
+    return lc_launch_t<int8_t, 4>(cfg, a, x, wp, scale, y, e, st);
 }
 
 }  // namespace cfwd

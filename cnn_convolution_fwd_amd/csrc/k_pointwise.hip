@@ -100,11 +100,13 @@ __global__ __launch_bounds__(256) void pw_prepare_kernel(const T* __restrict__ w
 
 // Workgroup: 4 waves = (4 / KW) pixel blocks x KW k groups; a wave owns 128
 // pixels x KBW blocks of 32 output channels.  Grid: pixel groups x k groups.
-template <typename T, int KBW>
+// EPI: the fused epilogue compiled in (a separate instantiation, so the
+// plain kernels carry none of its registers).
+template <typename T, int KBW, bool EPI>
 __global__ __launch_bounds__(256) void pw_kernel(const T* __restrict__ x, const uint8_t* __restrict__ wp,
                                                  T* __restrict__ y, int C, int K, int HW, long long x_img,
                                                  long long y_img, long long npix, int nsteps, int nkb, int KW,
-                                                 int ngk) {
+                                                 int ngk, Epi ep) {
     using P = PwT<T>;
     using XV = typename P::XV;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -183,7 +185,12 @@ __global__ __launch_bounds__(256) void pw_kernel(const T* __restrict__ x, const 
         for (int v = 0; v < 16; ++v) {
             const int k = (kb0 + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
             if (k < K) {
-                const float o[4] = {acc[b][0][v], acc[b][1][v], acc[b][2][v], acc[b][3][v]};
+                float o[4] = {acc[b][0][v], acc[b][1][v], acc[b][2][v], acc[b][3][v]};
+                if constexpr (EPI) {
+                    const long long off = (yb - y) + static_cast<long long>(k) * HW;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[i] = epi_float<T>(o[i], ep, k, off + i);
+                }
                 P::store4(yb + static_cast<long long>(k) * HW, o);
             }
         }
@@ -226,18 +233,16 @@ bool geometry(const Prob& p, int cfg, PwGeo* g, std::string* why) {
 }
 
 template <typename T>
-cfwd_status launch_t(const Prob& p, int cfg, const PwGeo& g, const void* x, const void* wp, void* y,
+cfwd_status launch_t(const Prob& p, int cfg, const PwGeo& g, const void* x, const void* wp, void* y, const Epi& e,
                      hipStream_t st) {
     const unsigned blocks = static_cast<unsigned>(g.pgroups * g.ngk);
     const long long hw = static_cast<long long>(p.h) * p.w;
-    if (kKBW[cfg] == 2)
-        pw_kernel<T, 2><<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const uint8_t*>(wp),
-                                                static_cast<T*>(y), p.c, p.k, static_cast<int>(hw), p.x_img, p.y_img,
-                                                g.npix, g.nsteps, g.nkb, g.KW, g.ngk);
-    else
-        pw_kernel<T, 1><<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const uint8_t*>(wp),
-                                                static_cast<T*>(y), p.c, p.k, static_cast<int>(hw), p.x_img, p.y_img,
-                                                g.npix, g.nsteps, g.nkb, g.KW, g.ngk);
+    const bool epi = e.bias || e.res || e.relu;
+    auto kern = (kKBW[cfg] == 2) ? (epi ? pw_kernel<T, 2, true> : pw_kernel<T, 2, false>)
+                                 : (epi ? pw_kernel<T, 1, true> : pw_kernel<T, 1, false>);
+    kern<<<blocks, 256, 0, st>>>(static_cast<const T*>(x), static_cast<const uint8_t*>(wp), static_cast<T*>(y), p.c,
+                                 p.k, static_cast<int>(hw), p.x_img, p.y_img, g.npix, g.nsteps, g.nkb, g.KW, g.ngk,
+                                 e);
     return check_hip(hipGetLastError(), "pointwise launch");
 }
 
@@ -272,13 +277,13 @@ cfwd_status pointwise_prepare(const Prob& p, int cfg, const void* w, void* wp, h
 }
 
 cfwd_status pointwise_launch(const Prob& p, int cfg, const void* x, const void* wp, const float*, void* y,
-                             hipStream_t st) {
+                             const Epi& e, hipStream_t st) {
     PwGeo g;
     std::string why;
     if (!geometry(p, cfg, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (wp == nullptr) return set_error(CFWD_ERR_WORKSPACE, "pointwise: prepared filter required");
-    if (p.dtype == CFWD_F32) return launch_t<float>(p, cfg, g, x, wp, y, st);
-    return launch_t<bf16_t>(p, cfg, g, x, wp, y, st);
+    if (p.dtype == CFWD_F32) return launch_t<float>(p, cfg, g, x, wp, y, e, st);
+    return launch_t<bf16_t>(p, cfg, g, x, wp, y, e, st);
 }
 
 }  // namespace cfwd

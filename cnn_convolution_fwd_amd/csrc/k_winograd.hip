@@ -287,10 +287,10 @@ template <int M> struct GemmGeo {
     static constexpr int NTHR = NW * 64;
 };
 
-template <typename T, int XB, int M>
+template <typename T, int XB, int M, bool EPI>  // EPI: fused epilogue compiled in
 __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* __restrict__ U, const uint8_t* __restrict__ V,
                                                    T* __restrict__ y, int K, int OH, int OW, long long y_img, int th,
-                                                   int tw, int T_, int Tpad, int nchunks, int ntk) {
+                                                   int tw, int T_, int Tpad, int nchunks, int ntk, Epi ep) {
     constexpr int A = M + 2;
     constexpr int XI = A * A;
     constexpr int NW = GemmGeo<M>::NW;
@@ -430,7 +430,9 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
                             const float c = static_cast<float>(mt.at[j][q]);
                             if (c != 0.0f) s = fmaf(t[i][q], c, s);
                         }
-                        T* dst = y + n * y_img + act_off<XB>(k, oh, ow, OH, OW);
+                        const long long o = n * y_img + act_off<XB>(k, oh, ow, OH, OW);
+                        T* dst = y + o;
+                        if constexpr (EPI) s = epi_float<T>(s, ep, k, o);  // fused epilogue
                         if constexpr (sizeof(T) == 4)
                             *dst = s;
                         else
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
 }
 
 template <typename T, int XB, int M>
-cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y,
+cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y, const Epi& e,
                      hipStream_t st) {
     {
         using O = typename OpT<T>::type;
@@ -469,28 +471,29 @@ cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vpr
     constexpr int TB = (M == 6) ? 32 : 64;
     constexpr int KS = (M == 6) ? 8 : 16;
     const size_t lds = static_cast<size_t>(A * A) * TB * KS * 4;
-    auto kern = gemm_kernel<T, XB, M>;
-    static bool attr = false;
-    if (lds > 65536 && !attr) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return check_hip(e, "hipFuncSetAttribute(winograd gemm)");
-        attr = true;
+    const bool epi = e.bias || e.res || e.relu;
+    auto kern = epi ? gemm_kernel<T, XB, M, true> : gemm_kernel<T, XB, M, false>;
+    static bool attr[2] = {false, false};
+    if (lds > 65536 && !attr[epi]) {
+        hipError_t he = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (he != hipSuccess) return check_hip(he, "hipFuncSetAttribute(winograd gemm)");
+        attr[epi] = true;
     }
     const unsigned blocks = static_cast<unsigned>(g.ntb * g.ntk);
     kern<<<blocks, GemmGeo<M>::NTHR, lds, st>>>(static_cast<const uint8_t*>(ubuf), static_cast<const uint8_t*>(vprep),
                                    static_cast<T*>(y), p.k, p.oh, p.ow, p.y_img, g.th, g.tw, g.T, g.Tpad, g.nchunks,
-                                   g.ntk);
+                                   g.ntk, e);
     return check_hip(hipGetLastError(), "winograd gemm launch");
 }
 
 template <typename T, int M>
-cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y,
+cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y, const Epi& e,
                      hipStream_t st) {
     switch (p.xb) {
-        case 1: return launch_t<T, 1, M>(p, g, x, vprep, ubuf, y, st);
-        case 4: return launch_t<T, 4, M>(p, g, x, vprep, ubuf, y, st);
-        case 8: return launch_t<T, 8, M>(p, g, x, vprep, ubuf, y, st);
+        case 1: return launch_t<T, 1, M>(p, g, x, vprep, ubuf, y, e, st);
+        case 4: return launch_t<T, 4, M>(p, g, x, vprep, ubuf, y, e, st);
+        case 8: return launch_t<T, 8, M>(p, g, x, vprep, ubuf, y, e, st);
         default: return set_error(CFWD_ERR_UNSUPPORTED, "winograd: bad channel block");
     }
 }
@@ -559,18 +562,18 @@ cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void*
 }
 
 cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch, void* y,
-                            hipStream_t st) {
-    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_launch(p, cfg, x, wp, y, st);
+                            const Epi& e, hipStream_t st) {
+    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_launch(p, cfg, x, wp, y, e, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (scratch == nullptr || wp == nullptr)
         return set_error(CFWD_ERR_WORKSPACE, "winograd: prepared filter and scratch are required");
     if (p.dtype == CFWD_F32)
-        return (m == 2) ? wg::launch_m<float, 2>(p, g, x, wp, scratch, y, st)
-                        : wg::launch_m<float, 6>(p, g, x, wp, scratch, y, st);
-    return (m == 2) ? wg::launch_m<bf16_t, 2>(p, g, x, wp, scratch, y, st)
-                    : wg::launch_m<bf16_t, 6>(p, g, x, wp, scratch, y, st);
+        return (m == 2) ? wg::launch_m<float, 2>(p, g, x, wp, scratch, y, e, st)
+                        : wg::launch_m<float, 6>(p, g, x, wp, scratch, y, e, st);
+    return (m == 2) ? wg::launch_m<bf16_t, 2>(p, g, x, wp, scratch, y, e, st)
+                    : wg::launch_m<bf16_t, 6>(p, g, x, wp, scratch, y, e, st);
 }
 
 }  // namespace cfwd

@@ -114,7 +114,16 @@ struct Args {
     long long x_img, y_img;
     int tbh, tbw, ntk, nchunks;
     int nblk;  // 8-column load blocks per patch row
+    Epi e;     // fused epilogue
 };
+
+// Fused epilogue (bias, residual, ReLU) on 8 consecutive outputs of channel
+// k starting at element offset `off`, of which the first nv are real.
+__device__ __forceinline__ void epi8(float* yv, const Epi& e, int k, long long off, int nv) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < nv) yv[i] = epi_float<bf16_t>(yv[i], e, k, off + i);
+}
 
 // Two bf16 (the halves of dword w) -> fp16 pair; p selects the half of each
 // source word (0: low, 1: high).
@@ -168,7 +177,9 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
-template <int TCB, int PWO>
+// EPI: the fused epilogue compiled in (a separate instantiation, so the
+// plain kernel carries none of its registers).
+template <int TCB, int PWO, bool EPI>
 __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
     using G = Geo<TCB>;
     constexpr int TR = G::TR, PUE = G::PUE, MAXU = G::MAXU;
@@ -476,7 +487,9 @@ __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
                 }
                 yv[e] = s;
             }
-            uint16_t* dst = a.y + n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
+            const long long yo = n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
+            if constexpr (EPI) epi8(yv, a.e, k, yo, a.OW - ow0);
+            uint16_t* dst = a.y + yo;
             if (vec_ok && ow0 + 8 <= a.OW) {
                 const u32x4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
                                  pack_bf16x2(yv[6], yv[7])};
@@ -503,7 +516,7 @@ __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
 // last MFMA, so it needs no second register set.
 constexpr int KB2 = 128;
 
-template <int TCB, int PWO>
+template <int TCB, int PWO, bool EPI>
 __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
     using G = Geo<TCB>;
     constexpr int TR = G::TR, PUE = G::PUE, MAXU = G::MAXU;
@@ -802,6 +815,9 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
                         if (co < 0) yv[e] -= zz[e];
                     }
                 }
+                if constexpr (EPI)
+                    epi8(yv, a.e, kt * KB2 + hb * 64 + kl,
+                         (ybase - a.y) + static_cast<long long>(kl) * a.OH * a.OW + pc * 8, 8);
                 const u32x4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
                                  pack_bf16x2(yv[6], yv[7])};
                 __builtin_nontemporal_store(
@@ -844,7 +860,9 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
                     }
                     yv[e] = s;
                 }
-                uint16_t* dst = a.y + n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
+                const long long yo = n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
+                if constexpr (EPI) epi8(yv, a.e, k, yo, a.OW - ow0);
+                uint16_t* dst = a.y + yo;
                 if (vec_ok && ow0 + 8 <= a.OW) {
                     const u32x4 o = {pack_bf16x2(yv[0], yv[1]), pack_bf16x2(yv[2], yv[3]), pack_bf16x2(yv[4], yv[5]),
                                      pack_bf16x2(yv[6], yv[7])};
@@ -941,13 +959,16 @@ inline bool plan(const Prob& p, int kb, Plan* pl, std::string* why) {
 }
 
 template <int TCB, int PWO, bool FOLD>
-cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void* vp, void* y, hipStream_t st) {
+cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void* vp, void* y, const Epi& e,
+                       hipStream_t st) {
     using G = Geo<TCB>;
     static_assert(G::LDS <= 160 * 1024, "LDS budget");
     if (pl.nblk > G::NBMAX) return set_error(CFWD_ERR_UNSUPPORTED, "winograd fused: patch wider than planned");
-    static bool attr = false;
-    auto kern = FOLD ? wf2f_kernel<TCB, PWO> : wf2_kernel<TCB, PWO>;
-    cfwd_status s = ig::allow_big_lds(kern, G::LDS, &attr);
+    const bool epi = e.bias || e.res || e.relu;
+    static bool attr[2] = {false, false};
+    auto kern = FOLD ? (epi ? wf2f_kernel<TCB, PWO, true> : wf2f_kernel<TCB, PWO, false>)
+                     : (epi ? wf2_kernel<TCB, PWO, true> : wf2_kernel<TCB, PWO, false>);
+    cfwd_status s = ig::allow_big_lds(kern, G::LDS, &attr[epi]);
     if (s != CFWD_OK) return s;
     Args a;
     a.x = static_cast<const uint16_t*>(x);
@@ -956,18 +977,23 @@ cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void*
     a.N = p.n; a.C = p.c; a.H = p.h; a.W = p.w; a.K = p.k; a.OH = p.oh; a.OW = p.ow; a.ph = p.ph; a.pw = p.pw;
     a.x_img = p.x_img; a.y_img = p.y_img;
     a.tbh = pl.tbh; a.tbw = pl.tbw; a.ntk = pl.ntk; a.nchunks = pl.nchunks; a.nblk = pl.nblk;
+    a.e = e;
     const unsigned blocks = static_cast<unsigned>(static_cast<long long>(p.n) * pl.tbh * pl.tbw * pl.ntk);
     kern<<<blocks, NTHR, G::LDS, st>>>(a);
     return check_hip(hipGetLastError(), "winograd fused launch");
 }
 
 template <bool FOLD>
-cfwd_status launch_fold(const Prob& p, const Plan& pl, const void* x, const void* wp, void* y, hipStream_t st) {
+cfwd_status launch_fold(const Prob& p, const Plan& pl, const void* x, const void* wp, void* y, const Epi& e,
+                        hipStream_t st) {
     const bool p1 = p.pw == 1;
     switch (pl.tcb) {
-        case 32: return p1 ? launch_tcb<32, 1, FOLD>(p, pl, x, wp, y, st) : launch_tcb<32, 0, FOLD>(p, pl, x, wp, y, st);
-        case 16: return p1 ? launch_tcb<16, 1, FOLD>(p, pl, x, wp, y, st) : launch_tcb<16, 0, FOLD>(p, pl, x, wp, y, st);
-        default: return p1 ? launch_tcb<8, 1, FOLD>(p, pl, x, wp, y, st) : launch_tcb<8, 0, FOLD>(p, pl, x, wp, y, st);
+        case 32:
+            return p1 ? launch_tcb<32, 1, FOLD>(p, pl, x, wp, y, e, st) : launch_tcb<32, 0, FOLD>(p, pl, x, wp, y, e, st);
+        case 16:
+            return p1 ? launch_tcb<16, 1, FOLD>(p, pl, x, wp, y, e, st) : launch_tcb<16, 0, FOLD>(p, pl, x, wp, y, e, st);
+        default:
+            return p1 ? launch_tcb<8, 1, FOLD>(p, pl, x, wp, y, e, st) : launch_tcb<8, 0, FOLD>(p, pl, x, wp, y, e, st);
     }
 }
 
@@ -1003,12 +1029,13 @@ cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* 
     return check_hip(hipGetLastError(), "winograd fused filter transform launch");
 }
 
-cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, hipStream_t st) {
+cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, const Epi& e,
+                                  hipStream_t st) {
     wf::Plan pl;
     std::string why;
     if (!wf::plan(p, wf::kb_of(cfg), &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (wp == nullptr) return set_error(CFWD_ERR_WORKSPACE, "winograd fused: prepared filter is required");
-    return cfg == 2 ? wf::launch_fold<true>(p, pl, x, wp, y, st) : wf::launch_fold<false>(p, pl, x, wp, y, st);
+    return cfg == 2 ? wf::launch_fold<true>(p, pl, x, wp, y, e, st) : wf::launch_fold<false>(p, pl, x, wp, y, e, st);
 }
 
 }  // namespace cfwd

@@ -258,3 +258,33 @@ def random_int8_problem(layer: Layer, n: int, seed: int) -> Int8Problem:
     fan = (layer.c // layer.groups) * layer.r * layer.s
     scale = (rng.uniform(0.5, 2.0, size=layer.k) * 127.0 / (4.0 * np.sqrt(_VAR_U127 * _VAR_U127 * fan))).astype(np.float32)
     return Int8Problem(layer, n, x, w, scale)
+
+
+# ------------------------------------------------------- fused-epilogue inputs
+
+
+@dataclass
+class EpilogueInputs:
+    """bias [K] and residual (logical NCHW, the output's shape) of a fused epilogue."""
+    bias: np.ndarray      # float32 (fp32 / bf16 problems) or int32 (int8)
+    residual: np.ndarray  # float32 holding bf16-exact values for bf16, int8 for int8
+
+
+def epilogue_inputs(out_shape, dtype: str, seed: int) -> EpilogueInputs:
+    """Seeded bias and residual for an output of ``out_shape`` = (N, K, OH, OW).
+
+    float: bias ~ U[-1, 1] (bf16-rounded for bf16), residual ~ U[-1, 1];
+    int8: bias ~ U{-4096..4096} (int32, added to the accumulator), residual ~
+    U{-127..127} (in the output's quantised scale).
+    """
+    rng = np.random.default_rng(seed)
+    K = out_shape[1]
+    if dtype == "i8":
+        bias = rng.integers(-4096, 4097, size=K, dtype=np.int64).astype(np.int32)
+        res = rng.integers(-127, 128, size=out_shape, dtype=np.int8)
+        return EpilogueInputs(bias, res)
+    bias = rng.uniform(-1.0, 1.0, size=K).astype(np.float32)
+    res = rng.uniform(-1.0, 1.0, size=out_shape).astype(np.float32)
+    if dtype == "bf16":
+        bias, res = round_to_bf16(bias), round_to_bf16(res)
+    return EpilogueInputs(bias, res)

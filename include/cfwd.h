@@ -100,6 +100,30 @@ typedef struct {
     float median_ms;
 } cfwd_algo;
 
+/* Activation of the fused epilogue. */
+typedef enum { CFWD_ACT_NONE = 0, CFWD_ACT_RELU = 1 } cfwd_activation;
+
+/* Fused epilogue of cfwd_conv2d_fwd_ex: what a ResNet block applies after
+ * its convolution, folded into the convolution's own output pass (Momenta
+ * talk "Paper Reading | 讓深度學習更高效運行的兩個視角", section "Graph層面":
+ * conv, bias and ReLU computed as one operation, the output written once).
+ *   bias      device [K]: fp32 for fp32 / bf16 problems, int32 for int8;
+ *             NULL = none.  4-byte aligned.
+ *   residual  device tensor of y's shape, layout and dtype (the skip
+ *             connection); NULL = none.  16-byte aligned, must not overlap y.
+ *   act       CFWD_ACT_NONE or CFWD_ACT_RELU.
+ * fp32 / bf16: y = act(conv + bias[k] + residual), in fp32, then one
+ *   conversion to the output dtype (bf16: round to nearest even).
+ * int8: y = clamp(rne(fp32(acc + bias[k]) * scale[k] + fp32(residual)), lo, 127)
+ *   with the bias added to the int32 accumulator (acc + bias must stay in
+ *   int32), one fp32 multiply, one fp32 add, ties to even, lo = 0 under ReLU
+ *   and -127 otherwise (the residual is taken to be in y's quantised scale). */
+typedef struct {
+    const void *bias;
+    const void *residual;
+    cfwd_activation act;
+} cfwd_epilogue;
+
 /* Library version string, e.g. "cfwd 0.1.0 gfx950". */
 const char *cfwd_version(void);
 
@@ -149,6 +173,18 @@ cfwd_status cfwd_conv2d_fwd(const cfwd_conv_desc *desc, cfwd_algo algo, const vo
                             const void *w_kcrs, const void *w_prepared,
                             const float *requant_scale, void *y, void *workspace,
                             size_t ws_bytes, void *stream);
+
+/* cfwd_conv2d_fwd with a fused epilogue (see cfwd_epilogue; NULL = none,
+ * which is exactly cfwd_conv2d_fwd).  Every algorithm and config applies it
+ * in its own output pass, so AUTO dispatch from the Fast-Run map works
+ * unchanged (the map is chosen on the convolution alone; a
+ * CFWD_FASTRUN_MODE=search miss with an epilogue falls back to the fixed
+ * preference instead of searching).  INVALID_ARG for an unknown activation,
+ * a misaligned bias or residual, or a residual overlapping y. */
+cfwd_status cfwd_conv2d_fwd_ex(const cfwd_conv_desc *desc, cfwd_algo algo, const void *x,
+                               const void *w_kcrs, const void *w_prepared,
+                               const float *requant_scale, const cfwd_epilogue *epilogue, void *y,
+                               void *workspace, size_t ws_bytes, void *stream);
 
 /* Scratch capacity of cfwd_conv2d_fwd_noalloc, per device (64 MiB). */
 #define CFWD_NOALLOC_SCRATCH_BYTES (64u << 20)
