@@ -66,6 +66,9 @@ ALIASES = {
     "bottleneck": "bottleneck_1x1_3x3_1x1_56x56", "plain": "plain_3x3_256_56x56",
     "resnet18_int8": "resnet18_int8_nchw4",
 }
+# (config, layer) pairs whose output takes the skip connection: the second
+# 3x3 of each ResNet-18 basic block, the bottleneck's expanding 1x1
+RESIDUAL_LAYERS = {(5, 2), (5, 4), (5, 9), (5, 14), (5, 19), (4, 2)}
 ROTATE_BYTES = 512 * 2**20
 MAX_SETS = 256
 
@@ -83,6 +86,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="rotated buffer sets (0: enough for > 512 MB)")
     ap.add_argument("--telemetry-window", type=float, default=0.5,
                     help="seconds of further untimed steps while clock and power are sampled")
+    ap.add_argument("--epilogue", default="none", choices=["none", "fused", "unfused"],
+                    help="bias + ReLU after every layer (plus the residual on ResNet block-closing layers): fused "
+                         "into the convolution, or as separate elementwise passes after it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle CPU work at most")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -163,7 +169,8 @@ def main():
     from cnn_convolution_fwd_amd import binding as B
     from cnn_convolution_fwd_amd import telemetry
     from cnn_convolution_fwd_amd.roofline import PEAK, bound, layer_algo_flops, layer_bytes, layer_flops
-    from cnn_convolution_fwd_amd.workloads import CONFIGS, bf16_bits, float_problem, int8_problem, pack_nchwx
+    from cnn_convolution_fwd_amd.workloads import (CONFIGS, bf16_bits, epilogue_inputs, float_problem, int8_problem,
+                                                    pack_nchwx)
 
     base = ALIASES.get(a.workload, a.workload)
     if base not in WORKLOADS:
@@ -174,6 +181,9 @@ def main():
     dtype = a.dtype or dtypes[0]
     if dtype not in dtypes:
         print("workload %s runs in %s" % (base, "/".join(dtypes)), file=sys.stderr)
+        sys.exit(2)
+    if a.epilogue == "unfused" and dtype == "i8":
+        print("an unfused int8 epilogue would need the int32 accumulators; use --epilogue fused", file=sys.stderr)
         sys.exit(2)
     N = a.n or cfg.n
     workload = "%s_n%d" % (base, N)
@@ -202,9 +212,21 @@ def main():
             x0 = to_dev(pr.x)
             scale = None
         w = to_dev(pr.w)
+        # epilogue of this layer: bias, ReLU (not on downsample shortcuts), and
+        # the skip connection on the layers that close a residual block
+        bias = res0 = None
+        relu = False
+        if a.epilogue != "none":
+            oh, ow = L.out_hw()
+            epi = epilogue_inputs((N, L.k, oh, ow), dtype, 7000 + li)
+            bias = torch.from_numpy(epi.bias).to(dev)
+            relu = "down" not in L.name
+            if (cfg_idx, li) in RESIDUAL_LAYERS:
+                res0 = to_dev(pack_nchwx(epi.residual, cfg.x_block) if int8 else epi.residual)
+        fused = a.epilogue == "fused"
         plan = B.LayerPlan(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c, requant_scale=scale,
-                           algo_spec=a.algo)
-        layers.append(dict(L=L, pr=pr, x0=x0, y0=plan.new_output(), plan=plan))
+                           algo_spec=a.algo, bias=bias if fused else None, relu=relu and fused)
+        layers.append(dict(L=L, pr=pr, x0=x0, y0=plan.new_output(), plan=plan, bias=bias, res0=res0, relu=relu))
 
     # every layer rotates over its own buffer sets, > 512 MB per layer, so a
     # layer timed alone (per-kernel figures) cannot read from the cache either
@@ -214,14 +236,25 @@ def main():
         l["nsets"] = ns
         l["xs"] = [l["x0"]] + [l["x0"].clone() for _ in range(ns - 1)]
         l["ys"] = [l["y0"]] + [torch.empty_like(l["y0"]) for _ in range(ns - 1)]
+        l["rs"] = None if l["res0"] is None else [l["res0"]] + [l["res0"].clone() for _ in range(ns - 1)]
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
     def launch(l, i):
         ns = l["nsets"]
-        st = l["plan"].launch_raw(l["xs"][i % ns].data_ptr(), l["ys"][i % ns].data_ptr(), sptr)
+        y = l["ys"][i % ns]
+        res = l["rs"][i % ns] if l["rs"] is not None else None
+        fused = a.epilogue == "fused"
+        st = l["plan"].launch_raw(l["xs"][i % ns].data_ptr(), y.data_ptr(), sptr,
+                                  res.data_ptr() if (fused and res is not None) else 0)
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
+        if a.epilogue == "unfused":  # the same epilogue as elementwise passes over y
+            y.add_(l["bias"].view(1, -1, 1, 1).to(y.dtype))
+            if res is not None:
+                y.add_(res)
+            if l["relu"]:
+                y.relu_()
 
     sampler = telemetry.Sampler(torch.cuda.current_device())
     t_end = time.perf_counter() + a.settle
@@ -264,8 +297,9 @@ def main():
     sampler.start()
     t_end = time.perf_counter() + a.telemetry_window
     i = 0
+    batch = max(8, int(20.0 / max(ms_per_step, 1e-3)))  # ~20 ms of steps between synchronisations
     while time.perf_counter() < t_end:
-        for _ in range(8):
+        for _ in range(batch):
             for l in layers:
                 launch(l, i)
             i += 1
@@ -322,6 +356,7 @@ def main():
             "mb_per_step": round(sum(p["bytes"] for p in per_layer) / 1e6, 2),
             "warm_ms_per_step": round(warm_ms, 5),
             "filter_prepare_ms": round(sum(p["prepare_ms"] for p in per_layer), 5),
+            "epilogue": a.epilogue,
         },
         "gpu_telemetry": gpu_telemetry,
         "roofline": {

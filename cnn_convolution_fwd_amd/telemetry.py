@@ -112,6 +112,9 @@ def _amdsmi_reader(bdf: Optional[str]) -> Optional[Callable[[], Dict[str, float]
         out = {}
         try:
             m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            act = m.get("average_gfx_activity")
+            if isinstance(act, (int, float)) and 0 <= act <= 100:
+                out["activity_pct"] = float(act)
             for key in ("current_gfxclk", "average_gfxclk_frequency"):
                 v = _num(m.get(key))
                 if v:
@@ -193,9 +196,13 @@ class Sampler:
         return self.summary()
 
     def summary(self) -> Dict[str, object]:
-        out: Dict[str, object] = {"source": self.source, "pci_bus_id": self.bdf, "samples": len(self.samples)}
+        """Median / min / max over the samples taken while the GPU was busy
+        (graphics activity >= 90% where the source reports it)."""
+        busy = [s for s in self.samples if s.get("activity_pct", 100.0) >= 90.0]
+        out: Dict[str, object] = {"source": self.source, "pci_bus_id": self.bdf, "samples": len(self.samples),
+                                  "busy_samples": len(busy)}
         for key, name in (("sclk_mhz", "sclk_mhz"), ("power_w", "power_w")):
-            v = [s[key] for s in self.samples if key in s]
+            v = [s[key] for s in busy if key in s]
             if v:
                 out[name] = {"median": round(statistics.median(v), 1), "min": round(min(v), 1),
                              "max": round(max(v), 1)}
