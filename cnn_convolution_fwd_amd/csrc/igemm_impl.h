@@ -942,8 +942,34 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 const long long kofs = EPI ? static_cast<long long>(k >> 2) * a.OH * a.OW * 4 + (k & 3) +
                                                  static_cast<long long>(oh0) * a.OW * 4
                                            : 0;
+                const int ebias = (EPI && a.e.bias) ? static_cast<const int32_t*>(a.e.bias)[ke] : 0;
+                const float elo = (EPI && a.e.relu) ? 0.0f : -127.0f;
 #pragma unroll
-                for (int f = 0; f < FM; ++f)
+                for (int f = 0; f < FM; ++f) {
+                    // fused epilogue: this fragment's residual bytes, all
+                    // requested before any is used; a 4-pixel group's image
+                    // and offset come from one division
+                    float eres[NG][4];
+                    if constexpr (EPI) {
+#pragma unroll
+                        for (int grp = 0; grp < NG; ++grp) {
+                            const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
+                            const int tn0 = p0 / thw, r0 = p0 - tn0 * thw;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                eres[grp][v] = 0.0f;
+                                int tn = tn0, rem = r0 + v;
+                                while (rem >= thw) {  // images of fewer than 4 pixels wrap more than once
+                                    rem -= thw;
+                                    ++tn;
+                                }
+                                if (a.e.res && p0 + v < tile_pix)
+                                    eres[grp][v] = static_cast<float>(static_cast<const int8_t*>(
+                                        a.e.res)[static_cast<long long>(min(n0 + tn, a.N - 1)) * a.y_img + kofs +
+                                                 static_cast<long long>(rem) * 4]);
+                            }
+                        }
+                    }
 #pragma unroll
                     for (int grp = 0; grp < NG; ++grp) {
                         const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
@@ -951,18 +977,15 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
                                 uint32_t q;
-                                if constexpr (EPI) {
-                                    const int pp = p0 + v, tn = pp / thw;
-                                    const long long o = static_cast<long long>(min(n0 + tn, a.N - 1)) * a.y_img + kofs +
-                                                        static_cast<long long>(pp - tn * thw) * 4;
-                                    q = requant_i8_epi_bits(acc[f][nf][grp * 4 + v], sc, a.e, ke, o);
-                                } else {
+                                if constexpr (EPI)
+                                    q = requant_i8_fused(acc[f][nf][grp * 4 + v], ebias, sc, eres[grp][v], elo);
+                                else
                                     q = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
-                                }
                                 lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(q);
                             }
                         }
                     }
+                }
             }
             __syncthreads();
             const long long OHW = static_cast<long long>(a.OH) * a.OW;
@@ -1015,23 +1038,44 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                                                static_cast<long long>(g * a.Kg + kl) * a.OH * a.OW +
                                                static_cast<long long>(oh0) * a.OW
                                          : 0;
+                const bool kin = kl < a.Kg;
+                const float ebias = (EPI && a.e.bias && kin) ? static_cast<const float*>(a.e.bias)[g * a.Kg + kl] : 0.0f;
 #pragma unroll
-                for (int f = 0; f < FM; ++f)
+                for (int f = 0; f < FM; ++f) {
+                    // fused epilogue: this fragment's residual values, all
+                    // requested before any is used
+                    constexpr int NGB = FT::NACC / 4;
+                    float eres[NGB][4];
+                    if constexpr (EPI) {
 #pragma unroll
-                    for (int grp = 0; grp < FT::NACC / 4; ++grp) {
+                        for (int grp = 0; grp < NGB; ++grp) {
+                            const int p0 = (wm * FM + f) * FR + 8 * grp + 4 * lgrp;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v)
+                                eres[grp][v] = (a.e.res && kin && p0 + v < tile_pix)
+                                                   ? Elem<T>::to_f(static_cast<const T*>(a.e.res)[ko + p0 + v])
+                                                   : 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int grp = 0; grp < NGB; ++grp) {
                         const int p0 = (wm * FM + f) * FR + 8 * grp + 4 * lgrp;
                         if (p0 < tile_pix) {
                             float v4[4];
 #pragma unroll
                             for (int v = 0; v < 4; ++v) v4[v] = acc[f][nf][grp * 4 + v];
-                            if (EPI && kl < a.Kg) {
+                            if constexpr (EPI) {
 #pragma unroll
-                                for (int v = 0; v < 4; ++v) v4[v] = epi_float<T>(v4[v], a.e, g * a.Kg + kl, ko + p0 + v);
+                                for (int v = 0; v < 4; ++v) {
+                                    const float t = v4[v] + ebias + eres[grp][v];
+                                    v4[v] = a.e.relu ? fmaxf(t, 0.0f) : t;
+                                }
                             }
                             const uint2 q = make_uint2(pack_bf16x2(v4[0], v4[1]), pack_bf16x2(v4[2], v4[3]));
                             *reinterpret_cast<uint2*>(lds + kk * pitch + p0 * 2) = q;
                         }
                     }
+                }
             }
             __syncthreads();
             const int pieces = tile_pix / 8;  // 16-byte pieces per channel row

@@ -166,8 +166,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // int32 accumulator -> int8: clamp(rne(fp32(acc) * scale), -127, 127).
-// __fmul_rn keeps the multiply a separate IEEE operation; rintf rounds to
-// nearest even.
+// One IEEE multiply (nothing follows it that could be contracted with it);
+// rintf rounds to nearest even.
 __device__ __forceinline__ int8_t requant_i8(int acc, float scale) {
     float q = rintf(__fmul_rn(static_cast<float>(acc), scale));
     q = fminf(fmaxf(q, -127.0f), 127.0f);
@@ -203,12 +203,21 @@ __device__ __forceinline__ float epi_float(float v, const Epi& e, int k, long lo
 // lo, 127), lo = 0 under ReLU, else -127; the value in the low byte, as in
 // requant_i8_bits (which this equals with no bias, residual or ReLU).  k
 // must be a real channel (< K) when there is a bias.
+// The same with its operands already loaded: bias (0 when absent), residual
+// (0.0 when absent: adding +0 only turns a -0 into +0, which rounds to the
+// same byte) and the lower clamp lo (0 under ReLU, else -127).
+// The multiply and the add are two roundings by definition: contraction into
+// one FMA is switched off here (the __f*_rn helpers are plain operators).
+__device__ __forceinline__ uint32_t requant_i8_fused(int acc, int bias, float scale, float res, float lo) {
+#pragma clang fp contract(off)
+    const float q = static_cast<float>(acc + bias) * scale + res;
+    return __float_as_uint(__builtin_amdgcn_fmed3f(q, lo, 127.0f) + 12582912.0f);
+}
+
 __device__ __forceinline__ uint32_t requant_i8_epi_bits(int acc, float scale, const Epi& e, int k, long long off) {
-    if (e.bias) acc += static_cast<const int32_t*>(e.bias)[k];
-    float q = __fmul_rn(static_cast<float>(acc), scale);
-    if (e.res) q = __fadd_rn(q, static_cast<float>(static_cast<const int8_t*>(e.res)[off]));
-    q = __builtin_amdgcn_fmed3f(q, e.relu ? 0.0f : -127.0f, 127.0f);
-    return __float_as_uint(__fadd_rn(q, 12582912.0f));
+    const int b = e.bias ? static_cast<const int32_t*>(e.bias)[k] : 0;
+    const float r = e.res ? static_cast<float>(static_cast<const int8_t*>(e.res)[off]) : 0.0f;
+    return requant_i8_fused(acc, b, scale, r, e.relu ? 0.0f : -127.0f);
 }
 
 template <typename T> struct Elem;

@@ -244,6 +244,18 @@ __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, 
         left[j] = (cg > 0) ? l : 0.0f;
         right[j] = (cg < cols - 1) ? r : 0.0f;
     }
+    // fused epilogue: the RB residual row vectors this thread stores, all
+    // requested here, before any computation (rows past the image clamped)
+    uint32_t rres[EPI ? RB : 1][NW];
+    float ebias = 0.0f;
+    if constexpr (EPI) {
+        if (ep.res) {
+            const T* rp = static_cast<const T*>(ep.res) + (yp - y);
+#pragma unroll
+            for (int i = 0; i < RB; ++i) RawVec<NW>::load(rp + (min(oh0 + i, H - 1) * W + ow0), rres[i]);
+        }
+        if (ep.bias) ebias = static_cast<const float*>(ep.bias)[c];
+    }
     // bf16: weight pairs (w0, w1) and (w1, w2) of each filter row, packed
     bf16x2_t w01[3], w12[3];
     if constexpr (sizeof(T) == 2) {
@@ -302,13 +314,10 @@ __global__ __launch_bounds__(256) void depthwise3x3_s1(const T* __restrict__ x, 
             // fused epilogue: bias, residual (the same vector of the
             // residual tensor), ReLU, before the one conversion
             if constexpr (EPI) {
-                uint32_t rr[NW];
-                if (ep.res) RawVec<NW>::load(static_cast<const T*>(ep.res) + (yp - y) + (oh * W + ow0), rr);
-                const float b = ep.bias ? static_cast<const float*>(ep.bias)[c] : 0.0f;
 #pragma unroll
                 for (int e = 0; e < V; ++e) {
-                    float v = out[e] + b;
-                    if (ep.res) v += WD::elem(rr, e);
+                    float v = out[e] + ebias;
+                    if (ep.res) v += WD::elem(rres[i], e);
                     out[e] = ep.relu ? fmaxf(v, 0.0f) : v;
                 }
             }

@@ -368,16 +368,30 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
                     const int pl = (wpx * NCB + cb) * 32 + j;
+                    // fused epilogue: the 16 channels' bias and residual values
+                    // of this lane's pixel, all requested before any is used
+                    float ebias[16], eres[16];
+                    if constexpr (EPI) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int k = kg * a.KW * KBW * 32 + (wk * KBW + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                            const bool kin = k < a.K;
+                            ebias[v] = (a.e.bias && kin) ? static_cast<const float*>(a.e.bias)[k] : 0.0f;
+                            eres[v] = (a.e.res && kin && pok[cb])
+                                          ? Elem<T>::to_f(static_cast<const T*>(a.e.res)[pn[cb] * a.y_img +
+                                                                                        static_cast<long long>(k) * ohw +
+                                                                                        ppix[cb]])
+                                          : 0.0f;
+                        }
+                    }
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int cl = (wk * KBW + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
                         uint8_t* d = otile + cl * pitch + pl * E;
                         float val = acc[b][cb][v];
                         if constexpr (EPI) {  // fused epilogue, before the conversion
-                            const int k = kg * a.KW * KBW * 32 + cl;
-                            if (k < a.K && pok[cb])
-                                val = epi_float<T>(val, a.e, k,
-                                                   pn[cb] * a.y_img + static_cast<long long>(k) * ohw + ppix[cb]);
+                            const float t = val + ebias[v] + eres[v];
+                            val = a.e.relu ? fmaxf(t, 0.0f) : t;
                         }
                         if constexpr (sizeof(T) == 4)
                             *reinterpret_cast<float*>(d) = val;
@@ -472,6 +486,23 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                 const long long ohw4 = static_cast<long long>(ohw) * 4;
                 uint8_t* yb = reinterpret_cast<uint8_t*>(y) + n * a.y_img + static_cast<long long>(pix) * 4 +
                               static_cast<long long>(kb0 * 8 + h) * ohw4;
+                // fused epilogue: the residual dwords (4 channels of this
+                // lane's pixel) of the block's four channel groups, requested
+                // before any is used; channels past K (scale 0, zeroed
+                // afterwards) take the last real channel's bias
+                uint32_t eres[4] = {0u, 0u, 0u, 0u};
+                if constexpr (EPI) {
+                    if (a.e.res) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int k0 = (kb0 + b) * 32 + 8 * q + 4 * h;
+                            if (k0 < a.K)
+                                eres[q] = *reinterpret_cast<const uint32_t*>(
+                                    static_cast<const int8_t*>(a.e.res) + n * a.y_img +
+                                    (static_cast<long long>(k0 / 4) * ohw + pix) * 4);
+                        }
+                    }
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int k0 = (kb0 + b) * 32 + 8 * q + 4 * h;
@@ -479,14 +510,14 @@ __global__ __launch_bounds__(256) void lc_kernel(const T* __restrict__ x, const 
                     const typename L::Acc& ac = acc[b][cb];
                     uint32_t word;
                     if constexpr (EPI) {
-                        // fused epilogue; channels past K (scale 0, zeroed
-                        // afterwards) read the last real channel's bias
-                        const long long o0 = n * a.y_img + (static_cast<long long>(k0 / 4) * ohw + pix) * 4;
                         uint32_t qb[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            qb[i] = requant_i8_epi_bits(ac[4 * q + i], sc[b][4 * q + i], a.e, min(k0 + i, a.K - 1),
-                                                        o0 + i);
+                        for (int i = 0; i < 4; ++i) {
+                            const int kb = min(k0 + i, a.K - 1);
+                            const int bi = a.e.bias ? static_cast<const int32_t*>(a.e.bias)[kb] : 0;
+                            const float r = static_cast<float>(static_cast<int8_t>((eres[q] >> (8 * i)) & 0xffu));
+                            qb[i] = requant_i8_fused(ac[4 * q + i], bi, sc[b][4 * q + i], r, a.e.relu ? 0.0f : -127.0f);
+                        }
                         word = pack_low_bytes(qb[0], qb[1], qb[2], qb[3]);
                     } else {
                         word = pack_low_bytes(

@@ -57,6 +57,12 @@ template <> struct PwT<bf16_t> {
         const u32x2_t q = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         __builtin_nontemporal_store(q, reinterpret_cast<u32x2_t*>(p));
     }
+    static __device__ __forceinline__ void unpack4(const XV& q, float* r) {
+        r[0] = __uint_as_float(q.x << 16);
+        r[1] = __uint_as_float(q.x & 0xffff0000u);
+        r[2] = __uint_as_float(q.y << 16);
+        r[3] = __uint_as_float(q.y & 0xffff0000u);
+    }
 };
 template <> struct PwT<float> {
     static constexpr int STEP = 8;
@@ -74,6 +80,12 @@ template <> struct PwT<float> {
         typedef float f32x4_t __attribute__((ext_vector_type(4)));
         const f32x4_t q = {v[0], v[1], v[2], v[3]};
         __builtin_nontemporal_store(q, reinterpret_cast<f32x4_t*>(p));
+    }
+    static __device__ __forceinline__ void unpack4(const XV& q, float* r) {
+        r[0] = __uint_as_float(q.x);
+        r[1] = __uint_as_float(q.y);
+        r[2] = __uint_as_float(q.z);
+        r[3] = __uint_as_float(q.w);
     }
 };
 
@@ -180,20 +192,40 @@ __global__ __launch_bounds__(256) void pw_kernel(const T* __restrict__ x, const 
     // D[row = channel][col = pixel]: lane (j, hh), element v -> channel
     // 8 (v / 4) + 4 hh + v % 4 of the block, pixels 4j .. 4j + 3 over the phases
 #pragma unroll
-    for (int b = 0; b < KBW; ++b)
+    for (int b = 0; b < KBW; ++b) {
+        // fused epilogue: every bias and residual vector of this block is
+        // requested before the first is used (the residual vector of a
+        // channel is the same 4 pixels the lane stores)
+        float bv[16];
+        XV rv[16];
+        if constexpr (EPI) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int kc = min((kb0 + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4), K - 1);
+                bv[v] = ep.bias ? static_cast<const float*>(ep.bias)[kc] : 0.0f;
+                if (ep.res)
+                    rv[v] = *reinterpret_cast<const XV*>(static_cast<const T*>(ep.res) + (yb - y) +
+                                                         static_cast<long long>(kc) * HW);
+            }
+        }
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int k = (kb0 + b) * 32 + 8 * (v / 4) + 4 * h + (v % 4);
             if (k < K) {
                 float o[4] = {acc[b][0][v], acc[b][1][v], acc[b][2][v], acc[b][3][v]};
                 if constexpr (EPI) {
-                    const long long off = (yb - y) + static_cast<long long>(k) * HW;
+                    float r[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    if (ep.res) P::unpack4(rv[v], r);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) o[i] = epi_float<T>(o[i], ep, k, off + i);
+                    for (int i = 0; i < 4; ++i) {
+                        const float t = o[i] + bv[v] + r[i];
+                        o[i] = ep.relu ? fmaxf(t, 0.0f) : t;
+                    }
                 }
                 P::store4(yb + static_cast<long long>(k) * HW, o);
             }
         }
+    }
 }
 
 struct PwGeo {
