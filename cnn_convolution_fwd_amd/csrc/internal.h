@@ -102,8 +102,19 @@ cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const 
 bool winograd_fused_supported(const Prob& p, int cfg, std::string* why);
 size_t winograd_fused_filter_bytes(const Prob& p, int cfg);
 cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st);
-cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, const Epi& e,
-                                  hipStream_t st);
+cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* scratch, void* y,
+                                  const Epi& e, hipStream_t st);
+
+// bf16 Winograd keeps its transformed operands in fp16, whose range is far
+// narrower than bf16's.  Input and filter are therefore scaled by powers of
+// two that bring their largest magnitude into [2^7, 2^8) -- then every
+// transformed operand stays below 65504 (F(6x6) grows an input by at most
+// 156.25, a filter by 49) and magnitudes down to 2^-22 of the largest stay
+// normal -- and the output is scaled back.  Powers of two are exact.
+// bf16_absmax: *out = the largest |x| of n bf16 values, as a bit pattern
+// (sign cleared); out points to an 8 KiB area whose words 64.. hold the
+// per-workgroup partial maxima.
+cfwd_status bf16_absmax(const void* x, long long n, unsigned* out, hipStream_t st);
 
 // Writes 0 to the NCHWX output channels past K (no-op unless K % xb != 0).
 cfwd_status zero_output_channel_padding(const Prob& p, void* y, hipStream_t st);
@@ -218,6 +229,22 @@ __device__ __forceinline__ uint32_t requant_i8_epi_bits(int acc, float scale, co
     const int b = e.bias ? static_cast<const int32_t*>(e.bias)[k] : 0;
     const float r = e.res ? static_cast<float>(static_cast<const int8_t*>(e.res)[off]) : 0.0f;
     return requant_i8_fused(acc, b, scale, r, e.relu ? 0.0f : -127.0f);
+}
+
+// Exponent of the largest magnitude whose bf16 bit pattern is `bits`
+// (floored, so an all-zero tensor gives finite factors).
+__device__ __forceinline__ int wg_exp(unsigned bits) { return max(static_cast<int>(bits >> 7) - 127, -100); }
+// Factor that brings that magnitude into [2^7, 2^8) (1 when no maximum is given).
+__device__ __forceinline__ float wg_norm(const unsigned* maxbits) {
+    return maxbits ? __builtin_amdgcn_ldexpf(1.0f, 7 - wg_exp(*maxbits)) : 1.0f;
+}
+// Exponent shift that undoes one operand's factor (0 when none is given);
+// read once per workgroup, applied per output with wg_denorm.
+__device__ __forceinline__ int wg_shift(const unsigned* maxbits) { return maxbits ? wg_exp(*maxbits) - 7 : 0; }
+// Undoes the input's and the filter's factors on an output (two steps, so
+// a large and a small shift do not overflow in between).
+__device__ __forceinline__ float wg_denorm(float v, int shift_x, int shift_w) {
+    return __builtin_amdgcn_ldexpf(__builtin_amdgcn_ldexpf(v, shift_x), shift_w);
 }
 
 template <typename T> struct Elem;

@@ -78,6 +78,7 @@ struct Geo {
     int TB, KB, ntk, ntb;   // tile block, output-channel block, block counts
     size_t u_bytes;         // transformed-input workspace
     size_t v_bytes;         // prepared filter
+    size_t hdr;             // bf16: 8 KiB after each for the operand maxima (wg_norm)
 };
 
 inline bool geometry(const Prob& p, int m, Geo* g, std::string* why) {
@@ -109,6 +110,7 @@ inline bool geometry(const Prob& p, int m, Geo* g, std::string* why) {
     g->ntb = g->Tpad / g->TB;
     g->u_bytes = static_cast<size_t>(g->xi) * g->nchunks * g->Tpad * 64;
     g->v_bytes = static_cast<size_t>(g->xi) * g->ntk * g->nchunks * g->KB * 64;
+    g->hdr = (p.dtype == CFWD_BF16) ? 8192 : 0;
     return true;
 }
 
@@ -118,8 +120,9 @@ inline bool geometry(const Prob& p, int m, Geo* g, std::string* why) {
 
 template <typename T, int M>
 __global__ __launch_bounds__(256) void prepare_kernel(const T* __restrict__ w, uint8_t* __restrict__ out, int K, int C,
-                                                      int KB, int ntk, int nchunks) {
+                                                      int KB, int ntk, int nchunks, const unsigned* __restrict__ wmax) {
     using O = typename OpT<T>::type;
+    const float wsc = wg_norm(wmax);  // bf16: filter scale for the fp16 range
     constexpr int A = M + 2;
     constexpr int E16 = 16 / static_cast<int>(sizeof(O));
     constexpr int CK = 4 * E16;
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(const T* __restrict__ w, u
                 const long long base =
                     ((((static_cast<long long>(x) * ntk + kt) * nchunks + chunk) * (KB / 32) + nfr) * 2 + piece) * 32 + row;
                 O* dst = reinterpret_cast<O*>(out + (base * 2 + half) * 16) + e;
-                *dst = OpT<T>::from(acc);
+                *dst = OpT<T>::from(acc * wsc);
             }
     }
 }
@@ -189,8 +192,10 @@ template <int M, int CK> struct InGeo {
 template <typename T, int XB, int M>
 __global__ __launch_bounds__(256) void input_kernel(const T* __restrict__ x, uint8_t* __restrict__ U, int N, int C, int H,
                                                     int W, int ph, int pw, long long x_img, int th, int tw, int T_,
-                                                    int Tpad, int nchunks, int tblocks_w) {
+                                                    int Tpad, int nchunks, int tblocks_w,
+                                                    const unsigned* __restrict__ xmax) {
     using O = typename OpT<T>::type;
+    const float xsc = wg_norm(xmax);  // bf16: input scale for the fp16 range
     constexpr int A = M + 2;
     constexpr int CK = 64 / static_cast<int>(sizeof(O));
     using IG = InGeo<M, CK>;
@@ -260,8 +265,60 @@ __global__ __launch_bounds__(256) void input_kernel(const T* __restrict__ x, uin
                 const float bk = static_cast<float>(mt.bt[j][k]);
                 if (bk != 0.0f) acc = fmaf(t[i][k], bk, acc);
             }
-            dst[(i * A + j) * xstride] = OpT<T>::from(acc);
+            dst[(i * A + j) * xstride] = OpT<T>::from(acc * xsc);
         }
+}
+
+// Largest magnitude of n bf16 values, as a bit pattern with the sign
+// cleared (for non-negative values the bit patterns order like the values):
+// each of kAbsmaxBlocks workgroups writes the maximum of its share to a slot,
+// then one workgroup reduces the slots (no atomics, nothing to clear first).
+constexpr int kAbsmaxBlocks = 1024;
+
+__device__ __forceinline__ unsigned block_max(unsigned m) {
+    __shared__ unsigned part[4];
+    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<unsigned>(__shfl_down(static_cast<int>(m), off)));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    return max(max(part[0], part[1]), max(part[2], part[3]));
+}
+
+__global__ __launch_bounds__(256) void bf16_absmax_partial(const uint16_t* __restrict__ x, long long n,
+                                                           unsigned* __restrict__ slots) {
+    unsigned m = 0;
+    const long long n8 = n / 8;
+    const uint4* x8 = reinterpret_cast<const uint4*>(x);
+    const long long stride = static_cast<long long>(gridDim.x) * 256;
+    // four independent 16-byte loads in flight per thread
+    long long i = blockIdx.x * 256LL + threadIdx.x;
+    for (; i + 3 * stride < n8; i += 4 * stride) {
+        uint4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = x8[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t w4[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) m = max(m, max(w4[q] & 0x7fffu, (w4[q] >> 16) & 0x7fffu));
+        }
+    }
+    for (; i < n8; i += stride) {
+        const uint4 v = x8[i];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) m = max(m, max(w4[q] & 0x7fffu, (w4[q] >> 16) & 0x7fffu));
+    }
+    for (long long t = n8 * 8 + blockIdx.x * 256LL + threadIdx.x; t < n; t += stride)
+        m = max(m, static_cast<unsigned>(x[t]) & 0x7fffu);
+    m = block_max(m);
+    if (threadIdx.x == 0) slots[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(256) void absmax_final(const unsigned* __restrict__ slots, unsigned* __restrict__ out) {
+    unsigned m = 0;
+    for (int i = threadIdx.x; i < kAbsmaxBlocks; i += 256) m = max(m, slots[i]);
+    m = block_max(m);
+    if (threadIdx.x == 0) *out = m;
 }
 
 // Zero rows of U for the padding tiles T .. Tpad-1 (they feed the last tile
@@ -290,7 +347,8 @@ template <int M> struct GemmGeo {
 template <typename T, int XB, int M, bool EPI>  // EPI: fused epilogue compiled in
 __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* __restrict__ U, const uint8_t* __restrict__ V,
                                                    T* __restrict__ y, int K, int OH, int OW, long long y_img, int th,
-                                                   int tw, int T_, int Tpad, int nchunks, int ntk, Epi ep) {
+                                                   int tw, int T_, int Tpad, int nchunks, int ntk, Epi ep,
+                                                   const unsigned* __restrict__ xmax, const unsigned* __restrict__ wmax) {
     constexpr int A = M + 2;
     constexpr int XI = A * A;
     constexpr int NW = GemmGeo<M>::NW;
@@ -304,6 +362,7 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lrow = lane & 31, h = lane >> 5;
+    const int osx = wg_shift(xmax), osw = wg_shift(wmax);  // bf16: shifts undoing the operand scales
     // tile block fastest: consecutive workgroups share the same filter slice
     const int tb = blockIdx.x % (Tpad / TB);
     const int kt = blockIdx.x / (Tpad / TB);
@@ -432,6 +491,7 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
                         }
                         const long long o = n * y_img + act_off<XB>(k, oh, ow, OH, OW);
                         T* dst = y + o;
+                        s = wg_denorm(s, osx, osw);  // bf16: undo the operand scales
                         if constexpr (EPI) s = epi_float<T>(s, ep, k, o);  // fused epilogue
                         if constexpr (sizeof(T) == 4)
                             *dst = s;
@@ -448,15 +508,24 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
 template <typename T, int XB, int M>
 cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y, const Epi& e,
                      hipStream_t st) {
+    // bf16: the operands' maxima sit after the transformed input (this
+    // call's) and after the prepared filter (written by the prepare step)
+    unsigned* xmax = g.hdr ? reinterpret_cast<unsigned*>(static_cast<uint8_t*>(ubuf) + g.u_bytes) : nullptr;
+    const unsigned* wmax = g.hdr ? reinterpret_cast<const unsigned*>(static_cast<const uint8_t*>(vprep) + g.v_bytes)
+                                 : nullptr;
     {
         using O = typename OpT<T>::type;
         constexpr int TXB = InGeo<M, 64 / static_cast<int>(sizeof(O))>::TXB;
         const int tblocks_w = (g.tw + TXB - 1) / TXB;
         const dim3 grid(static_cast<unsigned>(static_cast<long long>(p.n) * g.th * tblocks_w),
                         static_cast<unsigned>(g.nchunks));
+        if (xmax) {
+            cfwd_status s = bf16_absmax(x, static_cast<long long>(p.n) * p.x_img, xmax, st);
+            if (s != CFWD_OK) return s;
+        }
         input_kernel<T, XB, M><<<grid, 256, 0, st>>>(static_cast<const T*>(x), static_cast<uint8_t*>(ubuf), p.n, p.c,
                                                      p.h, p.w, p.ph, p.pw, p.x_img, g.th, g.tw, g.T, g.Tpad,
-                                                     g.nchunks, tblocks_w);
+                                                     g.nchunks, tblocks_w, xmax);
         cfwd_status s = check_hip(hipGetLastError(), "winograd input transform launch");
         if (s != CFWD_OK) return s;
         if (g.Tpad > g.T) {
@@ -483,7 +552,7 @@ cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vpr
     const unsigned blocks = static_cast<unsigned>(g.ntb * g.ntk);
     kern<<<blocks, GemmGeo<M>::NTHR, lds, st>>>(static_cast<const uint8_t*>(ubuf), static_cast<const uint8_t*>(vprep),
                                    static_cast<T*>(y), p.k, p.oh, p.ow, p.y_img, g.th, g.tw, g.T, g.Tpad, g.nchunks,
-                                   g.ntk, e);
+                                   g.ntk, e, xmax, wmax);
     return check_hip(hipGetLastError(), "winograd gemm launch");
 }
 
@@ -499,6 +568,15 @@ cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vpr
 }
 
 }  // namespace wg
+
+cfwd_status bf16_absmax(const void* x, long long n, unsigned* out, hipStream_t st) {
+    unsigned* slots = out + 64;  // words 64 .. 64 + kAbsmaxBlocks of the 8 KiB area
+    wg::bf16_absmax_partial<<<wg::kAbsmaxBlocks, 256, 0, st>>>(static_cast<const uint16_t*>(x), n, slots);
+    cfwd_status s = check_hip(hipGetLastError(), "bf16_absmax_partial launch");
+    if (s != CFWD_OK) return s;
+    wg::absmax_final<<<1, 256, 0, st>>>(slots, out);
+    return check_hip(hipGetLastError(), "absmax_final launch");
+}
 
 // F(2x2): config 0 = the three-launch form above (any float dtype and
 // layout), configs 1 and 2 = the fused single-launch kernels (bf16 NCHW).
@@ -527,14 +605,15 @@ size_t winograd_filter_bytes(const Prob& p, int m, int cfg) {
     if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_filter_bytes(p, cfg);
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
-    return g.v_bytes;
+    return g.v_bytes + g.hdr;
 }
 
 size_t winograd_scratch_bytes(const Prob& p, int m, int cfg) {
-    if (m == 2 && (cfg == 1 || cfg == 2)) return 0;
+    if (m == 2 && (cfg == 1 || cfg == 2))  // the fused form: only the input's largest magnitude
+        return winograd_fused_supported(p, cfg, nullptr) ? 8192 : 0;
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
-    return g.u_bytes;
+    return g.u_bytes + g.hdr;
 }
 
 cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st) {
@@ -549,21 +628,29 @@ cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void*
     uint8_t* out = static_cast<uint8_t*>(wp);
     if (p.dtype == CFWD_F32) {
         if (m == 2)
-            wg::prepare_kernel<float, 2><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+            wg::prepare_kernel<float, 2><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk,
+                                                             g.nchunks, nullptr);
         else
-            wg::prepare_kernel<float, 6><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+            wg::prepare_kernel<float, 6><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk,
+                                                             g.nchunks, nullptr);
     } else {
+        // the filter's largest magnitude goes after the transformed filter
+        unsigned* wmax = reinterpret_cast<unsigned*>(out + g.v_bytes);
+        cfwd_status s = bf16_absmax(w, static_cast<long long>(p.k) * p.cg * 9, wmax, st);
+        if (s != CFWD_OK) return s;
         if (m == 2)
-            wg::prepare_kernel<bf16_t, 2><<<nb, 256, 0, st>>>(static_cast<const bf16_t*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+            wg::prepare_kernel<bf16_t, 2><<<nb, 256, 0, st>>>(static_cast<const bf16_t*>(w), out, p.k, p.c, g.KB,
+                                                              g.ntk, g.nchunks, wmax);
         else
-            wg::prepare_kernel<bf16_t, 6><<<nb, 256, 0, st>>>(static_cast<const bf16_t*>(w), out, p.k, p.c, g.KB, g.ntk, g.nchunks);
+            wg::prepare_kernel<bf16_t, 6><<<nb, 256, 0, st>>>(static_cast<const bf16_t*>(w), out, p.k, p.c, g.KB,
+                                                              g.ntk, g.nchunks, wmax);
     }
     return check_hip(hipGetLastError(), "winograd filter transform launch");
 }
 
 cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch, void* y,
                             const Epi& e, hipStream_t st) {
-    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_launch(p, cfg, x, wp, y, e, st);
+    if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_launch(p, cfg, x, wp, scratch, y, e, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);

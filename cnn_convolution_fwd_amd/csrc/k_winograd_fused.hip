@@ -115,6 +115,10 @@ struct Args {
     int tbh, tbw, ntk, nchunks;
     int nblk;  // 8-column load blocks per patch row
     Epi e;     // fused epilogue
+    // largest input / filter magnitudes (bf16 bit patterns): the operands are
+    // scaled into the fp16 range by wg_norm and the outputs back by wg_denorm
+    const unsigned* xmax;
+    const unsigned* wmax;
 };
 
 // Fused epilogue (bias, residual, ReLU) on 8 consecutive outputs of channel
@@ -125,11 +129,11 @@ __device__ __forceinline__ void epi8(float* yv, const Epi& e, int k, long long o
         if (i < nv) yv[i] = epi_float<bf16_t>(yv[i], e, k, off + i);
 }
 
-// Two bf16 (the halves of dword w) -> fp16 pair; p selects the half of each
-// source word (0: low, 1: high).
-__device__ __forceinline__ uint32_t cvt_pair(uint32_t wlo, uint32_t whi, int p) {
-    const float flo = __uint_as_float(p ? (wlo & 0xffff0000u) : (wlo << 16));
-    const float fhi = __uint_as_float(p ? (whi & 0xffff0000u) : (whi << 16));
+// Two bf16 (the halves of dword w), times the power-of-two scale sc -> fp16
+// pair; p selects the half of each source word (0: low, 1: high).
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t wlo, uint32_t whi, int p, float sc) {
+    const float flo = __uint_as_float(p ? (wlo & 0xffff0000u) : (wlo << 16)) * sc;
+    const float fhi = __uint_as_float(p ? (whi & 0xffff0000u) : (whi << 16)) * sc;
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(flo, fhi));
 }
 
@@ -184,6 +188,8 @@ __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
     using G = Geo<TCB>;
     constexpr int TR = G::TR, PUE = G::PUE, MAXU = G::MAXU;
     constexpr F2 f2 = build_f2();
+    const float xsc = wg_norm(a.xmax);  // input scale into the fp16 range
+    const int osx = wg_shift(a.xmax), osw = wg_shift(a.wmax);  // and the shifts undoing both
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -252,10 +258,10 @@ __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
             for (int p = 0; p < 8; ++p) {
                 const int off = (((PWO + p) & 1) * PUE + ((PWO + p) >> 1)) * PIX;
                 uint4 o;
-                o.x = cvt_pair(word_of(stg[i][0], p >> 1), word_of(stg[i][1], p >> 1), p & 1);
-                o.y = cvt_pair(word_of(stg[i][2], p >> 1), word_of(stg[i][3], p >> 1), p & 1);
-                o.z = cvt_pair(word_of(stg[i][4], p >> 1), word_of(stg[i][5], p >> 1), p & 1);
-                o.w = cvt_pair(word_of(stg[i][6], p >> 1), word_of(stg[i][7], p >> 1), p & 1);
+                o.x = cvt_pair(word_of(stg[i][0], p >> 1), word_of(stg[i][1], p >> 1), p & 1, xsc);
+                o.y = cvt_pair(word_of(stg[i][2], p >> 1), word_of(stg[i][3], p >> 1), p & 1, xsc);
+                o.z = cvt_pair(word_of(stg[i][4], p >> 1), word_of(stg[i][5], p >> 1), p & 1, xsc);
+                o.w = cvt_pair(word_of(stg[i][6], p >> 1), word_of(stg[i][7], p >> 1), p & 1, xsc);
                 *reinterpret_cast<uint4*>(base + off) = o;
             }
         }
@@ -485,7 +491,7 @@ __global__ __launch_bounds__(NTHR) void wf2_kernel(Args a) {
                     if (co > 0) s += z[w][e];
                     if (co < 0) s -= z[w][e];
                 }
-                yv[e] = s;
+                yv[e] = wg_denorm(s, osx, osw);
             }
             const long long yo = n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
             if constexpr (EPI) epi8(yv, a.e, k, yo, a.OW - ow0);
@@ -521,6 +527,8 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
     using G = Geo<TCB>;
     constexpr int TR = G::TR, PUE = G::PUE, MAXU = G::MAXU;
     constexpr F2 f2 = build_f2();
+    const float xsc = wg_norm(a.xmax);  // input scale into the fp16 range
+    const int osx = wg_shift(a.xmax), osw = wg_shift(a.wmax);  // and the shifts undoing both
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -583,10 +591,10 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
             for (int p = 0; p < 8; ++p) {
                 const int off = (((PWO + p) & 1) * PUE + ((PWO + p) >> 1)) * PIX;
                 uint4 o;
-                o.x = cvt_pair(word_of(stg[i][0], p >> 1), word_of(stg[i][1], p >> 1), p & 1);
-                o.y = cvt_pair(word_of(stg[i][2], p >> 1), word_of(stg[i][3], p >> 1), p & 1);
-                o.z = cvt_pair(word_of(stg[i][4], p >> 1), word_of(stg[i][5], p >> 1), p & 1);
-                o.w = cvt_pair(word_of(stg[i][6], p >> 1), word_of(stg[i][7], p >> 1), p & 1);
+                o.x = cvt_pair(word_of(stg[i][0], p >> 1), word_of(stg[i][1], p >> 1), p & 1, xsc);
+                o.y = cvt_pair(word_of(stg[i][2], p >> 1), word_of(stg[i][3], p >> 1), p & 1, xsc);
+                o.z = cvt_pair(word_of(stg[i][4], p >> 1), word_of(stg[i][5], p >> 1), p & 1, xsc);
+                o.w = cvt_pair(word_of(stg[i][6], p >> 1), word_of(stg[i][7], p >> 1), p & 1, xsc);
                 *reinterpret_cast<uint4*>(base + off) = o;
             }
         }
@@ -815,6 +823,8 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
                         if (co < 0) yv[e] -= zz[e];
                     }
                 }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) yv[e] = wg_denorm(yv[e], osx, osw);
                 if constexpr (EPI)
                     epi8(yv, a.e, kt * KB2 + hb * 64 + kl,
                          (ybase - a.y) + static_cast<long long>(kl) * a.OH * a.OW + pc * 8, 8);
@@ -858,7 +868,7 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
                         if (co > 0) s += z[w][e];
                         if (co < 0) s -= z[w][e];
                     }
-                    yv[e] = s;
+                    yv[e] = wg_denorm(s, osx, osw);
                 }
                 const long long yo = n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW + ow0;
                 if constexpr (EPI) epi8(yv, a.e, k, yo, a.OW - ow0);
@@ -884,8 +894,10 @@ __global__ __launch_bounds__(NTHR) void wf2f_kernel(Args a) {
 // K and C.
 template <int KBT>
 __global__ __launch_bounds__(256) void wf2_prepare_kernel(const uint16_t* __restrict__ w, _Float16* __restrict__ out,
-                                                          int K, int C, int ntk, int nchunks) {
+                                                          int K, int C, int ntk, int nchunks,
+                                                          const unsigned* __restrict__ wmax) {
     constexpr F2 f2 = build_f2();
+    const float wsc = wg_norm(wmax);  // filter scale into the fp16 range
     const long long total = static_cast<long long>(ntk) * KBT * nchunks * CK;
     for (long long idx = blockIdx.x * 256LL + threadIdx.x; idx < total; idx += static_cast<long long>(gridDim.x) * 256) {
         const int c = static_cast<int>(idx % (nchunks * CK));
@@ -916,7 +928,7 @@ __global__ __launch_bounds__(256) void wf2_prepare_kernel(const uint16_t* __rest
                 const long long base =
                     ((((((static_cast<long long>(kt) * nchunks + chunk) * 16 + (4 * i + j)) * (KBT / 32) + b) * 2 + ks) * 32 +
                       mm) * 2 + hh) * 8 + e;
-                out[base] = static_cast<_Float16>(acc);
+                out[base] = static_cast<_Float16>(acc * wsc);
             }
     }
 }
@@ -960,7 +972,7 @@ inline bool plan(const Prob& p, int kb, Plan* pl, std::string* why) {
 
 template <int TCB, int PWO, bool FOLD>
 cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void* vp, void* y, const Epi& e,
-                       hipStream_t st) {
+                       const unsigned* xmax, const unsigned* wmax, hipStream_t st) {
     using G = Geo<TCB>;
     static_assert(G::LDS <= 160 * 1024, "LDS budget");
     if (pl.nblk > G::NBMAX) return set_error(CFWD_ERR_UNSUPPORTED, "winograd fused: patch wider than planned");
@@ -978,6 +990,8 @@ cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void*
     a.x_img = p.x_img; a.y_img = p.y_img;
     a.tbh = pl.tbh; a.tbw = pl.tbw; a.ntk = pl.ntk; a.nchunks = pl.nchunks; a.nblk = pl.nblk;
     a.e = e;
+    a.xmax = xmax;
+    a.wmax = wmax;
     const unsigned blocks = static_cast<unsigned>(static_cast<long long>(p.n) * pl.tbh * pl.tbw * pl.ntk);
     kern<<<blocks, NTHR, G::LDS, st>>>(a);
     return check_hip(hipGetLastError(), "winograd fused launch");
@@ -985,15 +999,15 @@ cfwd_status launch_tcb(const Prob& p, const Plan& pl, const void* x, const void*
 
 template <bool FOLD>
 cfwd_status launch_fold(const Prob& p, const Plan& pl, const void* x, const void* wp, void* y, const Epi& e,
-                        hipStream_t st) {
+                        const unsigned* xmax, const unsigned* wmax, hipStream_t st) {
     const bool p1 = p.pw == 1;
     switch (pl.tcb) {
         case 32:
-            return p1 ? launch_tcb<32, 1, FOLD>(p, pl, x, wp, y, e, st) : launch_tcb<32, 0, FOLD>(p, pl, x, wp, y, e, st);
+            return p1 ? launch_tcb<32, 1, FOLD>(p, pl, x, wp, y, e, xmax, wmax, st) : launch_tcb<32, 0, FOLD>(p, pl, x, wp, y, e, xmax, wmax, st);
         case 16:
-            return p1 ? launch_tcb<16, 1, FOLD>(p, pl, x, wp, y, e, st) : launch_tcb<16, 0, FOLD>(p, pl, x, wp, y, e, st);
+            return p1 ? launch_tcb<16, 1, FOLD>(p, pl, x, wp, y, e, xmax, wmax, st) : launch_tcb<16, 0, FOLD>(p, pl, x, wp, y, e, xmax, wmax, st);
         default:
-            return p1 ? launch_tcb<8, 1, FOLD>(p, pl, x, wp, y, e, st) : launch_tcb<8, 0, FOLD>(p, pl, x, wp, y, e, st);
+            return p1 ? launch_tcb<8, 1, FOLD>(p, pl, x, wp, y, e, xmax, wmax, st) : launch_tcb<8, 0, FOLD>(p, pl, x, wp, y, e, xmax, wmax, st);
     }
 }
 
@@ -1010,7 +1024,8 @@ bool winograd_fused_supported(const Prob& p, int cfg, std::string* why) {
 
 size_t winograd_fused_filter_bytes(const Prob& p, int cfg) {
     wf::Plan pl;
-    return wf::plan(p, wf::kb_of(cfg), &pl, nullptr) ? pl.v_bytes : 0;
+    // the transformed filter, then 8 KiB holding its largest magnitude
+    return wf::plan(p, wf::kb_of(cfg), &pl, nullptr) ? pl.v_bytes + 8192 : 0;
 }
 
 cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
@@ -1020,22 +1035,32 @@ cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* 
     if (!wf::plan(p, kb, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     const long long total = static_cast<long long>(pl.ntk) * kb * pl.nchunks * wf::CK;
     const unsigned nb = static_cast<unsigned>(std::min<long long>((total + 255) / 256, 65536));
+    unsigned* wmax = reinterpret_cast<unsigned*>(static_cast<uint8_t*>(wp) + pl.v_bytes);
+    cfwd_status s = bf16_absmax(w, static_cast<long long>(p.k) * p.c * 9, wmax, st);
+    if (s != CFWD_OK) return s;
     if (kb == wf::KB2)
         wf::wf2_prepare_kernel<wf::KB2><<<nb, 256, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<_Float16*>(wp),
-                                                             p.k, p.c, pl.ntk, pl.nchunks);
+                                                             p.k, p.c, pl.ntk, pl.nchunks, wmax);
     else
         wf::wf2_prepare_kernel<wf::KB><<<nb, 256, 0, st>>>(static_cast<const uint16_t*>(w), static_cast<_Float16*>(wp),
-                                                            p.k, p.c, pl.ntk, pl.nchunks);
+                                                            p.k, p.c, pl.ntk, pl.nchunks, wmax);
     return check_hip(hipGetLastError(), "winograd fused filter transform launch");
 }
 
-cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, const Epi& e,
-                                  hipStream_t st) {
+cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* scratch, void* y,
+                                  const Epi& e, hipStream_t st) {
     wf::Plan pl;
     std::string why;
     if (!wf::plan(p, wf::kb_of(cfg), &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
-    if (wp == nullptr) return set_error(CFWD_ERR_WORKSPACE, "winograd fused: prepared filter is required");
-    return cfg == 2 ? wf::launch_fold<true>(p, pl, x, wp, y, e, st) : wf::launch_fold<false>(p, pl, x, wp, y, e, st);
+    if (wp == nullptr || scratch == nullptr)
+        return set_error(CFWD_ERR_WORKSPACE, "winograd fused: prepared filter and scratch are required");
+    // this call's largest input magnitude, in the scratch
+    unsigned* xmax = static_cast<unsigned*>(scratch);
+    cfwd_status s = bf16_absmax(x, static_cast<long long>(p.n) * p.x_img, xmax, st);
+    if (s != CFWD_OK) return s;
+    const unsigned* wmax = reinterpret_cast<const unsigned*>(static_cast<const uint8_t*>(wp) + pl.v_bytes);
+    return cfg == 2 ? wf::launch_fold<true>(p, pl, x, wp, y, e, xmax, wmax, st)
+                    : wf::launch_fold<false>(p, pl, x, wp, y, e, xmax, wmax, st);
 }
 
 }  // namespace cfwd

@@ -18,7 +18,17 @@
  *                   are staged in LDS and multiplied on the matrix cores.
  *   WINOGRAD_F2X2_3X3 / WINOGRAD_F6X6_3X3
  *                   F(m x m, 3 x 3) minimal filtering for 3x3, stride 1,
- *                   dilation 1, groups 1, float dtypes only.
+ *                   dilation 1, groups 1, float dtypes only.  bf16 runs its
+ *                   transformed operands in fp16 (11 significant bits); to
+ *                   keep them in fp16's range, input and filter are scaled by
+ *                   powers of two that bring each one's largest magnitude
+ *                   (found on the device: the input's on every call, the
+ *                   filter's when it is prepared) into [2^7, 2^8), and the
+ *                   output is scaled back -- exactly, so any finite
+ *                   magnitudes work.  Values below 2^-22 of their tensor's
+ *                   largest magnitude become fp16 subnormals and lose
+ *                   precision; the Fast-Run accuracy gate sees that on the
+ *                   caller's data.
  *   DIRECT          direct summation; the depthwise (G = C = K) path.
  *   POINTWISE       1x1 convolution as a low-K matrix product.
  *   AUTO            resolved per problem: a Fast-Run map entry if one exists,
@@ -162,7 +172,9 @@ cfwd_status cfwd_workspace_size(const cfwd_conv_desc *desc, cfwd_algo algo, size
 
 /* Workspace bytes conv2d_fwd needs for `algo` when it is given a prepared
  * filter: the algorithm's scratch only (Winograd: the transformed input
- * tiles B^T d B, alpha^2 x ceil(C / chunk) x tiles x 64 bytes).  0 when none. */
+ * tiles B^T d B, alpha^2 x ceil(C / chunk) x tiles x 64 bytes, and for bf16
+ * 8 KiB for the input's largest magnitude; implicit GEMM split
+ * reductions: their int32 partial tiles).  0 when none. */
 cfwd_status cfwd_scratch_size(const cfwd_conv_desc *desc, cfwd_algo algo, size_t *bytes);
 
 /* y = conv(x, w).  w_kcrs is required.  w_prepared may be NULL; when it is

@@ -235,3 +235,28 @@ def test_fastrun_stale_workspace_nchw4_k37(dtype):
     check_float("auto after stale ws", output_to_host(y2, dtype, "NCHWX", L.k), yref, den, dtype,
                 B.algo_name(best))
     B.fastrun_clear()
+
+
+@pytest.mark.parametrize("magnitude", [1e3, 1e-6], ids=["x1e3", "x1e-6"])
+def test_bf16_magnitudes_every_candidate(magnitude):
+    """bf16 inputs and weights far from unit scale, every candidate (Winograd
+    included: its fp16 operands are scaled into range by powers of two),
+    against the oracle within the bf16 bound.  Unscaled, 1e3 would overflow
+    fp16 in F(6x6)'s transform and 1e-6 would be an fp16 subnormal."""
+    torch_cuda()
+    L = Layer("mag", 64, 40, 20, 24, 3, 3, 1, 1)
+    pr = random_float_problem(L, 2, "bf16", 77)
+    from cnn_convolution_fwd_amd.workloads import round_to_bf16
+    x = round_to_bf16(pr.x * np.float32(magnitude))
+    w = round_to_bf16(pr.w * np.float32(magnitude ** 0.5))
+    yref, den = oracle.conv2d(x, w, 1, 1)
+    cands = candidates_for((2, 64, 20, 24, 40, 3, 3), "bf16", 1, 1)
+    assert any(a.startswith("winograd") for a, _ in cands)
+    failures = []
+    for algo, cfg in cands:
+        say("magnitude", magnitude, algo, cfg)
+        y = run_conv(x, w, "bf16", 1, 1, algo=algo, config_id=cfg)
+        err = oracle.normalised_error(y, yref, den)
+        if not err <= tol_for("bf16", algo):
+            failures.append("%s/%d: error %.3g" % (algo, cfg, err))
+    assert not failures, "; ".join(failures)
