@@ -30,7 +30,7 @@ steps run, and the CPU oracle timed on a bounded sample of the same workload
 (threads used, host CPU model).
 
     python bench.py [--workload NAME] [--n N] [--dtype bf16|f32|i8] [--algo auto|family[/cfg]]
-                    [--steps K] [--warmup W]
+                    [--steps K] [--warmup W] [--layers I,J] [--fastrun-load F] [--fastrun-save F]
     python bench.py --copy-calibration    # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -91,6 +91,10 @@ def parse():
                          "into the convolution, or as separate elementwise passes after it")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle CPU work at most")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--layers", default="", help="comma-separated layer indices of the workload to run (default: all)")
+    ap.add_argument("--fastrun-load", default="", help="Fast-Run map file to load before set-up (its problems are not "
+                    "searched again)")
+    ap.add_argument("--fastrun-save", default="", help="write the Fast-Run map to this file after set-up")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of 1 GiB instead (scales HBM byte counters)")
     return ap.parse_args()
@@ -177,6 +181,12 @@ def main():
         print("unknown workload %s" % a.workload, file=sys.stderr)
         sys.exit(2)
     cfg_idx, layer_ids, dtypes = WORKLOADS[base]
+    if a.layers:
+        pick = [int(v) for v in a.layers.split(",")]
+        if not pick or any(li not in layer_ids for li in pick):
+            print("workload %s has layers %s" % (base, layer_ids), file=sys.stderr)
+            sys.exit(2)
+        layer_ids = pick
     cfg = CONFIGS[cfg_idx]
     dtype = a.dtype or dtypes[0]
     if dtype not in dtypes:
@@ -186,7 +196,7 @@ def main():
         print("an unfused int8 epilogue would need the int32 accumulators; use --epilogue fused", file=sys.stderr)
         sys.exit(2)
     N = a.n or cfg.n
-    workload = "%s_n%d" % (base, N)
+    workload = "%s_n%d" % (base, N) + ("_layers%s" % "-".join(str(li) for li in layer_ids) if a.layers else "")
     dev = torch.device("cuda:0")
     int8 = dtype == "i8"
     layout = "NCHWX" if int8 else "NCHW"
@@ -198,6 +208,8 @@ def main():
             return torch.from_numpy(np.ascontiguousarray(arr, np.int8)).to(dev)
         return torch.from_numpy(np.ascontiguousarray(arr, np.float32)).to(dev)
 
+    if a.fastrun_load:
+        B.fastrun_load(a.fastrun_load)
     # ---- per-layer set-up: inputs, algorithm (Fast-Run), prepared filter, scratch.
     # LayerPlan is the same sequence of library calls the parity tests run.
     layers = []
@@ -227,6 +239,9 @@ def main():
         plan = B.LayerPlan(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c, requant_scale=scale,
                            algo_spec=a.algo, bias=bias if fused else None, relu=relu and fused)
         layers.append(dict(L=L, pr=pr, x0=x0, y0=plan.new_output(), plan=plan, bias=bias, res0=res0, relu=relu))
+
+    if a.fastrun_save:
+        B.fastrun_save(a.fastrun_save)
 
     # every layer rotates over its own buffer sets, > 512 MB per layer, so a
     # layer timed alone (per-kernel figures) cannot read from the cache either
@@ -351,7 +366,8 @@ def main():
         "config": {
             "workload": workload, "n": N, "layers": nl, "layout": layout,
             "algo": "+".join(sorted({p["algo"] for p in per_layer})),
-            "dispatch": "fastrun_map" if a.algo == "auto" else "fixed", "rotated_buffer_sets": max(l["nsets"] for l in layers),
+            "dispatch": "fastrun_map" if a.algo == "auto" else "fixed",
+            "fastrun_map_loaded": os.path.basename(a.fastrun_load) or None, "rotated_buffer_sets": max(l["nsets"] for l in layers),
             "gflop_per_step": round(total_flops / 1e9, 3),
             "mb_per_step": round(sum(p["bytes"] for p in per_layer) / 1e6, 2),
             "warm_ms_per_step": round(warm_ms, 5),

@@ -391,9 +391,10 @@ def fastrun_select(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW
 class LayerPlan:
     """One conv layer set up the way an inference step runs it.
 
-    ``algo="auto"``: the Fast-Run selection phase runs once on (x, w) and
-    records its choice in the map; launches then pass AUTO, so the library
-    dispatches from the map (execution phase).  Otherwise the named family
+    ``algo="auto"``: unless the map already holds the problem, the Fast-Run
+    selection phase runs once on (x, w) and records its choice in the map;
+    launches then pass AUTO, so the library dispatches from the map
+    (execution phase).  Otherwise the named family
     (and config, "family/cfg") is resolved once and passed explicitly.  The
     filter is prepared once (constant weights) and the algorithm's scratch is
     allocated once; ``prepare_ms`` is the prepare step's device time.
@@ -409,8 +410,12 @@ class LayerPlan:
         self.out_shape = _out_shape(self.desc)
         self.dtype, self.device = x.dtype, x.device
         if algo_spec == "auto":
-            best, _ = fastrun_select(x, w, stride, padding, dilation, groups, layout, channels,
-                                     requant_scale=requant_scale)
+            # a problem already in the map (an earlier layer of the same shape,
+            # or a map loaded from a file) is dispatched from it unsearched
+            best = fastrun_lookup(self.desc)
+            if best is None:
+                best, _ = fastrun_select(x, w, stride, padding, dilation, groups, layout, channels,
+                                         requant_scale=requant_scale)
             self.chosen = resolve_algo(self.desc, algo())
             if self.chosen.key() != best.key():
                 raise RuntimeError("AUTO resolves to %s, Fast-Run chose %s" % (algo_name(self.chosen),

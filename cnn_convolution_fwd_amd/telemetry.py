@@ -196,11 +196,22 @@ class Sampler:
         return self.summary()
 
     def summary(self) -> Dict[str, object]:
-        """Median / min / max over the samples taken while the GPU was busy
-        (graphics activity >= 90% where the source reports it)."""
-        busy = [s for s in self.samples if s.get("activity_pct", 100.0) >= 90.0]
+        """Median / min / max over the samples taken while the GPU was busy:
+        graphics activity >= 90% where the source reports it, or >= 50% when
+        fewer than 5 samples reach 90% (steps of many short kernels, whose
+        launch gaps lower the averaged activity figure)."""
+        busy, thr = [], 90.0
+        for thr in (90.0, 50.0):
+            busy = [s for s in self.samples if s.get("activity_pct", 100.0) >= thr]
+            if len(busy) >= 5:
+                break
         out: Dict[str, object] = {"source": self.source, "pci_bus_id": self.bdf, "samples": len(self.samples),
-                                  "busy_samples": len(busy)}
+                                  "busy_samples": len(busy), "busy_threshold_pct": thr}
+        act = [s["activity_pct"] for s in self.samples if "activity_pct" in s]
+        if act:
+            out["activity_pct_median"] = round(statistics.median(act), 1)
+        else:  # no activity figure: every sample counts
+            out["busy_threshold_pct"] = None
         for key, name in (("sclk_mhz", "sclk_mhz"), ("power_w", "power_w")):
             v = [s[key] for s in busy if key in s]
             if v:
