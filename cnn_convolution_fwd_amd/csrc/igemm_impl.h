@@ -354,8 +354,9 @@ template <typename T> struct Frag<T, 32> {
 // EPI: the fused epilogue (bias, residual, ReLU) is applied as outputs are
 // converted; a separate instantiation, so the plain kernels carry none of
 // its registers.
+// RES: resident input (int8 NCHW4, 3x3 or 1x1 filters; see the main loop).
 template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false,
-          bool EPI = false>
+          bool EPI = false, bool RES = false>
 __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
     constexpr int NT = WN * FN * FR;
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     };
 
     uint4 bcur[FN][NP], bnxt[FN][NP];
-    if constexpr (RSV != 9) {
+    if constexpr (RSV != 9 && !RES) {
         load_b(bcur, 0);
         stage_load(0, stg);
         stage_store(0, stg);
@@ -622,7 +623,172 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 
     const int total_it = nch * RS;
     int it = 0;
-    if constexpr (RSV == 9 && FR == 32) {
+    if constexpr (RES) {
+        // ---- resident input (deep layers with small images: ResNet's 14x14
+        // and 7x7 stages).  A layer with a long reduction and few output
+        // pixels has few tiles, so each CU runs one or two workgroups, and
+        // staging one channel chunk at a time leaves every chunk's load
+        // latency (and barrier) exposed.  Here the input rows the tile reads
+        // -- whole rows, every channel chunk -- are requested at once, written
+        // to LDS, and after one barrier the taps run from LDS with no further
+        // barrier: only the weights stream in, one or two chunks ahead.
+        //
+        // The rows [r0, r1) of an image are one flat run of pixels in each
+        // NCHW4 channel-block plane, so they are staged as 16-byte loads of 4
+        // consecutive flat pixels (buffer loads: the run's last group may
+        // reach past the tensor, which reads as zero), transposed in
+        // registers into 4 pixels x 16 bytes of channels.  No halo is kept:
+        // a tap that falls outside the image (or a tile row past the batch)
+        // reads a zeroed pixel slot instead.
+        //
+        // LDS per chunk: image tn's pixel (ih, iw) at slot q = tn * e4 +
+        // (ih - r0) * W + iw (e4: the run rounded up to 4 pixels), the zero
+        // slot at TN * e4; 64 bytes of channels per slot, its 16-byte part j
+        // at position j ^ ((q >> SW) & 3) (the lanes of one fragment read,
+        // consecutive pixels of one part, spread over the banks).
+        static_assert(sizeof(T) == 1 && XB == 4 && !SPLIT && (RSV == 9 || RSV == 1),
+                      "resident input: int8 NCHW4, 3x3 or 1x1");
+        constexpr int SW = (FR == 32) ? 2 : 1;
+        const int r0 = max(ih0, 0), r1 = min(ih0 + a.PH, a.H);
+        const int p0 = r0 * a.W;
+        const int e4 = (max(r1 - r0, 0) * a.W + 3) & ~3;
+        const int zq = a.TN * e4;
+        const int chunk_bytes = (zq + 1) * 64;
+        {
+            const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<T*>(x), static_cast<short>(0), static_cast<int>(static_cast<long long>(a.N) * a.x_img),
+                0x00020000);
+            const unsigned HW = static_cast<unsigned>(a.H * a.W);
+            const int g4 = e4 / 4;                   // 4-pixel groups per image
+            const int units = nch * a.TN * g4 * 4;   // (chunk, image, group, 16-byte part)
+            for (int i = tid; i < nch * 4; i += NTHR)
+                *reinterpret_cast<uint4*>(lds + (i >> 2) * chunk_bytes + zq * 64 + (i & 3) * 16) = make_uint4(0, 0, 0, 0);
+            constexpr int MB = 4;  // units per thread in flight
+            for (int u0 = 0; u0 < units; u0 += MB * NTHR) {
+                uint4 ld[MB][4];
+                int dc[MB], dq[MB], dj[MB];  // chunk buffer, first slot, 16-byte part (dq < 0: none)
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const int u = u0 + m * NTHR + tid;
+                    const int j = u & 3;
+                    int rest = u >> 2;
+                    const int g = rest % g4;
+                    rest /= g4;
+                    const int tn = rest % a.TN;
+                    const int c = rest / a.TN;
+                    const int n = n0 + tn;
+                    const bool ok = u < units && n < a.N;
+                    // channel blocks 16 c + 4 j + b, pixels p0 + 4 g .. + 3
+                    const unsigned base = static_cast<unsigned>(n * a.x_img) +
+                                          ((static_cast<unsigned>(16 * c + 4 * j)) * HW + p0 + 4 * g) * 4u;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        // past the buffer's range (all of x is below 2^31 bytes): reads zero
+                        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ok ? base + b * HW * 4u : 0x80000000u, 0, 0);
+                        ld[m][b] = make_uint4(v[0], v[1], v[2], v[3]);
+                    }
+                    dc[m] = c * chunk_bytes;
+                    dq[m] = (u < units) ? tn * e4 + 4 * g : -1;
+                    dj[m] = j;
+                }
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    if (dq[m] < 0) continue;
+#pragma unroll
+                    for (int pp = 0; pp < 4; ++pp) {
+                        const int q = dq[m] + pp;
+                        *reinterpret_cast<uint4*>(lds + dc[m] + (q << 6) + ((dj[m] ^ ((q >> SW) & 3)) << 4)) =
+                            wide_pick<4>(ld[m], pp);
+                    }
+                }
+            }
+        }
+        // weights: a ring of D tap buffers, each refilled right after its
+        // use with the tap D ahead -- two chunks (3x3) or sixteen taps (1x1)
+        // where a tap's weights are at most two 16-byte pieces per lane, one
+        // chunk or eight taps otherwise (an L2 hit takes about a thousand
+        // cycles under this load, several taps' worth of matrix-core work)
+        constexpr bool DEEP = FN * NP <= 2;
+        constexpr int D = (RSV == 9) ? (DEEP ? 18 : 9) : (DEEP ? 16 : 8);
+        // taps per loop body: a multiple of the ring (ring slots and taps
+        // known at compile time) and even (A double buffer, below)
+        constexpr int U = (RSV == 9) ? 18 : 16;
+        const int last_it = total_it - 1;
+        uint4 wr[D][FN][NP];
+#pragma unroll
+        for (int d = 0; d < D; ++d) load_b(wr[d], min(d, last_it));
+        // A byte offsets inside a chunk buffer, per tap and fragment (piece 1
+        // of a 32x32 fragment is slot 2 + h: the address with bit 5 flipped)
+        int boff[RSV][FM];
+#pragma unroll
+        for (int f = 0; f < FM; ++f) {
+            // this lane's output pixel of fragment f and the input pixel of tap (0, 0)
+            const int p = (wm * FM + f) * FR + lrow;
+            const int tn = p / thw;
+            const int rem = p - tn * thw;
+            const int ohl = rem / a.TW;
+            const int owl = rem - ohl * a.TW;
+            const bool prow = p < tile_pix && n0 + tn < a.N;
+            const int ihb = (oh0 + ohl) * a.sh - a.ph;
+            const int iwb = (ow0 + owl) * a.sw - a.pw;
+#pragma unroll
+            for (int t = 0; t < RSV; ++t) {
+                const int ih = ihb + (t / a.S) * a.dh, iw = iwb + (t % a.S) * a.dw;
+                const bool ok = prow && static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) &&
+                                static_cast<unsigned>(iw) < static_cast<unsigned>(a.W);
+                const int q = ok ? tn * e4 + ih * a.W + iw - p0 : zq;
+                boff[t][f] = (q << 6) + ((pslot[0] ^ ((q >> SW) & 3)) << 4);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);  // every direct load has landed (and the first weights)
+        __syncthreads();
+        // A double buffer: the next tap's fragments are requested before
+        // this tap's matrix-core instructions, which then cover the LDS latency
+        uint4 ra[2][FM][NP];
+        auto read_a = [&](uint4 (&dst)[FM][NP], const uint8_t* pb, int t) {
+#pragma unroll
+            for (int f = 0; f < FM; ++f) {
+                const uint8_t* pa = pb + boff[t][f];
+                dst[f][0] = *reinterpret_cast<const uint4*>(pa);
+                if constexpr (NP == 2)
+                    dst[f][1] = *reinterpret_cast<const uint4*>(lds + ((static_cast<int>(pa - lds)) ^ 32));
+            }
+        };
+        // tap it0 + d; it0 is a multiple of U (so of 9 for 3x3 filters)
+        auto tap = [&](int it0, int d) {
+            const int itd = it0 + d;
+            // the tap after this one (at the very end: tap 0 of the last
+            // chunk, read and never used)
+            const int itn = min(itd + 1, last_it);
+            const int cn = (RSV == 9) ? itn / 9 : itn;
+            read_a(ra[(d + 1) & 1], lds + cn * chunk_bytes, (RSV == 9) ? (d + 1) % 9 : 0);
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int nf = 0; nf < FN; ++nf) {
+                    if constexpr (FR == 16)
+                        Mma<T>::run(acc[f][nf], ra[d & 1][f][0], wr[d % D][nf][0]);
+                    else
+                        Mma32<T>::run(acc[f][nf], ra[d & 1][f][0], ra[d & 1][f][1], wr[d % D][nf][0],
+                                      wr[d % D][nf][1]);
+                }
+            load_b(wr[d % D], min(itd + D, last_it));
+        };
+        read_a(ra[0], lds, 0);
+        // whole loop bodies without a branch inside (the compiler can then
+        // count the loads in flight across iterations), then the remainder
+        const int nfull = total_it / U;
+        for (int o = 0; o < nfull; ++o) {
+#pragma unroll
+            for (int d = 0; d < U; ++d) tap(o * U, d);
+        }
+        const int rem = total_it - nfull * U;
+#pragma unroll
+        for (int d = 0; d < U; ++d)
+            if (d < rem) tap(nfull * U, d);
+        it = total_it;
+        __syncthreads();  // the epilogue reuses the patch's LDS
+    } else if constexpr (RSV == 9 && FR == 32) {
         // 3x3 (nine-tap) filters, 32x32 fragments, wide staging: the nine taps
         // of a chunk are unrolled so that every register buffer is addressed
         // at compile time (a copy between prefetch buffers would make the
@@ -1441,6 +1607,97 @@ inline size_t split_scratch_bytes(const Prob& p, int sc) {
     return static_cast<size_t>(kSplitCfgs[sc].splits) * p.n * static_cast<size_t>(p.y_img) * 4;
 }
 
+// Resident-input configs (int8 NCHW4, 3x3 or 1x1): the base tile configs
+// whose kernel holds the input rows of every channel chunk in LDS at once
+// (RES in the kernel).  For layers with deep reductions and small images.
+constexpr int kResCfgs[] = {2, 3, 6, 11, 12, 13, 14, 16};
+constexpr int kNumResCfgs = sizeof(kResCfgs) / sizeof(kResCfgs[0]);
+
+// Geometry of resident config `rc`: tiles of whole output rows as geometry()
+// picks them, shrunk until the input rows of all channel chunks fit in LDS.
+inline bool res_geometry(const Prob& p, int rc, Geo* g, std::string* why) {
+    if (rc < 0 || rc >= kNumResCfgs) {
+        if (why) *why = "implicit GEMM: no such resident-input config";
+        return false;
+    }
+    const Cfg c = kCfgs[kResCfgs[rc]];
+    if (p.dtype != CFWD_I8 || p.layout != CFWD_LAYOUT_NCHWX || p.xb != 4 || p.g != 1) {
+        if (why) *why = "implicit GEMM resident input: int8 NCHW4 with groups 1 only";
+        return false;
+    }
+    if (!((p.r == 3 && p.s == 3) || (p.r == 1 && p.s == 1))) {
+        if (why) *why = "implicit GEMM resident input: 3x3 or 1x1 filters only";
+        return false;
+    }
+    if (p.cg % 64 != 0) {
+        if (why) *why = "implicit GEMM resident input: input channels must be a multiple of 64";
+        return false;
+    }
+    if (static_cast<long long>(p.n) * p.x_img >= (1LL << 31)) {
+        if (why) *why = "implicit GEMM resident input: input must be below 2 GiB";
+        return false;
+    }
+    const int nch = p.cg / 64;
+    const int P = c.pixels();
+    // tiles of whole output rows (TN whole images, or TH rows of one)
+    if (p.ow > P) {
+        if (why) *why = "implicit GEMM resident input: an output row is wider than the tile";
+        return false;
+    }
+    int TN, TH;
+    const int TW = p.ow;
+    if (p.oh * p.ow <= P) {
+        TN = std::min(p.n, P / (p.oh * p.ow));
+        TH = p.oh;
+    } else {
+        TN = 1;
+        TH = std::min(p.oh, P / p.ow);
+    }
+    // LDS: per chunk, TN runs of the input rows the tile reads (at most
+    // min(PH, H) rows of W pixels, rounded up to 4 pixels) and a zero slot,
+    // 64 bytes each
+    int PH = 0, PW = 0;
+    long long slots = 0;
+    for (;;) {
+        PH = (TH - 1) * p.sh + (p.r - 1) * p.dh + 1;
+        PW = (TW - 1) * p.sw + (p.s - 1) * p.dw + 1;
+        slots = static_cast<long long>(TN) * ((static_cast<long long>(std::min(PH, p.h)) * p.w + 3) & ~3LL) + 1;
+        if (nch * slots * 64 <= static_cast<long long>(kLdsBytes)) break;
+        if (TN > 1)
+            --TN;
+        else if (TH > 1)
+            --TH;
+        else {
+            if (why) *why = "implicit GEMM resident input: the rows of one output row do not fit in LDS";
+            return false;
+        }
+    }
+    g->TN = TN;
+    g->TH = TH;
+    g->TW = TW;
+    g->PH = PH;
+    g->PW = PW;
+    g->npix = TN * PH * PW;
+    g->tiles_n = (p.n + TN - 1) / TN;
+    g->tiles_h = (p.oh + TH - 1) / TH;
+    g->tiles_w = (p.ow + TW - 1) / TW;
+    g->nchunks = nch;
+    g->ntk = (p.kg + c.nt() - 1) / c.nt();
+    g->stg = 0;
+    const size_t tile_pix = static_cast<size_t>(TN) * TH * TW;
+    g->lds_bytes = std::max({static_cast<size_t>(nch * slots * 64), static_cast<size_t>(c.pixels()) * 8,
+                             static_cast<size_t>(c.nt() / 4) * (tile_pix * 4 + 16)});
+    if (g->lds_bytes > kLdsBytes) {
+        if (why) *why = "implicit GEMM resident input: the tile needs more LDS than a CU has";
+        return false;
+    }
+    if (static_cast<long long>(g->tiles_n) * g->tiles_h * g->tiles_w * g->ntk > 0x7fffffffLL) {
+        if (why) *why = "implicit GEMM: grid too large";
+        return false;
+    }
+    return true;
+}
+
 inline size_t filter_bytes(const Prob& p, const Cfg& c, const Geo& g) {
     return static_cast<size_t>(p.g) * g.ntk * g.nchunks * p.r * p.s * c.nt() * 64;
 }
@@ -1480,7 +1737,7 @@ template <typename K> cfwd_status allow_big_lds(K kern, size_t lds_bytes, bool* 
 // One launch of a tile config.  SPLIT: `nsplit` workgroups per tile, each
 // summing `cps` channel chunks into its partial tile in `part`.
 template <typename T, int XB, int WM, int WN, int FM, int FN, int STG, int FR, int RSV, bool SPLIT = false,
-          bool EPI = false>
+          bool EPI = false, bool RES = false>
 cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* wp, const float* scale, void* y,
                        const Epi& e, hipStream_t st, int cps = 0, int nsplit = 1, int32_t* part = nullptr) {
     Args a = make_args(p, g, x, wp, scale, y);
@@ -1489,7 +1746,7 @@ cfwd_status launch_one(const Prob& p, const Geo& g, const void* x, const void* w
         a.cps = cps;
         a.part = part;
     }
-    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV, SPLIT, EPI>;
+    auto kern = igemm_kernel<T, XB, WM, WN, FM, FN, STG, FR, RSV, SPLIT, EPI, RES>;
     static bool attr_done = false;
     const cfwd_status s = allow_big_lds(kern, g.lds_bytes, &attr_done);
     if (s != CFWD_OK) return s;
@@ -1600,6 +1857,9 @@ cfwd_status igemm_launch_f32_epi(int cfg, const Prob& p, const ig::Geo& g, const
 cfwd_status igemm_launch_bf16_epi(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
                                   const float* scale, void* y, const Epi& e, hipStream_t st);
 cfwd_status igemm_launch_i8_epi(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
+                                const float* scale, void* y, const Epi& e, hipStream_t st);
+// Resident-patch config rc (k_igemm_i8_res.hip).
+cfwd_status igemm_launch_i8_res(int rc, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
                                 const float* scale, void* y, const Epi& e, hipStream_t st);
 // Split config sc (k_igemm_i8_split.hip): the split kernel, then the reduce
 // kernel that sums the partial tiles in `part` and requantises into y.

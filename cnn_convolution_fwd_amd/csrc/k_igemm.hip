@@ -7,16 +7,28 @@ namespace cfwd {
 // Configs 0 .. kNumCfgs-1: the tiled kernel of igemm_impl.h; the next
 // lowc_num_configs(): the gather form for few input channels (k_lowc.hip);
 // the next kNumSplitCfgs: the tiled kernel with a split reduction
-// (k_igemm_i8_split.hip), whose partial tiles live in the scratch.
+// (k_igemm_i8_split.hip), whose partial tiles live in the scratch; the next
+// kNumResCfgs: the tiled kernel with the resident input (k_igemm_i8_res.hip).
 namespace {
 int split_first() { return ig::kNumCfgs + lowc_num_configs(); }
+int res_first() { return split_first() + ig::kNumSplitCfgs; }
 bool is_lowc(int cfg) { return cfg >= ig::kNumCfgs && cfg < split_first(); }
-bool is_split(int cfg) { return cfg >= split_first() && cfg < split_first() + ig::kNumSplitCfgs; }
-// base tile config of a tiled or split config
-int base_of(int cfg) { return is_split(cfg) ? ig::kSplitCfgs[cfg - split_first()].base : cfg; }
+bool is_split(int cfg) { return cfg >= split_first() && cfg < res_first(); }
+bool is_res(int cfg) { return cfg >= res_first() && cfg < res_first() + ig::kNumResCfgs; }
+// base tile config of a tiled, split or resident config
+int base_of(int cfg) {
+    if (is_split(cfg)) return ig::kSplitCfgs[cfg - split_first()].base;
+    if (is_res(cfg)) return ig::kResCfgs[cfg - res_first()];
+    return cfg;
+}
+// the tiles of a config (a split config has its base config's)
+bool geometry_of(const Prob& p, int cfg, ig::Geo* g, std::string* why) {
+    if (is_res(cfg)) return ig::res_geometry(p, cfg - res_first(), g, why);
+    return ig::geometry(p, ig::kCfgs[base_of(cfg)], g, why);
+}
 }  // namespace
 
-int igemm_num_configs() { return split_first() + ig::kNumSplitCfgs; }
+int igemm_num_configs() { return res_first() + ig::kNumResCfgs; }
 
 bool igemm_supported(const Prob& p, int cfg, std::string* why) {
     if (is_lowc(cfg)) return lowc_supported(p, cfg - ig::kNumCfgs, why);
@@ -25,6 +37,7 @@ bool igemm_supported(const Prob& p, int cfg, std::string* why) {
         int cps;
         return ig::split_geometry(p, cfg - split_first(), &g, &cps, why);
     }
+    if (is_res(cfg)) return ig::res_geometry(p, cfg - res_first(), &g, why);
     if (cfg < 0 || cfg >= ig::kNumCfgs) {
         if (why) *why = "implicit GEMM: no such config";
         return false;
@@ -35,7 +48,7 @@ bool igemm_supported(const Prob& p, int cfg, std::string* why) {
 size_t igemm_filter_bytes(const Prob& p, int cfg) {
     if (is_lowc(cfg)) return lowc_filter_bytes(p, cfg - ig::kNumCfgs);
     ig::Geo g;
-    if (!ig::geometry(p, ig::kCfgs[base_of(cfg)], &g, nullptr)) return 0;
+    if (!geometry_of(p, cfg, &g, nullptr)) return 0;
     return ig::filter_bytes(p, ig::kCfgs[base_of(cfg)], g);
 }
 
@@ -45,10 +58,12 @@ size_t igemm_scratch_bytes(const Prob& p, int cfg) {
 
 cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
     if (is_lowc(cfg)) return lowc_prepare(p, cfg - ig::kNumCfgs, w, wp, st);
-    cfg = base_of(cfg);  // a split config reads its base config's prepared filter
+    // split and resident configs read their base config's prepared filter
+    // (its layout depends only on the output-channel tile and the chunks)
     ig::Geo g;
     std::string why;
-    if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    if (!geometry_of(p, cfg, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    cfg = base_of(cfg);
     switch (p.dtype) {
         case CFWD_F32: return igemm_prepare_f32(cfg, p, g, w, wp, st);
         case CFWD_BF16: return igemm_prepare_bf16(cfg, p, g, w, wp, st);
@@ -66,6 +81,10 @@ cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp, 
         if (!ig::split_geometry(p, cfg - split_first(), &g, &cps, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
         if (scratch == nullptr) return set_error(CFWD_ERR_WORKSPACE, "implicit GEMM split reduction needs scratch");
         return igemm_launch_i8_split(cfg - split_first(), p, g, cps, x, wp, scale, y, scratch, e, st);
+    }
+    if (is_res(cfg)) {
+        if (!ig::res_geometry(p, cfg - res_first(), &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+        return igemm_launch_i8_res(cfg - res_first(), p, g, x, wp, scale, y, e, st);
     }
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     // the fused epilogue has instantiations of its own (no registers of it

@@ -79,6 +79,15 @@ SMALL = [
     ("split_c200_k37", 2, 200, 9, 11, 37, 3, 3, 1, 1, 1, 1),
     ("split_c130_3chunks", 3, 130, 7, 7, 72, 3, 3, 1, 1, 1, 1),
     ("split_1x1_s2_c256", 2, 256, 14, 14, 64, 1, 1, 2, 0, 1, 1),
+    # int8 resident patch (every channel chunk's patch in LDS at once):
+    # stride 2 with a batch that leaves a partial image tile; three chunks
+    # with odd image sizes and K = 40; 1x1 stride 2; dilation 2; a patch too
+    # big for LDS whole (the tile shrinks to fewer rows)
+    ("res_c128_s2_n3", 3, 128, 14, 14, 72, 3, 3, 2, 1, 1, 1),
+    ("res_c192_9x11", 2, 192, 9, 11, 40, 3, 3, 1, 1, 1, 1),
+    ("res_1x1_s2_c128", 3, 128, 13, 13, 72, 1, 1, 2, 0, 1, 1),
+    ("res_d2_c64", 2, 64, 10, 10, 40, 3, 3, 1, 2, 2, 1),
+    ("res_c512_20x20", 1, 512, 20, 20, 64, 3, 3, 1, 1, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
