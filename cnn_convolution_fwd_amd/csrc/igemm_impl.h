@@ -418,8 +418,13 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     // patch buffers in LDS: three on the nine-tap path of big per-wave tiles
     // (chunk c + 1 is staged while chunk c runs; their registers allow one
     // workgroup per CU anyway, so the LDS costs no occupancy), two otherwise
-    constexpr bool TB = (RSV == 9) && (FM * FN >= 8);
+    constexpr bool TB = (RSV == 9) && (FR == 32) && (FM * FN >= 8);
     constexpr int NBUF = TB ? 3 : 2;
+    // buffers actually used: a problem of one or two channel chunks needs no
+    // more than that many (its LDS allocation holds only those, so more
+    // workgroups share a CU); stores and reads of a next chunk are skipped
+    // when there is none
+    const int nbuf = min(nch, NBUF);
     const int ih0 = oh0 * a.sh - a.ph;
     const int iw0 = ow0 * a.sw - a.pw;
     const T* __restrict__ x = static_cast<const T*>(a.x);
@@ -519,7 +524,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             if (STG == 1) {
                 // pixels outside this patch row go to a per-thread dummy slot
                 // past both patch buffers (no branch per pixel)
-                uint8_t* dummy = lds + NBUF * patch_bytes + tid * 16;
+                uint8_t* dummy = lds + nbuf * patch_bytes + tid * 16;
 #pragma unroll
                 for (int p = 0; p < PP; ++p) {
                     const int col = u_pc[i] + p;
@@ -537,16 +542,29 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
     // for chunk `chunk` (wide staging only).  Invalid pixels or channels load
     // from the tensor base and are zeroed afterwards, so every call issues
     // exactly one load and the compiler can count outstanding loads exactly.
+    // The chunk-invariant part of each unit's element offset (image, pixel,
+    // 16-byte channel part) is computed once, so a load costs a 64-bit add:
+    // channel block (c0 / XB + ld) of pixel sp is element
+    // (c0 / XB + ld) * H * W * XB + sp * XB of the image (XB = 1: channel
+    // c0 + ld), and a chunk is CK / XB channel blocks (the wide path only runs
+    // where C / G and the chunk are whole channel blocks).
+    const long long HWX = static_cast<long long>(a.H) * a.W * XB;
+    long long u_base[MAXU];
+#pragma unroll
+    for (int i = 0; i < MAXU; ++i) {
+        const int j = u_j[i] < 0 ? 0 : u_j[i];
+        u_base[i] = (u_sp[i] >= 0) ? u_n[i] * a.x_img + static_cast<long long>((g * a.Cg + j * E16) / XB) * HWX +
+                                         static_cast<long long>(u_sp[i]) * XB
+                                   : 0;
+    }
     auto stage_piece = [&](int chunk, int l) {
         using R = typename Raw<T>::type;
         const int i = l / PP, ld = l % PP;
         const int cl = (chunk + cb) * CK + (u_j[i] < 0 ? 0 : u_j[i]) * E16;
         const int nval = a.Cg - cl;
         const bool valid = (u_sp[i] >= 0) && (XB == 1 ? ld < nval : ld * XB < nval);
-        const int c0 = g * a.Cg + cl;
-        const long long HW = static_cast<long long>(a.H) * a.W;
-        const long long off = (XB == 1) ? (c0 + ld) * HW + u_sp[i] : ((c0 / XB + ld) * HW + u_sp[i]) * XB;
-        const R* src = reinterpret_cast<const R*>(x) + (valid ? u_n[i] * a.x_img + off : 0);
+        const long long off = u_base[i] + static_cast<long long>((chunk + cb) * (CK / XB) + ld) * HWX;
+        const R* src = reinterpret_cast<const R*>(x) + (valid ? off : 0);
         const uint4 v = *reinterpret_cast<const uint4*>(src);
         stg[i][ld] = valid ? v : make_uint4(0, 0, 0, 0);
     };
@@ -831,7 +849,7 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             stage_load(0, stg);
             stage_load(1, stg1);  // zeros past the last chunk
             stage_store(0, stg);
-            stage_store(1, stg1);
+            if (nch > 1) stage_store(1, stg1);
         } else {
             stage_load(0, stg);
             stage_store(0, stg);
@@ -852,7 +870,9 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             for (int t = 0; t < 9; ++t) {
                 load_b(ring[(t + 2) % 3], min(it0 + t + 2, last_it));
                 if (t < 8) stage_piece(chunk + (TB ? 2 : 1), t);
-                const uint8_t* pt = (t < 8) ? pb + toffs[t + 1] : (TB ? pn + toffs[0] : pb + toffs[8]);
+                // (at the last chunk the last tap again: there is no next buffer)
+                const uint8_t* pt =
+                    (t < 8) ? pb + toffs[t + 1] : ((TB && chunk + 1 < nch) ? pn + toffs[0] : pb + toffs[8]);
 #pragma unroll
                 for (int i = 0; i < NP; ++i) {
 #pragma unroll
@@ -867,12 +887,16 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 if (chunk + 2 < nch) stage_store(bfar, stg);
                 __syncthreads();
             } else {
-                stage_store(bnext, stg);  // zeros past the last chunk: harmless
+                const bool more = chunk + 1 < nch;
+                if (more) stage_store(bnext, stg);
                 __syncthreads();
+                if (more) {
 #pragma unroll
-                for (int f = 0; f < FM; ++f)
+                    for (int f = 0; f < FM; ++f)
 #pragma unroll
-                    for (int i = 0; i < NP; ++i) ra[f][i] = *reinterpret_cast<const uint4*>(pn + abase[f] + i * PSTEP);
+                        for (int i = 0; i < NP; ++i)
+                            ra[f][i] = *reinterpret_cast<const uint4*>(pn + abase[f] + i * PSTEP);
+                }
             }
             bc = bnext;
         }
@@ -928,11 +952,13 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 }
                 load_b(wr9[t], min(itn + t, last_it));
             }
-            if (STG == 1 || more) stage_store(buf ^ 1, stg);  // wide: zeros past the last chunk
+            if (more) stage_store(buf ^ 1, stg);
             __syncthreads();
-            const uint8_t* pn = lds + (buf ^ 1) * patch_bytes;
+            if (more) {
+                const uint8_t* pn = lds + (buf ^ 1) * patch_bytes;
 #pragma unroll
-            for (int f = 0; f < FM; ++f) ra[f] = *reinterpret_cast<const uint4*>(pn + abase[f]);
+                for (int f = 0; f < FM; ++f) ra[f] = *reinterpret_cast<const uint4*>(pn + abase[f]);
+            }
         }
         it = total_it;
     } else if constexpr (FR == 32) {
@@ -1506,7 +1532,9 @@ inline bool tile_geometry(const Prob& p, const Cfg& c, int TN, int TH, int TW, G
     // linear 80-byte pixel slots for 32x32 fragments and the nine-tap 16x16
     // path, swizzled 64-byte slots otherwise
     const size_t pstride = (c.fr == 32 || p.r * p.s == 9) ? 80 : 64;
-    g->lds_bytes = std::max(nbuf * static_cast<size_t>(g->npix) * pstride + static_cast<size_t>(c.threads()) * 16,
+    // (a problem of fewer chunks than buffers allocates only as many)
+    const size_t nb = std::min(nbuf, static_cast<size_t>(g->nchunks));
+    g->lds_bytes = std::max(nb * static_cast<size_t>(g->npix) * pstride + static_cast<size_t>(c.threads()) * 16,
                             static_cast<size_t>(c.pixels()) * 8);
     // 16-bit NCHW outputs of whole-row tiles leave through an LDS transpose:
     // [NT channels][tile pixels * 2 + 16 bytes]
