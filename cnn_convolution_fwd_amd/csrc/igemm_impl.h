@@ -1886,7 +1886,14 @@ cfwd_status igemm_launch_bf16_epi(int cfg, const Prob& p, const ig::Geo& g, cons
                                   const float* scale, void* y, const Epi& e, hipStream_t st);
 cfwd_status igemm_launch_i8_epi(int cfg, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
                                 const float* scale, void* y, const Epi& e, hipStream_t st);
-// Resident-patch config rc (k_igemm_i8_res.hip).
+// Persistent single-chunk int8 configs (k_igemm_i8_stream.hip): they read
+// the prepared filter of tiled config stream_filter_config(sc).
+int stream_num_configs();
+bool stream_supported(const Prob& p, int sc, std::string* why);
+int stream_filter_config(int sc);
+cfwd_status stream_launch(const Prob& p, int sc, const void* x, const void* wp, const float* scale, void* y,
+                          const Epi& e, hipStream_t st);
+// Resident-input config rc (k_igemm_i8_res.hip).
 cfwd_status igemm_launch_i8_res(int rc, const Prob& p, const ig::Geo& g, const void* x, const void* wp,
                                 const float* scale, void* y, const Epi& e, hipStream_t st);
 // Split config sc (k_igemm_i8_split.hip): the split kernel, then the reduce

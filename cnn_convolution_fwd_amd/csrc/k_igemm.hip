@@ -8,13 +8,27 @@ namespace cfwd {
 // lowc_num_configs(): the gather form for few input channels (k_lowc.hip);
 // the next kNumSplitCfgs: the tiled kernel with a split reduction
 // (k_igemm_i8_split.hip), whose partial tiles live in the scratch; the next
-// kNumResCfgs: the tiled kernel with the resident input (k_igemm_i8_res.hip).
+// kNumResCfgs: the tiled kernel with the resident input (k_igemm_i8_res.hip);
+// the next stream_num_configs(): the persistent single-chunk int8 kernel
+// (k_igemm_i8_stream.hip).
 namespace {
 int split_first() { return ig::kNumCfgs + lowc_num_configs(); }
 int res_first() { return split_first() + ig::kNumSplitCfgs; }
 bool is_lowc(int cfg) { return cfg >= ig::kNumCfgs && cfg < split_first(); }
 bool is_split(int cfg) { return cfg >= split_first() && cfg < res_first(); }
 bool is_res(int cfg) { return cfg >= res_first() && cfg < res_first() + ig::kNumResCfgs; }
+int stream_first() { return res_first() + ig::kNumResCfgs; }
+bool is_stream(int cfg) { return cfg >= stream_first() && cfg < stream_first() + stream_num_configs(); }
+// The prepared-filter geometry of a streaming config: its tiled filter
+// config's output-channel tiles, one channel chunk.
+bool stream_filter_geo(const Prob& p, int cfg, int* fcfg, ig::Geo* g, std::string* why) {
+    if (!stream_supported(p, cfg - stream_first(), why)) return false;
+    *fcfg = stream_filter_config(cfg - stream_first());
+    const ig::Cfg c = ig::kCfgs[*fcfg];
+    g->ntk = (p.kg + c.nt() - 1) / c.nt();
+    g->nchunks = 1;
+    return true;
+}
 // base tile config of a tiled, split or resident config
 int base_of(int cfg) {
     if (is_split(cfg)) return ig::kSplitCfgs[cfg - split_first()].base;
@@ -28,7 +42,7 @@ bool geometry_of(const Prob& p, int cfg, ig::Geo* g, std::string* why) {
 }
 }  // namespace
 
-int igemm_num_configs() { return res_first() + ig::kNumResCfgs; }
+int igemm_num_configs() { return stream_first() + stream_num_configs(); }
 
 bool igemm_supported(const Prob& p, int cfg, std::string* why) {
     if (is_lowc(cfg)) return lowc_supported(p, cfg - ig::kNumCfgs, why);
@@ -38,6 +52,7 @@ bool igemm_supported(const Prob& p, int cfg, std::string* why) {
         return ig::split_geometry(p, cfg - split_first(), &g, &cps, why);
     }
     if (is_res(cfg)) return ig::res_geometry(p, cfg - res_first(), &g, why);
+    if (is_stream(cfg)) return stream_supported(p, cfg - stream_first(), why);
     if (cfg < 0 || cfg >= ig::kNumCfgs) {
         if (why) *why = "implicit GEMM: no such config";
         return false;
@@ -48,6 +63,10 @@ bool igemm_supported(const Prob& p, int cfg, std::string* why) {
 size_t igemm_filter_bytes(const Prob& p, int cfg) {
     if (is_lowc(cfg)) return lowc_filter_bytes(p, cfg - ig::kNumCfgs);
     ig::Geo g;
+    if (is_stream(cfg)) {
+        int fc;
+        return stream_filter_geo(p, cfg, &fc, &g, nullptr) ? ig::filter_bytes(p, ig::kCfgs[fc], g) : 0;
+    }
     if (!geometry_of(p, cfg, &g, nullptr)) return 0;
     return ig::filter_bytes(p, ig::kCfgs[base_of(cfg)], g);
 }
@@ -59,9 +78,15 @@ size_t igemm_scratch_bytes(const Prob& p, int cfg) {
 cfwd_status igemm_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
     if (is_lowc(cfg)) return lowc_prepare(p, cfg - ig::kNumCfgs, w, wp, st);
     // split and resident configs read their base config's prepared filter
-    // (its layout depends only on the output-channel tile and the chunks)
+    // (its layout depends only on the output-channel tile and the chunks),
+    // streaming configs their filter config's
     ig::Geo g;
     std::string why;
+    if (is_stream(cfg)) {
+        int fc;
+        if (!stream_filter_geo(p, cfg, &fc, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+        return igemm_prepare_i8(fc, p, g, w, wp, st);
+    }
     if (!geometry_of(p, cfg, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     cfg = base_of(cfg);
     switch (p.dtype) {
@@ -86,6 +111,7 @@ cfwd_status igemm_launch(const Prob& p, int cfg, const void* x, const void* wp, 
         if (!ig::res_geometry(p, cfg - res_first(), &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
         return igemm_launch_i8_res(cfg - res_first(), p, g, x, wp, scale, y, e, st);
     }
+    if (is_stream(cfg)) return stream_launch(p, cfg - stream_first(), x, wp, scale, y, e, st);
     if (!ig::geometry(p, ig::kCfgs[cfg], &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     // the fused epilogue has instantiations of its own (no registers of it
     // in the plain kernels)
