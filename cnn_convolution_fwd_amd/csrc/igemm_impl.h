@@ -780,16 +780,19 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
             const int itn = min(itd + 1, last_it);
             const int cn = (RSV == 9) ? itn / 9 : itn;
             read_a(ra[(d + 1) & 1], lds + cn * chunk_bytes, (RSV == 9) ? (d + 1) % 9 : 0);
+            // piece-major (32x32): the two MFMAs into one accumulator are FM * FN
+            // instructions apart
 #pragma unroll
-            for (int f = 0; f < FM; ++f)
+            for (int i = 0; i < NP; ++i)
 #pragma unroll
-                for (int nf = 0; nf < FN; ++nf) {
-                    if constexpr (FR == 16)
-                        Mma<T>::run(acc[f][nf], ra[d & 1][f][0], wr[d % D][nf][0]);
-                    else
-                        Mma32<T>::run(acc[f][nf], ra[d & 1][f][0], ra[d & 1][f][1], wr[d % D][nf][0],
-                                      wr[d % D][nf][1]);
-                }
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int nf = 0; nf < FN; ++nf) {
+                        if constexpr (FR == 16)
+                            Mma<T>::run(acc[f][nf], ra[d & 1][f][0], wr[d % D][nf][0]);
+                        else
+                            Mma32<T>::piece(acc[f][nf], ra[d & 1][f][i], wr[d % D][nf][i], i);
+                    }
             load_b(wr[d % D], min(itd + D, last_it));
         };
         read_a(ra[0], lds, 0);
@@ -1126,7 +1129,10 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
                 const bool kval = kt * NT + kk < a.Kg;
                 const float sc0 = a.scale[kval ? k : 0];  // no branch around the load
                 const float sc = kval ? sc0 : 0.0f;
-                uint8_t* lrow_base = lds + (kk >> 2) * pitch + (kk & 3);
+                // the quad of lanes kk & ~3 .. + 3 holds one channel block:
+                // its bytes are transposed across the quad so that each lane
+                // writes one pixel's 4 channels as a dword
+                uint8_t* cb_base = lds + (kk >> 2) * pitch;
                 // fused epilogue: channels past K (scale 0) take the last real
                 // channel's bias; pixels of images past N read image N - 1
                 // (their bytes are never stored)
@@ -1165,17 +1171,17 @@ __global__ __launch_bounds__(WM* WN * 64) void igemm_kernel(Args a) {
 #pragma unroll
                     for (int grp = 0; grp < NG; ++grp) {
                         const int p0 = (wm * FM + f) * FR + (FR == 16 ? 4 * lgrp : 8 * grp + 4 * lgrp);
-                        if (p0 < tile_pix) {
+                        uint32_t q[4];
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                uint32_t q;
-                                if constexpr (EPI)
-                                    q = requant_i8_fused(acc[f][nf][grp * 4 + v], ebias, sc, eres[grp][v], elo);
-                                else
-                                    q = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
-                                lrow_base[(p0 + v) * 4] = static_cast<uint8_t>(q);
-                            }
+                        for (int v = 0; v < 4; ++v) {
+                            if constexpr (EPI)
+                                q[v] = requant_i8_fused(acc[f][nf][grp * 4 + v], ebias, sc, eres[grp][v], elo);
+                            else
+                                q[v] = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
                         }
+                        const uint32_t d = quad_transpose_bytes(pack_low_bytes(q[0], q[1], q[2], q[3]), lane);
+                        // (pixels past the tile land in the row's 16-byte pad)
+                        if (p0 < tile_pix) *reinterpret_cast<uint32_t*>(cb_base + (p0 + (lane & 3)) * 4) = d;
                     }
                 }
             }

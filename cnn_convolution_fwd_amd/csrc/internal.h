@@ -196,6 +196,19 @@ __device__ __forceinline__ uint32_t requant_i8_bits(int acc, float scale) {
     return __float_as_uint(__fadd_rn(q, 12582912.0f));
 }
 
+// 4 x 4 byte transpose within each quad of lanes (lanes 4m .. 4m + 3): lane
+// j of a quad holds bytes b0..b3 and afterwards holds byte j of each of the
+// four lanes, lane i's in byte i.  Two cross-lane moves (DPP quad
+// permutations: lane ^ 1, then lane ^ 2), each followed by a byte / half-word
+// merge.  Every lane of a quad must execute it.
+__device__ __forceinline__ uint32_t quad_transpose_bytes(uint32_t d, int lane) {
+    const uint32_t t1 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(d), 0xB1, 0xF, 0xF, false));
+    const uint32_t e = (lane & 1) ? (((t1 >> 8) & 0x00FF00FFu) | (d & 0xFF00FF00u))
+                                  : ((d & 0x00FF00FFu) | ((t1 & 0x00FF00FFu) << 8));
+    const uint32_t t2 = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(e), 0x4E, 0xF, 0xF, false));
+    return (lane & 2) ? ((t2 >> 16) | (e & 0xFFFF0000u)) : ((e & 0x0000FFFFu) | (t2 << 16));
+}
+
 // Low bytes of four words -> one word, b0 in the lowest byte.
 __device__ __forceinline__ uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
     const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);

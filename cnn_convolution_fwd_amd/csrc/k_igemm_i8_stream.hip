@@ -213,12 +213,16 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
                     ra[(t + 1) & 1][f][1] = *reinterpret_cast<const uint4*>(pb + qb[f] + toff[t + 1] + 32);
                 }
             }
+            // piece-major: the two MFMAs into one accumulator are FM * FN
+            // instructions apart (back to back, the second would wait for
+            // the first's result)
 #pragma unroll
-            for (int f = 0; f < FM; ++f)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int nf = 0; nf < FN; ++nf)
-                    ig::Mma32<int8_t>::run(acc[f][nf], ra[t & 1][f][0], ra[t & 1][f][1], wr[t % D][nf][0],
-                                           wr[t % D][nf][1]);
+                for (int f = 0; f < FM; ++f)
+#pragma unroll
+                    for (int nf = 0; nf < FN; ++nf)
+                        ig::Mma32<int8_t>::piece(acc[f][nf], ra[t & 1][f][i], wr[t % D][nf][i], i);
         }
 
         // ---- epilogue: requantise into ebuf as [channel block][tile pixel][4 channels]
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
             const bool kval = kc < a.K;
             const float sc0 = a.scale[kval ? kc : 0];
             const float sc = kval ? sc0 : 0.0f;
-            uint8_t* row = ebuf + (kk >> 2) * pitch + (kk & 3);
+            uint8_t* cbrow = ebuf + (kk >> 2) * pitch;  // this lane's channel block
             const int ke = EPI ? min(kc, a.K - 1) : 0;
             const int ebias = (EPI && a.e.bias) ? static_cast<const int32_t*>(a.e.bias)[ke] : 0;
             const float elo = (EPI && a.e.relu) ? 0.0f : -127.0f;
@@ -253,17 +257,18 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
                                         static_cast<const int8_t*>(a.e.res)[kofs + static_cast<long long>(p0 + v) * 4]);
                         }
                     }
-                    if (p0 < tile_pix) {
+                    uint32_t q[4];
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) {
-                            uint32_t q;
-                            if constexpr (EPI)
-                                q = requant_i8_fused(acc[f][nf][grp * 4 + v], ebias, sc, eres[v], elo);
-                            else
-                                q = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
-                            row[(p0 + v) * 4] = static_cast<uint8_t>(q);
-                        }
+                    for (int v = 0; v < 4; ++v) {
+                        if constexpr (EPI)
+                            q[v] = requant_i8_fused(acc[f][nf][grp * 4 + v], ebias, sc, eres[v], elo);
+                        else
+                            q[v] = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
                     }
+                    // lanes 4m .. 4m + 3 hold the 4 channels of one block:
+                    // transposed, each writes one pixel's dword
+                    const uint32_t dq = quad_transpose_bytes(pack_low_bytes(q[0], q[1], q[2], q[3]), lane);
+                    if (p0 < tile_pix) *reinterpret_cast<uint32_t*>(cbrow + (p0 + (lane & 3)) * 4) = dq;
                 }
             }
         }
