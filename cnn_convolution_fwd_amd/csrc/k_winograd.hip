@@ -580,10 +580,13 @@ cfwd_status bf16_absmax(const void* x, long long n, unsigned* out, hipStream_t s
 
 // F(2x2): config 0 = the three-launch form above (any float dtype and
 // layout), configs 1 and 2 = the fused single-launch kernels (bf16 NCHW).
-int winograd_num_configs(int m) { return m == 2 ? 3 : 1; }
+// F(6x6): config 0 = the three-launch form, config 1 = the fused kernel
+// (bf16 or fp32 NCHW).
+int winograd_num_configs(int m) { return m == 2 ? 3 : 2; }
 
 bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
     if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_supported(p, cfg, why);
+    if (m == 6 && cfg == 1) return winograd_f6_fused_supported(p, why);
     if (cfg != 0 || (m != 2 && m != 6)) {
         if (why) *why = "winograd: no such config";
         return false;
@@ -597,12 +600,20 @@ bool winograd_supported(const Prob& p, int m, int cfg, std::string* why) {
         if (why) *why = "winograd F(6x6): bf16 needs at least 32 input channels per group to meet its error bound";
         return false;
     }
+    // with padding 2 a corner output sees a single input pixel per channel,
+    // so the sum of |x*w| it is normalised by is small, while the rounding of
+    // the tile's 64 transformed values reaches it in full
+    if (m == 6 && p.dtype == CFWD_BF16 && (p.ph > 1 || p.pw > 1)) {
+        if (why) *why = "winograd F(6x6): bf16 needs padding 0 or 1 to meet its error bound";
+        return false;
+    }
     wg::Geo g;
     return wg::geometry(p, m, &g, why);
 }
 
 size_t winograd_filter_bytes(const Prob& p, int m, int cfg) {
     if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_filter_bytes(p, cfg);
+    if (m == 6 && cfg == 1) return winograd_f6_fused_filter_bytes(p);
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
     return g.v_bytes + g.hdr;
@@ -611,6 +622,7 @@ size_t winograd_filter_bytes(const Prob& p, int m, int cfg) {
 size_t winograd_scratch_bytes(const Prob& p, int m, int cfg) {
     if (m == 2 && (cfg == 1 || cfg == 2))  // the fused form: only the input's largest magnitude
         return winograd_fused_supported(p, cfg, nullptr) ? 8192 : 0;
+    if (m == 6 && cfg == 1) return winograd_f6_fused_scratch_bytes(p);
     wg::Geo g;
     if (!wg::geometry(p, m, &g, nullptr)) return 0;
     return g.u_bytes + g.hdr;
@@ -618,6 +630,7 @@ size_t winograd_scratch_bytes(const Prob& p, int m, int cfg) {
 
 cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void* wp, hipStream_t st) {
     if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_prepare(p, cfg, w, wp, st);
+    if (m == 6 && cfg == 1) return winograd_f6_fused_prepare(p, w, wp, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
@@ -651,6 +664,7 @@ cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void*
 cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const void* wp, void* scratch, void* y,
                             const Epi& e, hipStream_t st) {
     if (m == 2 && (cfg == 1 || cfg == 2)) return winograd_fused_launch(p, cfg, x, wp, scratch, y, e, st);
+    if (m == 6 && cfg == 1) return winograd_f6_fused_launch(p, x, wp, scratch, y, e, st);
     wg::Geo g;
     std::string why;
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);

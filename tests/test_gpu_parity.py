@@ -135,6 +135,41 @@ def test_small_shapes_all_candidates(case, dtype, layout, xb):
     assert not failures, "; ".join(failures)
 
 
+# Fused Winograd F(6x6) (config 1 of winograd_f6x6_3x3): ragged tile rows and
+# columns with a ragged output-channel block; tile blocks whose rows run over
+# five images; 34 tile columns (two column blocks); padding 0 and 2; 80
+# channels (the last 32-channel chunk half used)
+WF6 = [
+    # name, N, C, H, W, K, pad
+    ("wf6_c64_14x24_k40", 2, 64, 14, 24, 40, 1),
+    ("wf6_c80_n5_8x8", 5, 80, 8, 8, 64, 1),
+    ("wf6_c64_w200", 1, 64, 8, 200, 32, 1),
+    ("wf6_c96_p0", 3, 96, 16, 16, 64, 0),
+    ("wf6_c64_p2", 2, 64, 10, 16, 48, 2),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("case", WF6, ids=[c[0] for c in WF6])
+def test_winograd_f6_fused_shapes(case, dtype):
+    torch_cuda()
+    name, N, C, H, W, K, pd = case
+    L = Layer(name, C, K, H, W, 3, 3, 1, pd, 1, 1)
+    pr = random_float_problem(L, N, dtype, zlib.crc32((name + dtype).encode()))
+    yref, den = oracle.conv2d(pr.x, pr.w, 1, pd, 1, 1)
+    cands = [c for c in candidates_for((N, C, H, W, K, 3, 3), dtype, 1, pd) if c[0] == "winograd_f6x6_3x3"]
+    if dtype == "bf16" and pd > 1:
+        # refused: a corner output's normalising sum covers one pixel per channel
+        assert not cands, cands
+        return
+    assert ("winograd_f6x6_3x3", 1) in cands, cands
+    for algo, cfg in cands:
+        for prepared in (False, True):
+            say("case", name, dtype, algo, cfg, "prepared" if prepared else "")
+            y = run_conv(pr.x, pr.w, dtype, 1, pd, algo=algo, config_id=cfg, prepared=prepared)
+            check_float("%s/%s/%d" % (name, algo, cfg), y, yref, den, dtype, algo)
+
+
 def test_prepared_filter_path_matches():
     torch_cuda()
     L = Layer("p", 24, 40, 10, 12, 3, 3, 1, 1)
