@@ -52,12 +52,10 @@ constexpr int TB = 32;                  // tile slots per workgroup (rows of the
 constexpr int KB = 32;                  // output channels per workgroup
 constexpr int NTHR = 256;               // four waves
 constexpr int XPW = 16;                 // positions per wave
-constexpr int U_LDS = 64 * TB * 32;     // one step's transformed input: 64 KiB
 constexpr int KS = 16;                  // output channels per slice of the output transform
 constexpr int MP = 36;                  // LDS pitch (floats) of one (position, channel) row of 32 tiles
 constexpr int M_LDS = 64 * KS * MP * 4;
 constexpr int LDS_MAX = 160 * 1024;
-constexpr int PATCH_MAX = LDS_MAX - U_LDS;
 
 // ---------------------------------------------------------------- matrices
 
@@ -136,59 +134,60 @@ template <> struct Op<bf16_t> {
         const _Float16 v = static_cast<_Float16>(c);
         return V{v, v};
     }
+    static __device__ __forceinline__ V splat_bits(uint32_t b) { return __builtin_bit_cast(V, b); }
 };
 template <> struct Op<float> {
     using V = float;
     static __device__ __forceinline__ V splat(float c) { return c; }
+    static __device__ __forceinline__ V splat_bits(uint32_t b) { return __uint_as_float(b); }
 };
 
-// first column of the given parity (0 even, 1 odd, 2 any) whose entry in row
-// `row` of the rescaled B^T is +1 (-1 when there is none)
-constexpr int bs_first_one(int row, int par) {
+// The rescaled B^T has the form the transforms below are written for:
+//   row 0:           d6 - d0 + c (d2 - d4)          row 7: d7 - d1 + c (d3 - d5)
+//   rows P, P+1 (P = 1, 3, 5): E +- s O with E = d6 + a d2 + b d4 and
+//   O = d1 + g d3 + e d5
+struct PairCoef {
+    float a, b, g, e, s;
+};
+constexpr PairCoef pair_coef(int P) {
+    const float s = kF6.bs[P][1];
+    return PairCoef{kF6.bs[P][2], kF6.bs[P][4], kF6.bs[P][3] / s, kF6.bs[P][5] / s, s};
+}
+constexpr bool check_form() {
+    const float c = kF6.bs[0][2];
+    const float r0[8] = {-1, 0, c, 0, -c, 0, 1, 0};
+    const float r7[8] = {0, -1, 0, c, 0, -c, 0, 1};
     for (int k = 0; k < 8; ++k)
-        if ((par == 2 || (k & 1) == par) && kF6.bs[row][k] == 1.0f) return k;
-    return -1;
-}
-
-// sum over the columns of parity PAR of row ROW of the rescaled B^T times d
-template <typename T, int ROW, int PAR>
-__device__ __forceinline__ typename Op<T>::V bs_part(const typename Op<T>::V (&d)[8]) {
-    using V = typename Op<T>::V;
-    constexpr int one = bs_first_one(ROW, PAR);
-    V acc = Op<T>::splat(0.0f);
-    if constexpr (one >= 0) acc = d[one];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if (k == one || (PAR != 2 && (k & 1) != PAR)) continue;
-        const float c = kF6.bs[ROW][k];
-        if (c == 0.0f) continue;
-        if (c == 1.0f)
-            acc = acc + d[k];
-        else if (c == -1.0f)
-            acc = acc - d[k];
-        else
-            acc = Op<T>::splat(c) * d[k] + acc;
+        if (kF6.bs[0][k] != r0[k] || kF6.bs[7][k] != r7[k]) return false;
+    for (int P = 1; P < 7; P += 2) {
+        const PairCoef q = pair_coef(P);
+        for (int sg = 0; sg < 2; ++sg) {
+            const float ss = sg ? -q.s : q.s;
+            const float r[8] = {0, ss, q.a, ss * q.g, q.b, ss * q.e, 1, 0};
+            for (int k = 0; k < 8; ++k)
+                if (kF6.bs[P + sg][k] != r[k]) return false;
+        }
     }
-    return acc;
+    return true;
 }
+static_assert(check_form(), "rescaled B^T does not have the factored form");
 
-template <typename T, int P>
-__device__ __forceinline__ void bs_pair(const typename Op<T>::V (&d)[8], typename Op<T>::V (&o)[8]) {
-    const auto e = bs_part<T, P, 0>(d);
-    const auto od = bs_part<T, P, 1>(d);
-    o[P] = e + od;
-    o[P + 1] = e - od;
-}
-
-// d <- (rescaled B^T) d for one 8-point line
+// d <- (rescaled B^T) d for one 8-point line: 24 operations
 template <typename T>
 __device__ __forceinline__ void bt8(typename Op<T>::V (&d)[8]) {
-    typename Op<T>::V o[8];
-    o[0] = bs_part<T, 0, 2>(d);
-    o[7] = bs_part<T, 7, 2>(d);
-    bs_pair<T, 1>(d, o);
-    bs_pair<T, 3>(d, o);
-    bs_pair<T, 5>(d, o);
+    using O = Op<T>;
+    typename O::V o[8];
+    const auto c = O::splat(kF6.bs[0][2]);
+    o[0] = c * (d[2] - d[4]) + (d[6] - d[0]);
+    o[7] = c * (d[3] - d[5]) + (d[7] - d[1]);
+#pragma unroll
+    for (int P = 1; P < 7; P += 2) {
+        const PairCoef q = pair_coef(P);
+        const auto e = O::splat(q.b) * d[4] + (O::splat(q.a) * d[2] + d[6]);
+        const auto od = O::splat(q.e) * d[5] + (O::splat(q.g) * d[3] + d[1]);
+        o[P] = O::splat(q.s) * od + e;
+        o[P + 1] = O::splat(-q.s) * od + e;
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) d[k] = o[k];
 }
@@ -219,10 +218,13 @@ struct Args {
     int C, H, W, K, OH, OW, ph, pw;
     long long x_img, y_img;  // elements per image
     int x_bytes;             // bytes of the whole input (< 2 GiB): the buffer bound
+    int v_bytes;             // bytes of the prepared filter (< 2 GiB)
     int th, tw, NR;          // tile rows and columns per image; tile rows in the batch
     int tcb, tr;             // tile block: tr tile rows of tcb tiles
     int nrb, ncb, ntk, nchunks, nsteps;
-    int rp, plane, nbk, nunits;  // LDS row pitch and plane size (dwords); 16-byte blocks per row; staging units
+    int nbk, nunits;         // 16-byte load blocks per patch row; staging units
+    int nbkp, rp, sk;        // patch layout (16-byte slots): block pitch, row pitch, skew per tile row
+    int patch_bytes;         // one patch buffer
     Epi e;
     // bf16: largest input / filter magnitudes (bit patterns), for the fp16 scaling
     const unsigned* xmax;
@@ -243,17 +245,19 @@ __device__ __forceinline__ uint32_t bf16_pair_to_f16(uint32_t wlo, uint32_t whi,
 }
 
 template <typename T>
-__device__ __forceinline__ void mma(f32x16& c, const uint4& a, const uint4& b) {
+__device__ __forceinline__ void mma(f32x16& c, const uint4& a, const uint4& b, int i) {
     if constexpr (sizeof(T) == 2) {
         c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
                                                    0);
     } else {
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(word_of(a, i)), __uint_as_float(word_of(b, i)), c, 0,
+                                                 0, 0);
     }
 }
+
+template <bool B> struct BoolC {
+    static constexpr bool value = B;
+};
 
 // MAXU: staging units per thread at most; EPI: fused epilogue compiled in.
 template <typename T, int MAXU, bool EPI>
@@ -261,16 +265,16 @@ __global__ __launch_bounds__(NTHR) void wf6_kernel(Args a) {
     constexpr bool BF = sizeof(T) == 2;
     constexpr int ES = static_cast<int>(sizeof(T));
     constexpr int E = 16 / ES;  // pixels per 16-byte load; channels per staging slot
-    using V = typename Op<T>::V;
+    using O = Op<T>;
+    using V = typename O::V;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    uint8_t* const patch = lds + U_LDS;  // U of one step, then the patch planes
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lrow = lane & 31;
     const int h = lane >> 5;
-    const float xsc = BF ? wg_norm(a.xmax) : 1.0f;
+    const float xsc = BF ? wg_norm(a.xmax) : 1.0f;  // bf16: input scale into the fp16 range
 
     // work order: the filter slice kt is the slowest index, so each XCD's
     // contiguous range of blocks shares one slice in its L2
@@ -280,25 +284,35 @@ __global__ __launch_bounds__(NTHR) void wf6_kernel(Args a) {
     lin -= kt * nblk;
     const int cb = lin % a.ncb;
     const int rb = lin / a.ncb;
-    const int R0 = rb * a.tr;      // first tile row of the block (over the batch)
-    const int tc0 = cb * a.tcb;    // first tile column
+    const int R0 = rb * a.tr;        // first tile row of the block (over the batch)
+    const int tc0 = cb * a.tcb;      // first tile column
     const int cw0 = 6 * tc0 - a.pw;  // first window column
     const int cs = cw0 >= 0 ? (cw0 / E) * E : -((-cw0 + E - 1) / E) * E;  // staged from here (16-byte aligned)
     const int off = cw0 - cs;
     const int HW = a.H * a.W;
+    const int PH = 8 * a.tr;  // patch rows
 
-    // ---- staging units (patch row pr, 16-byte column block cbk, channel slot j), cbk fastest
+    // ---- patch: two buffers of 16-byte slots, one per (half h, patch row r,
+    // pixel p), holding the step's channels 8h .. 8h+7 as fp16 (bf16) or its
+    // four fp32 channels of half h, at slot
+    //   (h PH + r) rp + (h TR + r / 8) sk + (p % E) nbkp + p / E
+    // -- pixel p % E of every 16-byte load block together, so the E stores
+    // of the staging units run through consecutive slots across the lanes,
+    // and an odd row pitch and a skew per tile row spread the window reads
+    // over the banks -- then a 128-byte area that staging threads without a
+    // unit write into
+    const int dummy = 2 * a.patch_bytes;
+    // staging units (half j, patch row pr, 16-byte column block cbk), cbk fastest
     int u_voff[MAXU];  // byte offset of the unit's first channel (none / outside the image: past the bound)
-    int u_lds[MAXU];   // LDS byte offset of the unit in the patch (plane 4j)
-    bool u_has[MAXU];
+    int u_lds[MAXU];   // byte offset in a patch buffer (no unit: -1)
 #pragma unroll
     for (int i = 0; i < MAXU; ++i) {
         const int u = tid + i * NTHR;
         const bool has = u < a.nunits;
         const int cbk = u % a.nbk;
         const int t = u / a.nbk;
-        const int j = t & 1;
-        const int pr = t >> 1;
+        const int pr = t % PH;
+        const int j = t / PH;
         const int R = R0 + (pr >> 3);
         const int n = R / a.th;
         const int ih = 6 * (R - n * a.th) - a.ph + (pr & 7);
@@ -308,178 +322,251 @@ __global__ __launch_bounds__(NTHR) void wf6_kernel(Args a) {
         u_voff[i] = in ? static_cast<int>((n * a.x_img + static_cast<long long>(8 * j) * HW +
                                            static_cast<long long>(ih) * a.W + iw) * ES)
                        : static_cast<int>(0x80000000u);
-        u_lds[i] = ((4 * j) * a.plane + pr * a.rp + cbk * E) * 4;
-        u_has[i] = has;
+        u_lds[i] = has ? ((j * PH + pr) * a.rp + (j * a.tr + (pr >> 3)) * a.sk + cbk) * 16 : -1;
     }
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.x), 0, a.x_bytes, 0x00020000);
-    // staged data of one step: bf16 loads 8 channels x 8 pixels per unit and
-    // converts them to 4 planes x 8 pixels of fp16 pairs in place (the same
-    // 32 dwords); fp32 loads 4 channels x 4 pixels, one plane each
+    // one step's staged data: bf16 loads 8 channels x 8 pixels per unit and
+    // converts them in place to 8 pixels x 8 fp16 channels; fp32 loads 4
+    // channels x 4 pixels, stored transposed (4 pixels x 4 channels)
     uint4 stg[MAXU][8];
-    auto stage_load = [&](int st) {
+    // units [i0, i1) of the thread
+    auto stage_load = [&](int st, int i0, int i1) __attribute__((always_inline)) {
         // channels of step st: bf16 16 st + 8 j + e; fp32 16 (st/2) + 8 j + 4 (st%2) + e
         const int cbase = BF ? st * 16 : (st >> 1) * 16 + (st & 1) * 4;
         const int soff = cbase * HW * ES;
 #pragma unroll
-        for (int i = 0; i < MAXU; ++i)
+        for (int i = i0; i < i1; ++i)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, u_voff[i] + soff + e * HW * ES, 0, 0);
+                // lane part in the vector offset, the step's channel part in the scalar
+                // one (a unit outside the image stays past the bound either way)
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, u_voff[i], soff + e * HW * ES, 0);
                 stg[i][e] = make_uint4(v.x, v.y, v.z, v.w);
             }
     };
-    // bf16: to fp16 pairs, output index 2 p + hf = plane p, pixels 4 hf .. 4 hf + 3
-    auto stage_convert = [&]() {
-        if constexpr (BF) {
+    auto stage_convert = [&](int i0, int i1) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < MAXU; ++i) {
-                uint4 o[8];
-#pragma unroll
-                for (int p = 0; p < 4; ++p)
-#pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        uint32_t w[4];
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) {
-                            const int px = 4 * hf + x;
-                            w[x] = bf16_pair_to_f16(word_of(stg[i][2 * p], px >> 1), word_of(stg[i][2 * p + 1], px >> 1),
-                                                    px & 1, xsc);
-                        }
-                        o[2 * p + hf] = make_uint4(w[0], w[1], w[2], w[3]);
-                    }
-#pragma unroll
-                for (int k = 0; k < 8; ++k) stg[i][k] = o[k];
-            }
-        }
-    };
-    auto stage_store = [&]() {
-#pragma unroll
-        for (int i = 0; i < MAXU; ++i) {
-            if (!u_has[i]) continue;
-            uint8_t* base = patch + u_lds[i];
+        for (int i = i0; i < i1; ++i) {
+            uint4 o[8];
             if constexpr (BF) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    *reinterpret_cast<uint4*>(base + ((k >> 1) * a.plane + 4 * (k & 1)) * 4) = stg[i][k];
+                for (int x = 0; x < 8; ++x) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        w[p] = bf16_pair_to_f16(word_of(stg[i][2 * p], x >> 1),
+                                                    word_of(stg[i][2 * p + 1], x >> 1), x & 1, xsc);
+                    o[x] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(base + e * a.plane * 4) = stg[i][e];
+                for (int x = 0; x < 4; ++x)
+                    o[x] = make_uint4(word_of(stg[i][0], x), word_of(stg[i][1], x), word_of(stg[i][2], x),
+                                      word_of(stg[i][3], x));
             }
+#pragma unroll
+            for (int x = 0; x < E; ++x) stg[i][x] = o[x];
+        }
+    };
+    auto stage_store = [&](int buf, int i0, int i1) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = i0; i < i1; ++i) {
+            uint8_t* base = lds + (u_lds[i] >= 0 ? buf + u_lds[i] : dummy);
+            const int xs = u_lds[i] >= 0 ? a.nbkp * 16 : 16;
+#pragma unroll
+            for (int x = 0; x < E; ++x) *reinterpret_cast<uint4*>(base + xs * x) = stg[i][x];
         }
     };
 
-    // ---- transform role: tile slot s = lrow, plane q = tid / 32
-    const int q = tid >> 5;
+    // ---- transform: lane (tile slot lrow, half h) forms this wave's two
+    // Winograd rows -- (1,2), (3,4), (5,6) for waves 0-2, (0,7) for wave 3 --
+    // for the four units (bf16 channel pairs, fp32 channels) of half h
     const int tr_ = lrow / a.tcb;
     const bool slot_ok = lrow < a.tr * a.tcb;
-    const int tbase = q * a.plane + (slot_ok ? 8 * tr_ * a.rp + off + 6 * (lrow - tr_ * a.tcb) : off);
-    const int ubase = ((q >> 2) * 32 + lrow) * 16 + (q & 3) * 4;
-    V u[8][8];
-    auto read_window = [&]() {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(patch) + tbase;
+    const int trw = slot_ok ? tr_ : 0, tcw = slot_ok ? lrow - tr_ * a.tcb : 0;
+    // byte offset of the window's column j (row 0 of the window)
+    const int px0 = off + 6 * tcw;
+    const int wrow = ((h * PH + 8 * trw) * a.rp + (h * a.tr + trw) * a.sk) * 16;
+    const int nbkp16 = a.nbkp * 16;
+    auto wcol = [&](int j) __attribute__((always_inline)) { return wrow + ((px0 + j) & (E - 1)) * nbkp16 + ((px0 + j) / E) * 16; };
+    const int rpb = a.rp * 16;  // bytes per patch row
+    const int P = 2 * wave + 1;  // first row of the pair (waves 0-2)
+    const PairCoef c1 = pair_coef(1), c3 = pair_coef(3), c5 = pair_coef(5);
+    const V ca = O::splat(wave == 0 ? c1.a : wave == 1 ? c3.a : c5.a);
+    const V cbb = O::splat(wave == 0 ? c1.b : wave == 1 ? c3.b : c5.b);
+    const V cg = O::splat(wave == 0 ? c1.g : wave == 1 ? c3.g : c5.g);
+    const V ce = O::splat(wave == 0 ? c1.e : wave == 1 ? c3.e : c5.e);
+    const V csp = O::splat(wave == 0 ? c1.s : wave == 1 ? c3.s : c5.s);
+    const V csn = O::splat(wave == 0 ? -c1.s : wave == 1 ? -c3.s : -c5.s);
+    const V c07 = O::splat(kF6.bs[0][2]);
+    V t[2][8][4];  // [row of the pair][window column][unit], then U in place
+    // column pass: t[r][j] = (row r of the rescaled B^T) . d[.][j]
+    // Two passes over the window's columns, even rows then odd rows (one
+    // column ahead in registers): the pair waves form E (rows 2, 4, 6) and
+    // O (rows 1, 3, 5) and then E +- s O; wave 3 forms row 0 from the even
+    // rows and row 7 from the odd ones.  W3: wave 3's code or the pair waves'.
+    auto column_loop = [&](auto w3c, int buf) __attribute__((always_inline)) {
+        constexpr bool W3 = decltype(w3c)::value;
+        const uint8_t* src = lds + buf;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int par = 0; par < 2; ++par) {
+            // rows of this pass: wave 3 par, par+2, par+4, par+6; pairs 2-par, 4-par, 6-par
+            constexpr int NRW = W3 ? 4 : 3;
+            const int r0 = W3 ? par : 2 - par;
+            uint4 dc[4], dn[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) u[i][j] = __builtin_bit_cast(V, src[i * a.rp + j]);
-    };
-    auto transform = [&]() {
+            for (int k = 0; k < NRW; ++k) dc[k] = *reinterpret_cast<const uint4*>(src + (r0 + 2 * k) * rpb + wcol(0));
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            V c[8];
+            for (int j = 0; j < 8; ++j) {
+                if (j < 7) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[i] = u[i][j];
-            bt8<T>(c);
+                    for (int k = 0; k < NRW; ++k)
+                        dn[k] = *reinterpret_cast<const uint4*>(src + (r0 + 2 * k) * rpb + wcol(j + 1));
+                }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) u[i][j] = c[i];
+                for (int u = 0; u < 4; ++u) {
+                    V dv[4];
+#pragma unroll
+                    for (int k = 0; k < NRW; ++k) dv[k] = O::splat_bits(word_of(dc[k], u));
+                    if constexpr (W3) {
+                        // rows (0 2 4 6) or (1 3 5 7): c (d[1] - d[2]) + (d[3] - d[0])
+                        t[par][j][u] = c07 * (dv[1] - dv[2]) + (dv[3] - dv[0]);
+                    } else if (par == 0) {
+                        // rows 2 4 6: E = b d4 + (a d2 + d6)
+                        t[0][j][u] = cbb * dv[1] + (ca * dv[0] + dv[2]);
+                    } else {
+                        // rows 1 3 5: O = e d5 + (g d3 + d1)
+                        t[1][j][u] = ce * dv[2] + (cg * dv[1] + dv[0]);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int k = 0; k < NRW; ++k) dc[k] = dn[k];
+            }
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) bt8<T>(u[i]);
-    };
-    auto write_u = [&]() {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
+        if constexpr (!W3) {
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint32_t*>(lds + ubase + (i * 8 + j) * 1024) = __builtin_bit_cast(uint32_t, u[i][j]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const V ev = t[0][j][u], od = t[1][j][u];
+                    t[0][j][u] = csp * od + ev;
+                    t[1][j][u] = csn * od + ev;
+                }
+        }
+    };
+    auto column_pass = [&](int buf) __attribute__((always_inline)) {
+        if (wave == 3)
+            column_loop(BoolC<true>{}, buf);
+        else
+            column_loop(BoolC<false>{}, buf);
+    };
+    // row pass of row r: U[r][c] = sum_j t[r][j] B^T[c][j]
+    auto row_pass = [&](int r) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            V line[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) line[j] = t[r][j][u];
+            bt8<T>(line);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[r][j][u] = line[j];
+        }
+    };
+    auto a_op = [&](int r, int c) __attribute__((always_inline)) {
+        return make_uint4(__builtin_bit_cast(uint32_t, t[r][c][0]), __builtin_bit_cast(uint32_t, t[r][c][1]),
+                          __builtin_bit_cast(uint32_t, t[r][c][2]), __builtin_bit_cast(uint32_t, t[r][c][3]));
     };
 
-    // ---- product role: positions 16 wave + x; prepared filter
-    // V[xi][kt][chunk][piece][32 rows][half][16 B], step st = 2 chunk + piece
-    const long long vxs = static_cast<long long>(a.ntk) * a.nchunks * 2048;
-    const uint8_t* __restrict__ vlane = a.v + static_cast<long long>(16 * wave) * vxs +
-                                        static_cast<long long>(kt) * a.nchunks * 2048 + lrow * 32 + h * 16;
-    // filter operands: a ring of 8 -- slot r holds position r, then (after
-    // its product) position r + 8 of the same step, then position r of the
-    // next step
+    // ---- product: position x of this wave = (row x / 8 of its pair, column
+    // x % 8); prepared filter V[xi][kt][chunk][piece][32 rows][half][16 B],
+    // step st = 2 chunk + piece
+    const int ra = wave == 3 ? 0 : P, rbw = wave == 3 ? 7 : P + 1;
+    // (a buffer resource over the prepared filter: the lane's part of an
+    // offset in a vector register, the position and step part in a scalar one)
+    const int vxs = a.ntk * a.nchunks * 2048;
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.v), 0, a.v_bytes, 0x00020000);
+    const int vlane = lrow * 32 + h * 16;
+    const int vrow0 = 8 * ra * vxs + kt * a.nchunks * 2048, vrow1 = 8 * rbw * vxs + kt * a.nchunks * 2048;
+    // filter operands: a ring of 8 -- slot c holds row ra's column c, then
+    // (after its products) row rbw's column c, then the next step's row ra
     uint4 vr[8];
     f32x16 acc[XPW];
 #pragma unroll
     for (int x = 0; x < XPW; ++x) acc[x] = f32x16{};
-    auto load_v = [&](int x, int st) { vr[x & 7] = *reinterpret_cast<const uint4*>(vlane + x * vxs + st * 1024); };
-    // the products of step st_cur (U in LDS, V in the ring), reloading the
-    // ring with step st_next (none when negative); the A operands are read
-    // two positions ahead
-    auto mfma_step = [&](int st_cur, int st_next) {
-        const uint8_t* ua = lds + (16 * wave) * 1024 + h * 512 + lrow * 16;
-        uint4 ar[3];
-        ar[0] = *reinterpret_cast<const uint4*>(ua);
-        ar[1] = *reinterpret_cast<const uint4*>(ua + 1024);
-#pragma unroll
-        for (int x = 0; x < XPW; ++x) {
-            if (x + 2 < XPW) ar[(x + 2) % 3] = *reinterpret_cast<const uint4*>(ua + (x + 2) * 1024);
-            mma<T>(acc[x], ar[x % 3], vr[x & 7]);
-            if (x < 8)
-                load_v(x + 8, st_cur);
-            else if (st_next >= 0)
-                load_v(x - 8, st_next);
-        }
+    auto load_v = [&](int r, int c, int st) __attribute__((always_inline)) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rv, vlane, (r ? vrow1 : vrow0) + c * vxs + st * 1024, 0);
+        vr[c] = make_uint4(v.x, v.y, v.z, v.w);
     };
-    // MFMAs of one step interleaved with the vector work of the next
-    constexpr int NMF = BF ? XPW : 4 * XPW;
-    constexpr int NV = BF ? 44 : 8;
-    auto interleave = [&]() {
+    // the products of row r of the pair for step st; the ring reloads with
+    // (row 1, step st) after row 0 and (row 0, step st_next) after row 1
+    auto mfma_row = [&](int r, int st, int st_next) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < NMF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // NV vector ALU instructions
+        for (int c = 0; c < 8; ++c) {
+            const uint4 av = a_op(r, c);
+#pragma unroll
+            for (int i = 0; i < (BF ? 1 : 4); ++i) mma<T>(acc[8 * r + c], av, vr[c], i);
+            if (r == 0)
+                load_v(1, c, st);
+            else
+                load_v(0, c, st_next);
         }
     };
 
-    // ---- pipeline: step st's patch is transformed while the products of
-    // step st-1 run; two barriers per step (patch and U reads done; U and the
-    // next patch written).  The last step reloads its own patch (not read
-    // again), so every step runs the same code.
+    // ---- pipeline: step st transforms from buffer st % 2 while step st+1's
+    // patch is loaded and stored into the other buffer; one barrier per step.
+    // The last step loads its own patch again (into a buffer no longer read),
+    // so every step runs the same code.
+    // Staging two steps ahead: the end of step st loads the patch of step
+    // st+2, which step st+1 converts and stores in two halves (the second
+    // half while the first half's registers hold the next loads' targets).
+    constexpr int UH = (MAXU + 1) / 2;
     const int ns = a.nsteps;
-    stage_load(0);
-    stage_convert();
-    stage_store();
-    __syncthreads();
+    const int pb = a.patch_bytes;
+    stage_load(0, 0, MAXU);
+    stage_convert(0, MAXU);
+    stage_store(0, 0, MAXU);
+    stage_load(min(1, ns - 1), 0, MAXU);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) load_v(x, 0);
-    stage_load(min(1, ns - 1));
-    read_window();
-    transform();
-    stage_convert();
+    for (int c = 0; c < 8; ++c) load_v(0, c, 0);
     __syncthreads();
-    write_u();
-    stage_store();
-    __syncthreads();
-    for (int st = 1; st < ns; ++st) {
-        stage_load(min(st + 1, ns - 1));
+    // the products of one row interleaved with the vector work that follows
+    constexpr int MFR = BF ? 8 : 32;  // MFMAs per row of the pair
+    for (int st = 0; st < ns; ++st) {
+        const int cur = (st & 1) * pb;
+        const int nxt = pb - cur;
+        const int st2 = min(st + 2, ns - 1);
+        column_pass(cur);
         __builtin_amdgcn_sched_barrier(0);
-        read_window();
-        mfma_step(st - 1, st);
-        transform();
-        stage_convert();
-        interleave();
+        stage_convert(0, UH);
+        stage_store(nxt, 0, UH);
+        row_pass(0);
         __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        write_u();
-        stage_store();
+        mfma_row(0, st, min(st + 1, ns - 1));
+        row_pass(1);
+#pragma unroll
+        for (int i = 0; i < MFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, BF ? 12 : 3, 0);  // vector ALU
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_row(1, st, min(st + 1, ns - 1));
+        stage_convert(UH, MAXU);
+        stage_store(nxt, UH, MAXU);
+#pragma unroll
+        for (int i = 0; i < MFR; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, BF ? 20 : 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // both halves of step st+2 are loaded after every filter load this
+        // step waits for: loads complete in order, so a filter wait issued
+        // behind a staging load would wait for the staging load as well
+        stage_load(st2, 0, MAXU);
         __syncthreads();
     }
-    mfma_step(ns - 1, -1);
     __syncthreads();
 
     // ---- output transform, 16 output channels at a time: M[xi][channel][tile]
@@ -492,11 +579,13 @@ __global__ __launch_bounds__(NTHR) void wf6_kernel(Args a) {
         if ((lrow >> 4) == sl) {
             const int col = lrow & 15;
 #pragma unroll
-            for (int x = 0; x < XPW; ++x)
+            for (int x = 0; x < XPW; ++x) {
+                const int xi = 8 * (x < 8 ? ra : rbw) + (x & 7);
 #pragma unroll
                 for (int v4 = 0; v4 < 4; ++v4)
-                    *reinterpret_cast<float4*>(Ms + ((16 * wave + x) * KS + col) * MP + 8 * v4 + 4 * h) =
+                    *reinterpret_cast<float4*>(Ms + (xi * KS + col) * MP + 8 * v4 + 4 * h) =
                         make_float4(acc[x][4 * v4], acc[x][4 * v4 + 1], acc[x][4 * v4 + 2], acc[x][4 * v4 + 3]);
+            }
         }
         __syncthreads();
         for (int pq = tid; pq < TB * KS; pq += NTHR) {
@@ -507,34 +596,34 @@ __global__ __launch_bounds__(NTHR) void wf6_kernel(Args a) {
             if (row >= a.tr * a.tcb || R >= a.NR || tx >= a.tw || k >= a.K) continue;
             const int n = R / a.th, ty = R - n * a.th;
             // t = A^T M, one column of M at a time
-            float t[6][8];
+            float tt[6][8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                float mc[8], o[6];
+                float mc[8], o6[6];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) mc[i] = Ms[((i * 8 + j) * KS + kl) * MP + row];
-                at8(mc, o);
+                at8(mc, o6);
 #pragma unroll
-                for (int p = 0; p < 6; ++p) t[p][j] = o[p];
+                for (int p = 0; p < 6; ++p) tt[p][j] = o6[p];
             }
 #pragma unroll
             for (int p = 0; p < 6; ++p) {
                 const int oh = 6 * ty + p;
                 if (oh >= a.OH) continue;
                 float yr[6];
-                at8(t[p], yr);
+                at8(tt[p], yr);
                 const long long rowoff = n * a.y_img + (static_cast<long long>(k) * a.OH + oh) * a.OW;
 #pragma unroll
                 for (int qq = 0; qq < 6; ++qq) {
                     const int ow = 6 * tx + qq;
                     if (ow >= a.OW) continue;
                     const long long o = rowoff + ow;
-                    float s = BF ? wg_denorm(yr[qq], osx, osw) : yr[qq];
-                    if constexpr (EPI) s = epi_float<T>(s, a.e, k, o);
+                    float sv = BF ? wg_denorm(yr[qq], osx, osw) : yr[qq];
+                    if constexpr (EPI) sv = epi_float<T>(sv, a.e, k, o);
                     if constexpr (BF)
-                        reinterpret_cast<uint16_t*>(a.y)[o] = float_to_bf16(s);
+                        reinterpret_cast<uint16_t*>(a.y)[o] = float_to_bf16(sv);
                     else
-                        reinterpret_cast<float*>(a.y)[o] = s;
+                        reinterpret_cast<float*>(a.y)[o] = sv;
                 }
             }
         }
@@ -607,14 +696,14 @@ __global__ __launch_bounds__(256) void wf6_prepare_kernel(const T* __restrict__ 
 
 struct Plan {
     int E, th, tw, NR, tcb, tr, nrb, ncb, ntk, nchunks, nsteps;
-    int pws, nbk, rp, plane, nunits, maxu;
+    int pws, nbk, nbkp, rp, sk, patch_bytes, nunits, maxu;
     size_t lds, v_bytes;
 };
 
 constexpr int kMaxuBf16 = 2, kMaxuF32 = 4;  // staging units per thread the kernels are built for
 
 inline bool plan(const Prob& p, Plan* pl, std::string* why) {
-    auto no = [&](const char* s) {
+    auto no = [&](const char* s) __attribute__((always_inline)) {
         if (why) *why = s;
         return false;
     };
@@ -659,8 +748,9 @@ inline bool plan(const Prob& p, Plan* pl, std::string* why) {
         for (int tr = std::min<long long>(TB / tcb, NR); tr >= 1; --tr) {
             const int pws = (E - 1 + 6 * tcb + 2 + E - 1) / E * E;
             const int nunits = 8 * tr * (pws / E) * 2;
-            const long long patch = 8LL * 8 * tr * pws * 4;
-            if (nunits > maxu * NTHR || patch > PATCH_MAX) continue;
+            const int nbkp = (pws / E) | 1;
+            const long long patch = 2LL * (2 * 8 * tr * (E * nbkp + 1) + 2 * 6 * tr) * 16;  // two buffers
+            if (nunits > maxu * NTHR || patch + 128 > LDS_MAX) continue;
             const long long nrb = (NR + tr - 1) / tr, ncb = (pl->tw + tcb - 1) / tcb;
             const long long blocks = nrb * ncb * pl->ntk;
             const double rounds = static_cast<double>((blocks + 255) / 256);
@@ -681,11 +771,17 @@ inline bool plan(const Prob& p, Plan* pl, std::string* why) {
     if (best < 0) return no("winograd F(6x6) fused: no tile block fits");
     const long long blocks = static_cast<long long>(pl->nrb) * pl->ncb * pl->ntk;
     if (blocks >= (1LL << 31)) return no("winograd F(6x6) fused: too many workgroups");
-    pl->rp = pl->pws;  // a multiple of 4 dwords: 16-byte staging stores stay aligned
-    pl->plane = 8 * pl->tr * pl->rp;
+    // patch layout: odd block pitch, odd row pitch and a skew per tile row,
+    // chosen with a model of the bank conflicts of the window reads and the
+    // staging stores over the blocks' shapes
+    pl->nbkp = pl->nbk | 1;
+    pl->rp = E * pl->nbkp + 1;
+    pl->sk = 6;
+    pl->patch_bytes = (2 * 8 * pl->tr * pl->rp + 2 * pl->tr * pl->sk) * 16;
     pl->maxu = maxu;
-    pl->lds = std::max<size_t>(U_LDS + 8 * static_cast<size_t>(pl->plane) * 4, M_LDS);
+    pl->lds = std::max<size_t>(2 * static_cast<size_t>(pl->patch_bytes) + 128, M_LDS);
     pl->v_bytes = static_cast<size_t>(64) * pl->ntk * pl->nchunks * 2048;
+    if (pl->v_bytes >= (size_t(1) << 31)) return no("winograd F(6x6) fused: prepared filter of 2 GiB or more");
     return true;
 }
 
@@ -706,9 +802,11 @@ cfwd_status launch_t(const Prob& p, const Plan& pl, const void* x, const void* v
     a.C = p.c; a.H = p.h; a.W = p.w; a.K = p.k; a.OH = p.oh; a.OW = p.ow; a.ph = p.ph; a.pw = p.pw;
     a.x_img = p.x_img; a.y_img = p.y_img;
     a.x_bytes = static_cast<int>(static_cast<long long>(p.n) * p.x_img * p.esize);
+    a.v_bytes = static_cast<int>(pl.v_bytes);
     a.th = pl.th; a.tw = pl.tw; a.NR = pl.NR; a.tcb = pl.tcb; a.tr = pl.tr;
     a.nrb = pl.nrb; a.ncb = pl.ncb; a.ntk = pl.ntk; a.nchunks = pl.nchunks; a.nsteps = pl.nsteps;
-    a.rp = pl.rp; a.plane = pl.plane; a.nbk = pl.nbk; a.nunits = pl.nunits;
+    a.nbk = pl.nbk; a.nunits = pl.nunits; a.nbkp = pl.nbkp; a.rp = pl.rp; a.sk = pl.sk;
+    a.patch_bytes = pl.patch_bytes;
     a.e = e;
     a.xmax = xmax;
     a.wmax = wmax;
