@@ -222,6 +222,7 @@ struct Args {
     int th, tw, NR;          // tile rows and columns per image; tile rows in the batch
     int tcb, tr;             // tile block: tr tile rows of tcb tiles
     int nrb, ncb, ntk, nchunks, nsteps;
+    int kgrp;                // filter slices per group of the work order (divides ntk)
     int nbk, nunits;         // 16-byte load blocks per patch row; staging units
     int nbkp, rp, sk;        // patch layout (16-byte slots): block pitch, row pitch, skew per tile row
     int patch_bytes;         // one patch buffer
@@ -276,12 +277,16 @@ __global__ __launch_bounds__(NTHR) void wf6_kernel(Args a) {
     const int h = lane >> 5;
     const float xsc = BF ? wg_norm(a.xmax) : 1.0f;  // bf16: input scale into the fp16 range
 
-    // work order: the filter slice kt is the slowest index, so each XCD's
-    // contiguous range of blocks shares one slice in its L2
+    // work order: groups of kgrp filter slices are the slowest index and the
+    // slice within a group the fastest, so each XCD's contiguous range of
+    // blocks shares kgrp slices in its L2 and reads each input patch once
+    // from beyond it for the kgrp slices
     int lin = xcd_linear(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
     const int nblk = a.nrb * a.ncb;
-    const int kt = lin / nblk;
-    lin -= kt * nblk;
+    const int kg = lin / (nblk * a.kgrp);
+    lin -= kg * nblk * a.kgrp;
+    const int kt = kg * a.kgrp + lin % a.kgrp;
+    lin /= a.kgrp;
     const int cb = lin % a.ncb;
     const int rb = lin / a.ncb;
     const int R0 = rb * a.tr;        // first tile row of the block (over the batch)
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(256) void wf6_prepare_kernel(const T* __restrict__ 
 // ---------------------------------------------------------------- host plan
 
 struct Plan {
-    int E, th, tw, NR, tcb, tr, nrb, ncb, ntk, nchunks, nsteps;
+    int E, th, tw, NR, tcb, tr, nrb, ncb, ntk, nchunks, nsteps, kgrp;
     int pws, nbk, nbkp, rp, sk, patch_bytes, nunits, maxu;
     size_t lds, v_bytes;
 };
@@ -779,6 +784,11 @@ inline bool plan(const Prob& p, Plan* pl, std::string* why) {
     pl->sk = 6;
     pl->patch_bytes = (2 * 8 * pl->tr * pl->rp + 2 * pl->tr * pl->sk) * 16;
     pl->maxu = maxu;
+    // two filter slices per group when together they take at most half an
+    // XCD's L2 (a slice is 64 positions x C x 32 channels: 1 MiB in bf16's
+    // fp16 form and 2 MiB in fp32 at C = 256)
+    const size_t slice = static_cast<size_t>(64) * p.c * KB * (p.dtype == CFWD_BF16 ? 2 : 4);
+    pl->kgrp = (pl->ntk % 2 == 0 && 2 * slice <= (size_t(2) << 20)) ? 2 : 1;
     pl->lds = std::max<size_t>(2 * static_cast<size_t>(pl->patch_bytes) + 128, M_LDS);
     pl->v_bytes = static_cast<size_t>(64) * pl->ntk * pl->nchunks * 2048;
     if (pl->v_bytes >= (size_t(1) << 31)) return no("winograd F(6x6) fused: prepared filter of 2 GiB or more");
@@ -805,6 +815,7 @@ cfwd_status launch_t(const Prob& p, const Plan& pl, const void* x, const void* v
     a.v_bytes = static_cast<int>(pl.v_bytes);
     a.th = pl.th; a.tw = pl.tw; a.NR = pl.NR; a.tcb = pl.tcb; a.tr = pl.tr;
     a.nrb = pl.nrb; a.ncb = pl.ncb; a.ntk = pl.ntk; a.nchunks = pl.nchunks; a.nsteps = pl.nsteps;
+    a.kgrp = pl.kgrp;
     a.nbk = pl.nbk; a.nunits = pl.nunits; a.nbkp = pl.nbkp; a.rp = pl.rp; a.sk = pl.sk;
     a.patch_bytes = pl.patch_bytes;
     a.e = e;

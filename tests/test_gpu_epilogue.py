@@ -44,6 +44,8 @@ SMALL = [
     ("wino_p0_w16", 2, 48, 16, 16, 64, 3, 3, 1, 0, 1, 1),
     ("deep7x7_c256", 2, 256, 7, 7, 72, 3, 3, 1, 1, 1, 1),
     ("split_c200_k37", 2, 200, 9, 11, 37, 3, 3, 1, 1, 1, 1),
+    # fused Winograd F(6x6) for both float dtypes (64 channels, W a multiple of 8)
+    ("wf6_c64_w24", 2, 64, 14, 24, 40, 3, 3, 1, 1, 1, 1),
 ]
 
 LAYOUTS = [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)]
