@@ -105,15 +105,6 @@ cfwd_status winograd_fused_prepare(const Prob& p, int cfg, const void* w, void* 
 cfwd_status winograd_fused_launch(const Prob& p, int cfg, const void* x, const void* wp, void* scratch, void* y,
                                   const Epi& e, hipStream_t st);
 
-// Fused Winograd F(6x6,3x3) for bf16 or fp32 NCHW (config 1 of F(6x6)): the
-// transformed input stays on chip; scratch only for bf16's input maximum.
-bool winograd_f6_fused_supported(const Prob& p, std::string* why);
-size_t winograd_f6_fused_filter_bytes(const Prob& p);
-size_t winograd_f6_fused_scratch_bytes(const Prob& p);
-cfwd_status winograd_f6_fused_prepare(const Prob& p, const void* w, void* wp, hipStream_t st);
-cfwd_status winograd_f6_fused_launch(const Prob& p, const void* x, const void* wp, void* scratch, void* y,
-                                     const Epi& e, hipStream_t st);
-
 // bf16 Winograd keeps its transformed operands in fp16, whose range is far
 // narrower than bf16's.  Input and filter are therefore scaled by powers of
 // two that bring their largest magnitude into [2^7, 2^8) -- then every

@@ -32,6 +32,7 @@
 // inputs keep fp32 operands on the fp32 matrix cores.  Accumulation is fp32.
 #include "igemm_impl.h"
 #include "winograd_mats.h"
+#include "winograd_f6_fused.h"
 
 namespace cfwd {
 namespace wg {

@@ -40,6 +40,7 @@
 // factors, so (G g G^T) * (B^T d B) is unchanged elementwise.
 #include "igemm_impl.h"
 #include "winograd_mats.h"
+#include "winograd_f6_fused.h"
 
 namespace cfwd {
 namespace wf6 {
