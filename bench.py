@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--fastrun-load", default="", help="Fast-Run map file to load before set-up (its problems are not "
                     "searched again)")
     ap.add_argument("--fastrun-save", default="", help="write the Fast-Run map to this file after set-up")
+    ap.add_argument("--allow-inexact-int8", action="store_true",
+                    help="let Fast-Run time int8 Winograd F(2x2) (outputs within 1 of the exact ones)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain device copy of 1 GiB instead (scales HBM byte counters)")
     return ap.parse_args()
@@ -210,6 +212,8 @@ def main():
 
     if a.fastrun_load:
         B.fastrun_load(a.fastrun_load)
+    if a.allow_inexact_int8:
+        B.fastrun_allow_inexact_int8(True)
     # ---- per-layer set-up: inputs, algorithm (Fast-Run), prepared filter, scratch.
     # LayerPlan is the same sequence of library calls the parity tests run.
     layers = []
@@ -367,7 +371,8 @@ def main():
             "workload": workload, "n": N, "layers": nl, "layout": layout,
             "algo": "+".join(sorted({p["algo"] for p in per_layer})),
             "dispatch": "fastrun_map" if a.algo == "auto" else "fixed",
-            "fastrun_map_loaded": os.path.basename(a.fastrun_load) or None, "rotated_buffer_sets": max(l["nsets"] for l in layers),
+            "fastrun_map_loaded": os.path.basename(a.fastrun_load) or None,
+            "inexact_int8_allowed": bool(a.allow_inexact_int8), "rotated_buffer_sets": max(l["nsets"] for l in layers),
             "gflop_per_step": round(total_flops / 1e9, 3),
             "mb_per_step": round(sum(p["bytes"] for p in per_layer) / 1e6, 2),
             "warm_ms_per_step": round(warm_ms, 5),

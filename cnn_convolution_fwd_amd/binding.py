@@ -30,7 +30,7 @@ EXPORTED = [
     "cfwd_prepare_filter", "cfwd_workspace_size", "cfwd_scratch_size", "cfwd_conv2d_fwd", "cfwd_fastrun_select",
     "cfwd_fastrun_workspace_size", "cfwd_fastrun_lookup", "cfwd_fastrun_load", "cfwd_fastrun_save",
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
-    "cfwd_conv2d_fwd_noalloc", "cfwd_conv2d_fwd_ex",
+    "cfwd_conv2d_fwd_noalloc", "cfwd_conv2d_fwd_ex", "cfwd_fastrun_allow_inexact_int8",
 ]
 ACT_NONE, ACT_RELU = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CFWD_NOALLOC_SCRATCH_BYTES
@@ -98,6 +98,7 @@ def _lib():
             "cfwd_fastrun_load": [ctypes.c_char_p],
             "cfwd_fastrun_save": [ctypes.c_char_p],
             "cfwd_fastrun_clear": [],
+            "cfwd_fastrun_allow_inexact_int8": [ctypes.c_int],
             "cfwd_fastrun_choose": [P(Algo), P(ctypes.c_float), ctypes.c_int, ctypes.c_int, P(ctypes.c_int),
                                     P(ctypes.c_int)],
         }
@@ -211,6 +212,11 @@ def fastrun_save(path: str):
 
 def fastrun_clear():
     _check(_lib().cfwd_fastrun_clear())
+
+
+def fastrun_allow_inexact_int8(allow: bool):
+    """Let int8 candidates that may differ by 1 from the exact result (int8 Winograd F(2x2)) join Fast-Run."""
+    _check(_lib().cfwd_fastrun_allow_inexact_int8(1 if allow else 0))
 
 
 def fastrun_choose(cands: Sequence[Algo], times: Sequence[Sequence[float]], gate_ok: Sequence[bool]) -> int:

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -24,6 +25,7 @@
 #include <vector>
 
 #include "internal.h"
+#include "winograd_i8.h"
 
 #define CFWD_VERSION "0.1.0"
 
@@ -174,11 +176,24 @@ bool supported(const Prob& p, cfwd_algo_kind k, int cfg, std::string* why) {
 const cfwd_algo_kind kFamilies[] = {CFWD_ALGO_IMPLICIT_GEMM, CFWD_ALGO_POINTWISE, CFWD_ALGO_DIRECT,
                                     CFWD_ALGO_WINOGRAD_F2X2_3X3, CFWD_ALGO_WINOGRAD_F6X6_3X3};
 
+// int8 results that are not always the exact integer ones: Winograd F(2x2)
+// with its float intermediate.  Such candidates join Fast-Run only when the
+// caller allows them (cfwd_fastrun_allow_inexact_int8), and then pass its
+// gate if no output is more than 1 away from the exact result.
+std::atomic<int> g_allow_inexact_i8{0};
+
+bool inexact_i8(const Prob& p, cfwd_algo_kind k) {
+    return p.dtype == CFWD_I8 && k == CFWD_ALGO_WINOGRAD_F2X2_3X3;
+}
+
 std::vector<cfwd_algo> candidates(const Prob& p) {
     std::vector<cfwd_algo> out;
-    for (cfwd_algo_kind k : kFamilies)
+    const bool inexact_ok = g_allow_inexact_i8.load() != 0;
+    for (cfwd_algo_kind k : kFamilies) {
+        if (inexact_i8(p, k) && !inexact_ok) continue;
         for (int c = 0; c < num_configs(k); ++c)
             if (supported(p, k, c, nullptr)) out.push_back(cfwd_algo{k, c, 0.0f});
+    }
     return out;
 }
 
@@ -358,7 +373,10 @@ cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w,
         case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, scratch, e, st); break;
         case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, e, st); break;
         case CFWD_ALGO_DIRECT: s = direct_launch(p, a.config_id, x, w, scale, y, e, st); break;
-        case CFWD_ALGO_WINOGRAD_F2X2_3X3: s = winograd_launch(p, 2, a.config_id, x, wp, scratch, y, e, st); break;
+        case CFWD_ALGO_WINOGRAD_F2X2_3X3:
+            s = (p.dtype == CFWD_I8) ? winograd_i8_launch(p, x, wp, scale, scratch, y, e, st)
+                                     : winograd_launch(p, 2, a.config_id, x, wp, scratch, y, e, st);
+            break;
         case CFWD_ALGO_WINOGRAD_F6X6_3X3: s = winograd_launch(p, 6, a.config_id, x, wp, scratch, y, e, st); break;
         default: return set_error(CFWD_ERR_INVALID_ARG, "unknown algorithm kind");
     }
@@ -751,7 +769,10 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
         if (s != CFWD_OK) break;
         float err;
         std::memcpy(&err, &h[0], 4);
-        ok[i] = (p.dtype == CFWD_I8) ? (h[1] == 0) : (h[1] == 0 && err <= gate_tolerance(p, a.kind));
+        if (p.dtype == CFWD_I8)  // h[0]: largest |difference| of the int8 outputs
+            ok[i] = inexact_i8(p, a.kind) ? (h[0] <= 1u) : (h[1] == 0);
+        else
+            ok[i] = h[1] == 0 && err <= gate_tolerance(p, a.kind);
     }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
@@ -919,6 +940,11 @@ cfwd_status cfwd_fastrun_load(const char* path) {
 // given n candidates in Fast-Run order with reps timings each (row-major) and
 // a pass/fail flag per candidate, writes the index that would be chosen (or
 // -1) to *chosen.
+cfwd_status cfwd_fastrun_allow_inexact_int8(int allow) {
+    g_allow_inexact_i8.store(allow ? 1 : 0);
+    return CFWD_OK;
+}
+
 cfwd_status cfwd_fastrun_choose(const cfwd_algo* cands, const float* times, int n, int reps, const int* gate_ok,
                                 int* chosen) {
     if (!cands || !times || !gate_ok || !chosen || n < 0 || reps <= 0)

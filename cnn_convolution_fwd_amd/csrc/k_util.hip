@@ -60,13 +60,23 @@ __global__ __launch_bounds__(256) void gate_float(const T* __restrict__ cand, co
     }
 }
 
+// stats[0]: largest |cand - ref|; stats[1]: outputs that differ
 __global__ __launch_bounds__(256) void gate_i8(const int8_t* __restrict__ cand, const int8_t* __restrict__ ref,
                                                long long n, unsigned* stats) {
-    unsigned bad = 0;
-    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<long long>(gridDim.x) * 256)
-        bad += (cand[i] != ref[i]) ? 1u : 0u;
-    for (int off = 32; off > 0; off >>= 1) bad += static_cast<unsigned>(__shfl_down(static_cast<int>(bad), off));
-    if ((threadIdx.x & 63) == 0) atomicAdd(stats + 1, bad);
+    unsigned worst = 0, bad = 0;
+    for (long long i = blockIdx.x * 256LL + threadIdx.x; i < n; i += static_cast<long long>(gridDim.x) * 256) {
+        const int d = static_cast<int>(cand[i]) - static_cast<int>(ref[i]);
+        bad += (d != 0) ? 1u : 0u;
+        worst = max(worst, static_cast<unsigned>(d < 0 ? -d : d));
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        worst = max(worst, static_cast<unsigned>(__shfl_down(static_cast<int>(worst), off)));
+        bad += static_cast<unsigned>(__shfl_down(static_cast<int>(bad), off));
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicMax(stats, worst);
+        atomicAdd(stats + 1, bad);
+    }
 }
 
 // Plain (cache-allocating) 16-byte stores over the whole buffer: afterwards

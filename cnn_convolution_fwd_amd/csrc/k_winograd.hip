@@ -30,7 +30,10 @@
 // bf16 inputs use fp16 transformed operands (fp16 keeps 11 bits; the
 // transform entries reach 32, so bf16's 8 bits lose too much for F(6x6)); fp32
 // inputs keep fp32 operands on the fp32 matrix cores.  Accumulation is fp32.
+#include <type_traits>
+
 #include "igemm_impl.h"
+#include "winograd_i8.h"
 #include "winograd_mats.h"
 #include "winograd_f6_fused.h"
 
@@ -50,6 +53,12 @@ template <> struct OpT<bf16_t> {
     using type = _Float16;
     static __device__ __forceinline__ _Float16 from(float v) { return static_cast<_Float16>(v); }
 };
+// int8 F(2x2): B^T d B holds multiples of 1/4 of magnitude <= 512 and G g G^T
+// integers of magnitude <= 1152 (G has entries 0, +-1), both exact in fp16
+template <> struct OpT<int8_t> {
+    using type = _Float16;
+    static __device__ __forceinline__ _Float16 from(float v) { return static_cast<_Float16>(v); }
+};
 
 // 32x32 fragments with fp16 operands (bf16 inputs) or fp32 operands.
 template <typename T> struct WMma;
@@ -60,6 +69,7 @@ template <> struct WMma<bf16_t> {
     }
     static constexpr int pslot(int i, int h) { return 2 * i + h; }
 };
+template <> struct WMma<int8_t> : WMma<bf16_t> {};
 template <> struct WMma<float> {
     static __device__ __forceinline__ void piece(f32x16& c, const uint4& a, const uint4& b) {
         c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
@@ -87,8 +97,8 @@ inline bool geometry(const Prob& p, int m, Geo* g, std::string* why) {
         if (why) *why = "winograd: needs 3x3, stride 1, dilation 1, groups 1";
         return false;
     }
-    if (p.dtype == CFWD_I8) {
-        if (why) *why = "winograd: float dtypes only (int8 needs an exact integer transform)";
+    if (p.dtype == CFWD_I8 && m != 2) {
+        if (why) *why = "winograd: int8 only with F(2x2) (the F(6x6) transforms are not exact in fp16)";
         return false;
     }
     g->m = m;
@@ -349,7 +359,8 @@ template <typename T, int XB, int M, bool EPI>  // EPI: fused epilogue compiled 
 __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* __restrict__ U, const uint8_t* __restrict__ V,
                                                    T* __restrict__ y, int K, int OH, int OW, long long y_img, int th,
                                                    int tw, int T_, int Tpad, int nchunks, int ntk, Epi ep,
-                                                   const unsigned* __restrict__ xmax, const unsigned* __restrict__ wmax) {
+                                                   const unsigned* __restrict__ xmax, const unsigned* __restrict__ wmax,
+                                                   const float* __restrict__ scale) {
     constexpr int A = M + 2;
     constexpr int XI = A * A;
     constexpr int NW = GemmGeo<M>::NW;
@@ -492,12 +503,21 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
                         }
                         const long long o = n * y_img + act_off<XB>(k, oh, ow, OH, OW);
                         T* dst = y + o;
-                        s = wg_denorm(s, osx, osw);  // bf16: undo the operand scales
-                        if constexpr (EPI) s = epi_float<T>(s, ep, k, o);  // fused epilogue
-                        if constexpr (sizeof(T) == 4)
-                            *dst = s;
-                        else
-                            dst->bits = float_to_bf16(s);
+                        if constexpr (std::is_same_v<T, int8_t>) {
+                            // the exact result is an integer: round the float
+                            // one to it, then requantise as the integer paths do
+                            const int acc = __float2int_rn(s);
+                            const uint32_t q = EPI ? requant_i8_epi_bits(acc, scale[k], ep, k, o)
+                                                   : requant_i8_bits(acc, scale[k]);
+                            *dst = static_cast<int8_t>(q & 0xffu);
+                        } else {
+                            s = wg_denorm(s, osx, osw);  // bf16: undo the operand scales
+                            if constexpr (EPI) s = epi_float<T>(s, ep, k, o);  // fused epilogue
+                            if constexpr (sizeof(T) == 4)
+                                *dst = s;
+                            else
+                                dst->bits = float_to_bf16(s);
+                        }
                     }
                 }
             }
@@ -508,7 +528,7 @@ __global__ __launch_bounds__(GemmGeo<M>::NTHR) void gemm_kernel(const uint8_t* _
 
 template <typename T, int XB, int M>
 cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y, const Epi& e,
-                     hipStream_t st) {
+                     const float* scale, hipStream_t st) {
     // bf16: the operands' maxima sit after the transformed input (this
     // call's) and after the prepared filter (written by the prepare step)
     unsigned* xmax = g.hdr ? reinterpret_cast<unsigned*>(static_cast<uint8_t*>(ubuf) + g.u_bytes) : nullptr;
@@ -553,17 +573,17 @@ cfwd_status launch_t(const Prob& p, const Geo& g, const void* x, const void* vpr
     const unsigned blocks = static_cast<unsigned>(g.ntb * g.ntk);
     kern<<<blocks, GemmGeo<M>::NTHR, lds, st>>>(static_cast<const uint8_t*>(ubuf), static_cast<const uint8_t*>(vprep),
                                    static_cast<T*>(y), p.k, p.oh, p.ow, p.y_img, g.th, g.tw, g.T, g.Tpad, g.nchunks,
-                                   g.ntk, e, xmax, wmax);
+                                   g.ntk, e, xmax, wmax, scale);
     return check_hip(hipGetLastError(), "winograd gemm launch");
 }
 
 template <typename T, int M>
 cfwd_status launch_m(const Prob& p, const Geo& g, const void* x, const void* vprep, void* ubuf, void* y, const Epi& e,
-                     hipStream_t st) {
+                     hipStream_t st, const float* scale = nullptr) {
     switch (p.xb) {
-        case 1: return launch_t<T, 1, M>(p, g, x, vprep, ubuf, y, e, st);
-        case 4: return launch_t<T, 4, M>(p, g, x, vprep, ubuf, y, e, st);
-        case 8: return launch_t<T, 8, M>(p, g, x, vprep, ubuf, y, e, st);
+        case 1: return launch_t<T, 1, M>(p, g, x, vprep, ubuf, y, e, scale, st);
+        case 4: return launch_t<T, 4, M>(p, g, x, vprep, ubuf, y, e, scale, st);
+        case 8: return launch_t<T, 8, M>(p, g, x, vprep, ubuf, y, e, scale, st);
         default: return set_error(CFWD_ERR_UNSUPPORTED, "winograd: bad channel block");
     }
 }
@@ -640,7 +660,10 @@ cfwd_status winograd_prepare(const Prob& p, int m, int cfg, const void* w, void*
     if (blocks > 65536) blocks = 65536;
     const unsigned nb = static_cast<unsigned>(blocks);
     uint8_t* out = static_cast<uint8_t*>(wp);
-    if (p.dtype == CFWD_F32) {
+    if (p.dtype == CFWD_I8) {  // F(2x2) only (geometry): integer G, no scaling
+        wg::prepare_kernel<int8_t, 2><<<nb, 256, 0, st>>>(static_cast<const int8_t*>(w), out, p.k, p.c, g.KB, g.ntk,
+                                                          g.nchunks, nullptr);
+    } else if (p.dtype == CFWD_F32) {
         if (m == 2)
             wg::prepare_kernel<float, 2><<<nb, 256, 0, st>>>(static_cast<const float*>(w), out, p.k, p.c, g.KB, g.ntk,
                                                              g.nchunks, nullptr);
@@ -671,11 +694,24 @@ cfwd_status winograd_launch(const Prob& p, int m, int cfg, const void* x, const 
     if (!wg::geometry(p, m, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (scratch == nullptr || wp == nullptr)
         return set_error(CFWD_ERR_WORKSPACE, "winograd: prepared filter and scratch are required");
+    if (p.dtype == CFWD_I8) return set_error(CFWD_ERR_INVALID_ARG, "winograd: int8 goes through winograd_i8_launch");
     if (p.dtype == CFWD_F32)
         return (m == 2) ? wg::launch_m<float, 2>(p, g, x, wp, scratch, y, e, st)
                         : wg::launch_m<float, 6>(p, g, x, wp, scratch, y, e, st);
     return (m == 2) ? wg::launch_m<bf16_t, 2>(p, g, x, wp, scratch, y, e, st)
                     : wg::launch_m<bf16_t, 6>(p, g, x, wp, scratch, y, e, st);
+}
+
+cfwd_status winograd_i8_launch(const Prob& p, const void* x, const void* wp, const float* scale, void* scratch,
+                               void* y, const Epi& e, hipStream_t st) {
+    wg::Geo g;
+    std::string why;
+    if (p.dtype != CFWD_I8) return set_error(CFWD_ERR_INVALID_ARG, "winograd_i8_launch: int8 problems only");
+    if (!wg::geometry(p, 2, &g, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    if (scratch == nullptr || wp == nullptr)
+        return set_error(CFWD_ERR_WORKSPACE, "winograd: prepared filter and scratch are required");
+    if (scale == nullptr) return set_error(CFWD_ERR_INVALID_ARG, "winograd int8: requant scales are required");
+    return wg::launch_m<int8_t, 2>(p, g, x, wp, scratch, y, e, st, scale);
 }
 
 }  // namespace cfwd

@@ -18,7 +18,8 @@
  *                   are staged in LDS and multiplied on the matrix cores.
  *   WINOGRAD_F2X2_3X3 / WINOGRAD_F6X6_3X3
  *                   F(m x m, 3 x 3) minimal filtering for 3x3, stride 1,
- *                   dilation 1, groups 1, float dtypes only.  bf16 runs its
+ *                   dilation 1, groups 1; float dtypes, and int8 for
+ *                   F(2x2) config 0 (below).  bf16 runs its
  *                   transformed operands in fp16 (11 significant bits); to
  *                   keep them in fp16's range, input and filter are scaled by
  *                   powers of two that bring each one's largest magnitude
@@ -29,6 +30,17 @@
  *                   largest magnitude become fp16 subnormals and lose
  *                   precision; the Fast-Run accuracy gate sees that on the
  *                   caller's data.
+ *                   int8 F(2x2) (MegEngine Beta release article, section
+ *                   "业界领先的原生 ARM 推理性能": int8 Winograd with float as
+ *                   the intermediate format, no narrowing of the weights):
+ *                   B^T d B (multiples of 1/4, |.| <= 512) and G g G^T
+ *                   (integers, |.| <= 1152) are fp16 operands, exactly; the
+ *                   channel sums and the output transform are fp32, then
+ *                   rounded to the nearest integer and requantised as below.
+ *                   Exact while every fp32 partial sum stays below 2^22 in
+ *                   magnitude; beyond that an output can be 1 away from the
+ *                   exact one.  Runs when named explicitly; a Fast-Run
+ *                   candidate only after cfwd_fastrun_allow_inexact_int8(1).
  *   DIRECT          direct summation; the depthwise (G = C = K) path.
  *   POINTWISE       1x1 convolution as a low-K matrix product.
  *   AUTO            resolved per problem: a Fast-Run map entry if one exists,
@@ -227,7 +239,8 @@ cfwd_status cfwd_conv2d_fwd_noalloc(const cfwd_conv_desc *desc, cfwd_algo algo, 
  * Cache and L2 are flushed by overwriting a 512 MiB region of the workspace
  * unless x and y together already exceed that, so candidates are timed from
  * HBM), reject any whose output fails the accuracy gate against the generic
- * DIRECT kernel's result on the same data (bit-identical for int8;
+ * DIRECT kernel's result on the same data (bit-identical for int8, except
+ * int8 Winograd F(2x2): no output more than 1 away;
  * normalised error <= 1e-5 fp32 except Winograd F(6x6), 1e-3 fp32 F(6x6),
  * 1e-2 bf16; NaN or infinity fails), keep the fastest (times within 1% count
  * as equal and the earlier candidate wins), record it in the map and return
@@ -250,6 +263,13 @@ cfwd_status cfwd_fastrun_lookup(const cfwd_conv_desc *desc, cfwd_algo *algo);
 cfwd_status cfwd_fastrun_load(const char *path);
 cfwd_status cfwd_fastrun_save(const char *path);
 cfwd_status cfwd_fastrun_clear(void);
+
+/* Whether int8 candidates whose results are not always bit-identical to the
+ * integer ones (int8 Winograd F(2x2), see WINOGRAD_F2X2_3X3 above) take part
+ * in cfwd_list_candidates and cfwd_fastrun_select: 0 (the default) = no,
+ * nonzero = yes.  Process-wide; an algorithm named explicitly runs either
+ * way, and a Fast-Run map entry chosen while they were allowed stays in use. */
+cfwd_status cfwd_fastrun_allow_inexact_int8(int allow);
 
 /* The host-side part of Fast-Run's choice, for callers that time candidates
  * themselves (and for testing the rule without a GPU): cands[n] in Fast-Run

@@ -91,12 +91,44 @@ def test_candidates_order_and_validity():
 def test_winograd_refuses_unsupported_problems():
     for desc in (B.make_desc(1, 8, 8, 8, 8, 3, 3, 2, 1, dtype="f32"),       # stride 2
                  B.make_desc(1, 8, 8, 8, 8, 5, 5, 1, 2, dtype="f32"),       # 5x5
-                 B.make_desc(1, 8, 8, 8, 8, 3, 3, 1, 1, dtype="i8"),        # int8
+                 B.make_desc(1, 8, 8, 8, 8, 3, 3, 2, 1, dtype="i8"),        # int8 stride 2
                  B.make_desc(1, 8, 8, 8, 8, 3, 3, 1, 1, 1, 2, dtype="f32")):  # groups
         for kind in ("winograd_f2x2_3x3", "winograd_f6x6_3x3"):
             with pytest.raises(B.CfwdError) as e:
                 B.resolve_algo(desc, B.algo(kind))
             assert e.value.status == B.ERR_UNSUPPORTED
+    # int8: F(2x2) three-launch form only (F(6x6) transforms are not exact in fp16)
+    i8 = B.make_desc(1, 8, 8, 8, 8, 3, 3, 1, 1, dtype="i8")
+    with pytest.raises(B.CfwdError) as e:
+        B.resolve_algo(i8, B.algo("winograd_f6x6_3x3"))
+    assert e.value.status == B.ERR_UNSUPPORTED
+    for cfg in (1, 2):
+        with pytest.raises(B.CfwdError):
+            B.resolve_algo(i8, B.algo("winograd_f2x2_3x3", cfg))
+
+
+@pytest.mark.parametrize("layout,xb", [("NCHW", None), ("NCHWX", 4), ("NCHWX", 8)])
+def test_int8_winograd_is_opt_in(layout, xb):
+    """int8 Winograd F(2x2) runs when named, and joins the candidate list only
+    after cfwd_fastrun_allow_inexact_int8(1); AUTO never picks it unmeasured."""
+    desc = B.make_desc(2, 64, 56, 56, 64, 3, 3, 1, 1, 1, 1, layout, xb, "i8")
+    a = B.resolve_algo(desc, B.algo("winograd_f2x2_3x3"))
+    assert (a.kind, a.config_id) == (B.ALGO_WINOGRAD_F2X2_3X3, 0)
+    # prepared filter: 16 positions x 1 K block of 64 x 2 chunks of 32 channels x 64 x 64 bytes
+    assert B.filter_size(desc, a) == 16 * 1 * 2 * 64 * 64
+    # scratch: 16 positions x 2 chunks x 2 * 28 * 28 tiles (padded to 64) x 64 bytes, no maxima area
+    tiles = (2 * 28 * 28 + 63) // 64 * 64
+    assert B.scratch_size(desc, a) == 16 * 2 * tiles * 64
+    kinds = lambda: [x.kind for x in B.list_candidates(desc)]  # noqa: E731
+    try:
+        assert B.ALGO_WINOGRAD_F2X2_3X3 not in kinds()
+        B.fastrun_allow_inexact_int8(True)
+        assert B.ALGO_WINOGRAD_F2X2_3X3 in kinds()
+        assert B.fastrun_workspace_size(desc) >= B.workspace_size(desc, a)
+    finally:
+        B.fastrun_allow_inexact_int8(False)
+    assert B.ALGO_WINOGRAD_F2X2_3X3 not in kinds()
+    assert B.resolve_algo(desc, B.algo()).kind != B.ALGO_WINOGRAD_F2X2_3X3
 
 
 def test_filter_and_workspace_sizes():
