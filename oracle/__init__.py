@@ -184,6 +184,32 @@ class Oracle:
         y, den = self.conv2d(x, w, stride, padding, dilation, groups)
         return self.epilogue(y, den, bias, residual, relu)
 
+    # ---- bottleneck block (Momenta talk, sections "優化1：Bottleneck" and
+    # "Operator的粒度"): three convolutions chained, each with its epilogue
+
+    def bottleneck(self, x, w1, w2, w3, b1=None, b2=None, b3=None, residual=None, relu=(False, False, False)):
+        """fp64 (y, den) of a bottleneck block on NCHW ``x``.
+
+        t1 = act1(conv(x, w1) + b1)            1x1, C -> M
+        t2 = act2(conv(t1, w2, pad 1) + b2)    3x3, zero padding 1, M -> M
+        y  = act3(conv(t2, w3) + b3 + residual) 1x1, M -> K
+        all stride 1, act = ReLU where ``relu`` says so, nothing rounded in
+        between.  ``den`` is the chain's error normaliser: each stage's
+        normaliser passed through the next convolution with |w|, plus |bias|
+        (and |residual| at the end).  A relative rounding of size eps at any
+        stage (a stored intermediate, an accumulation) moves y by at most
+        about eps * den, since |t_i| <= den_i and ReLU does not enlarge
+        differences.
+        """
+        r1, r2, r3 = relu
+        t1, d1 = self.conv2d_fused(x, w1, b1, None, r1)
+        y2, _ = self.conv2d(t1, w2, 1, 1)
+        d2, _ = self.conv2d(d1, np.abs(np.asarray(w2, dtype=np.float64)), 1, 1)
+        t2, d2 = self.epilogue(y2, d2, b2, None, r2)
+        y3, _ = self.conv2d(t2, w3)
+        d3, _ = self.conv2d(d2, np.abs(np.asarray(w3, dtype=np.float64)))
+        return self.epilogue(y3, d3, b3, residual, r3)
+
     def requant_epi(self, acc, scale, bias=None, residual=None, relu=False):
         """int8 outputs of the fused int8 epilogue over [N, K, ...] accumulators."""
         acc = np.ascontiguousarray(acc, dtype=np.int64)
@@ -307,6 +333,10 @@ def epilogue(*a, **k):
 
 def conv2d_fused(*a, **k):
     return default().conv2d_fused(*a, **k)
+
+
+def bottleneck(*a, **k):
+    return default().bottleneck(*a, **k)
 
 
 def requant_epi(*a, **k):
