@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--fastrun-load", default="", help="Fast-Run map file to load before set-up (its problems are not "
                     "searched again)")
     ap.add_argument("--fastrun-save", default="", help="write the Fast-Run map to this file after set-up")
+    ap.add_argument("--block", default="layers", choices=["layers", "fused"],
+                    help="bottleneck workload: its three layers one by one, or the fused block kernel")
     ap.add_argument("--allow-inexact-int8", action="store_true",
                     help="let Fast-Run time int8 Winograd F(2x2) (outputs within 1 of the exact ones)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -174,7 +176,8 @@ def main():
 
     from cnn_convolution_fwd_amd import binding as B
     from cnn_convolution_fwd_amd import telemetry
-    from cnn_convolution_fwd_amd.roofline import PEAK, bound, layer_algo_flops, layer_bytes, layer_flops
+    from cnn_convolution_fwd_amd.roofline import (PEAK, block_algo_flops, block_bytes, block_flops, bound,
+                                                   layer_algo_flops, layer_bytes, layer_flops)
     from cnn_convolution_fwd_amd.workloads import (CONFIGS, bf16_bits, epilogue_inputs, float_problem, int8_problem,
                                                     pack_nchwx)
 
@@ -193,6 +196,10 @@ def main():
     dtype = a.dtype or dtypes[0]
     if dtype not in dtypes:
         print("workload %s runs in %s" % (base, "/".join(dtypes)), file=sys.stderr)
+        sys.exit(2)
+    if a.block == "fused" and (base != "bottleneck_1x1_3x3_1x1_56x56" or a.layers or a.epilogue == "unfused"):
+        print("--block fused runs the whole bottleneck workload (no --layers, epilogue none or fused)",
+              file=sys.stderr)
         sys.exit(2)
     if a.epilogue == "unfused" and dtype == "i8":
         print("an unfused int8 epilogue would need the int32 accumulators; use --epilogue fused", file=sys.stderr)
@@ -217,7 +224,33 @@ def main():
     # ---- per-layer set-up: inputs, algorithm (Fast-Run), prepared filter, scratch.
     # LayerPlan is the same sequence of library calls the parity tests run.
     layers = []
-    for li in layer_ids:
+    if a.block == "fused":
+        # the three layers as one fused block: x and weights drawn as each
+        # layer's standalone problem, the epilogues those layers would take
+        prs = [float_problem(cfg_idx, li, n=N, dtype=dtype) for li in layer_ids]
+        Ls = [cfg.layers[li] for li in layer_ids]
+        x0 = to_dev(prs[0].x)
+        w1, w2, w3 = (to_dev(p.w) for p in prs)
+        desc = B.bottleneck_desc_for(x0, w1, w3)
+        B.bottleneck_check(desc)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        w2p = B.bottleneck_prepare(w2, desc)
+        e1.record()
+        torch.cuda.synchronize()
+        biases, relus, res0 = [None] * 3, [False] * 3, None
+        if a.epilogue == "fused":
+            for j, (li, L) in enumerate(zip(layer_ids, Ls)):
+                epi = epilogue_inputs((N, L.k, L.h, L.w), dtype, 7000 + li)
+                biases[j] = torch.from_numpy(epi.bias).to(dev)
+                relus[j] = True
+                if (cfg_idx, li) in RESIDUAL_LAYERS:
+                    res0 = to_dev(epi.residual)
+        blk = dict(block=True, Ls=Ls, prs=prs, x0=x0, w=(w1, w2p, w3), desc=desc, biases=biases, relus=relus,
+                   res0=res0, y0=torch.empty((N, Ls[2].k, Ls[2].h, Ls[2].w), dtype=x0.dtype, device=dev),
+                   prepare_ms=e0.elapsed_time(e1))
+        layers.append(blk)
+    for li in (layer_ids if a.block == "layers" else []):
         L = cfg.layers[li]
         if int8:
             pr = int8_problem(cfg_idx, li, n=N)
@@ -264,6 +297,16 @@ def main():
         y = l["ys"][i % ns]
         res = l["rs"][i % ns] if l["rs"] is not None else None
         fused = a.epilogue == "fused"
+        if l.get("block"):
+            w1, w2p, w3 = l["w"]
+            ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+            r = l["relus"]
+            ep = B.BottleneckEpilogue(*(ptr(b) for b in l["biases"]), ptr(res), int(r[0]), int(r[1]), int(r[2]))
+            st = B.bottleneck_fwd_raw(l["desc"], l["xs"][i % ns].data_ptr(), w1.data_ptr(), w2p.data_ptr(),
+                                      w3.data_ptr(), ep, y.data_ptr(), sptr)
+            if st != 0:
+                raise RuntimeError(B.library().cfwd_last_error().decode())
+            return
         st = l["plan"].launch_raw(l["xs"][i % ns].data_ptr(), y.data_ptr(), sptr,
                                   res.data_ptr() if (fused and res is not None) else 0)
         if st != 0:
@@ -336,11 +379,20 @@ def main():
     total_flops = 0
     per_layer = []
     for l, t in zip(layers, layer_avg):
-        L = l["L"]
-        name = l["plan"].name
-        fl = layer_flops(L, N)               # direct-equivalent (the metric)
-        afl = layer_algo_flops(L, N, name)   # what the chosen algorithm performs
-        by = layer_bytes(L, N, dtype)
+        if l.get("block"):
+            L1, L3 = l["Ls"][0], l["Ls"][2]
+            dims = (N, L1.c, L1.h, L1.w, L1.k, L3.k)
+            L = type(L1)("bottleneck_block", L1.c, L3.k, L1.h, L1.w, 1, 1, 1, 0, 1, 1)
+            name = "bottleneck_fused"
+            fl, afl = block_flops(*dims), block_algo_flops(*dims)
+            by = block_bytes(*dims, 2)
+            l["plan"] = type("P", (), {"name": name, "prepare_ms": l["prepare_ms"]})()
+        else:
+            L = l["L"]
+            name = l["plan"].name
+            fl = layer_flops(L, N)               # direct-equivalent (the metric)
+            afl = layer_algo_flops(L, N, name)   # what the chosen algorithm performs
+            by = layer_bytes(L, N, dtype)
         kind, _ = bound(afl, by, peak_key)
         total_flops += fl
         if kind == "hbm":
@@ -378,6 +430,7 @@ def main():
             "warm_ms_per_step": round(warm_ms, 5),
             "filter_prepare_ms": round(sum(p["prepare_ms"] for p in per_layer), 5),
             "epilogue": a.epilogue,
+            "block": a.block,
         },
         "gpu_telemetry": gpu_telemetry,
         "roofline": {
@@ -404,6 +457,10 @@ def main():
         def run_oracle(nimg):
             t0 = time.perf_counter()
             for l in layers:
+                if l.get("block"):
+                    p0, p1, p2 = l["prs"]
+                    oracle.bottleneck(p0.x[:nimg], p0.w, p1.w, p2.w)
+                    continue
                 L, pr = l["L"], l["pr"]
                 if int8:
                     oracle.conv2d_int8_requant(pr.x[:nimg], pr.w, pr.scale, L.stride, L.pad, L.dil, L.groups)
@@ -418,7 +475,8 @@ def main():
             nimg = max(1, min(N, int(a.cpu_budget / t1) - 1))
             if nimg > 1:
                 t1 = run_oracle(nimg)
-        sflops = sum(layer_flops(l["L"], nimg) for l in layers)
+        sflops = sum(block_flops(nimg, l["Ls"][0].c, l["Ls"][0].h, l["Ls"][0].w, l["Ls"][0].k, l["Ls"][2].k)
+                     if l.get("block") else layer_flops(l["L"], nimg) for l in layers)
         out["cpu_baseline"] = {
             "value": round(sflops / t1 / 1e12, 6),
             "unit": unit,

@@ -31,6 +31,7 @@ EXPORTED = [
     "cfwd_fastrun_workspace_size", "cfwd_fastrun_lookup", "cfwd_fastrun_load", "cfwd_fastrun_save",
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
     "cfwd_conv2d_fwd_noalloc", "cfwd_conv2d_fwd_ex", "cfwd_fastrun_allow_inexact_int8",
+    "cfwd_bottleneck_check", "cfwd_bottleneck_filter_size", "cfwd_bottleneck_prepare", "cfwd_bottleneck_fwd",
 ]
 ACT_NONE, ACT_RELU = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CFWD_NOALLOC_SCRATCH_BYTES
@@ -45,6 +46,18 @@ class ConvDesc(ctypes.Structure):
 class Epilogue(ctypes.Structure):
     """cfwd_epilogue: bias [K] (fp32, or int32 for int8), residual (y's shape / layout / dtype), activation."""
     _fields_ = [("bias", ctypes.c_void_p), ("residual", ctypes.c_void_p), ("act", ctypes.c_int)]
+
+
+class BottleneckDesc(ctypes.Structure):
+    """cfwd_bottleneck_desc: x [N, C, H, W], inner channels ``mid``, output channels ``k``."""
+    _fields_ = [(n, ctypes.c_int) for n in ("n", "c", "h", "w", "mid", "k")] + [("dtype", ctypes.c_int)]
+
+
+class BottleneckEpilogue(ctypes.Structure):
+    """cfwd_bottleneck_epilogue: fp32 biases b1 [mid], b2 [mid], b3 [K], bf16 residual, ReLU after each stage."""
+    _fields_ = [("b1", ctypes.c_void_p), ("b2", ctypes.c_void_p), ("b3", ctypes.c_void_p),
+                ("residual", ctypes.c_void_p), ("relu1", ctypes.c_int), ("relu2", ctypes.c_int),
+                ("relu3", ctypes.c_int)]
 
 
 class Algo(ctypes.Structure):
@@ -99,6 +112,10 @@ def _lib():
             "cfwd_fastrun_save": [ctypes.c_char_p],
             "cfwd_fastrun_clear": [],
             "cfwd_fastrun_allow_inexact_int8": [ctypes.c_int],
+            "cfwd_bottleneck_check": [P(BottleneckDesc)],
+            "cfwd_bottleneck_filter_size": [P(BottleneckDesc), P(sz)],
+            "cfwd_bottleneck_prepare": [P(BottleneckDesc), vp, vp, sz, vp],
+            "cfwd_bottleneck_fwd": [P(BottleneckDesc), vp, vp, vp, vp, P(BottleneckEpilogue), vp, vp],
             "cfwd_fastrun_choose": [P(Algo), P(ctypes.c_float), ctypes.c_int, ctypes.c_int, P(ctypes.c_int),
                                     P(ctypes.c_int)],
         }
@@ -464,3 +481,60 @@ class LayerPlan:
         _check(self.launch_raw(x.data_ptr(), out.data_ptr(), _stream(),
                                residual.data_ptr() if residual is not None else 0))
         return out
+
+
+# ------------------------------------------------------- fused bottleneck block
+
+_DTYPE_CODES = {"f32": F32, "fp32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16, "i8": I8, "int8": I8}
+
+
+def bottleneck_desc(n, c, h, w, mid, k, dtype="bf16") -> BottleneckDesc:
+    return BottleneckDesc(n, c, h, w, mid, k, _DTYPE_CODES[dtype] if isinstance(dtype, str) else dtype)
+
+
+def bottleneck_check(desc: BottleneckDesc) -> None:
+    """Raise CfwdError (UNSUPPORTED with the reason) unless the fused kernel runs this block."""
+    _check(_lib().cfwd_bottleneck_check(ctypes.byref(desc)))
+
+
+def bottleneck_filter_size(desc: BottleneckDesc) -> int:
+    b = ctypes.c_size_t()
+    _check(_lib().cfwd_bottleneck_filter_size(ctypes.byref(desc), ctypes.byref(b)))
+    return b.value
+
+
+def bottleneck_desc_for(x, w1, w3) -> BottleneckDesc:
+    n, c, h, wd = x.shape
+    return bottleneck_desc(n, c, h, wd, w1.shape[0], w3.shape[0], _dtype_of(x))
+
+
+def bottleneck_prepare(w2, desc: BottleneckDesc):
+    """Prepared 3x3 weights of the block (uint8 device tensor)."""
+    torch = _torch()
+    _check_dev(w2)
+    nbytes = bottleneck_filter_size(desc)
+    wp = torch.empty(nbytes, dtype=torch.uint8, device=w2.device)
+    _check(_lib().cfwd_bottleneck_prepare(ctypes.byref(desc), w2.data_ptr(), wp.data_ptr(), nbytes, _stream()))
+    return wp
+
+
+def bottleneck_fwd_raw(desc: BottleneckDesc, x: int, w1: int, w2p: int, w3: int, ep, y: int, stream) -> int:
+    """cfwd_bottleneck_fwd with integer device pointers; returns the status."""
+    return _lib().cfwd_bottleneck_fwd(ctypes.byref(desc), x, w1, w2p, w3, ctypes.byref(ep) if ep is not None else None,
+                                      y, stream)
+
+
+def bottleneck_fwd(x, w1, w2_prepared, w3, b1=None, b2=None, b3=None, residual=None, relu=(False, False, False),
+                   out=None):
+    """y = the fused bottleneck block of NCHW ``x`` on the current stream (see cfwd.h)."""
+    torch = _torch()
+    _check_dev(x, w1, w2_prepared, w3, b1, b2, b3, residual, out)
+    desc = bottleneck_desc_for(x, w1, w3)
+    if out is None:
+        out = torch.empty((desc.n, desc.k, desc.h, desc.w), dtype=x.dtype, device=x.device)
+    ptr = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+    ep = BottleneckEpilogue(ptr(b1), ptr(b2), ptr(b3), ptr(residual), int(bool(relu[0])), int(bool(relu[1])),
+                            int(bool(relu[2])))
+    _check(bottleneck_fwd_raw(desc, x.data_ptr(), w1.data_ptr(), w2_prepared.data_ptr(), w3.data_ptr(), ep,
+                              out.data_ptr(), _stream()))
+    return out

@@ -26,6 +26,7 @@
 
 #include "internal.h"
 #include "winograd_i8.h"
+#include "bottleneck.h"
 
 #define CFWD_VERSION "0.1.0"
 
@@ -940,6 +941,62 @@ cfwd_status cfwd_fastrun_load(const char* path) {
 // given n candidates in Fast-Run order with reps timings each (row-major) and
 // a pass/fail flag per candidate, writes the index that would be chosen (or
 // -1) to *chosen.
+cfwd_status cfwd_bottleneck_check(const cfwd_bottleneck_desc* desc) {
+    std::string why;
+    const cfwd_status s = bottleneck_check(desc, &why);
+    return s == CFWD_OK ? s : set_error(s, why);
+}
+
+cfwd_status cfwd_bottleneck_filter_size(const cfwd_bottleneck_desc* desc, size_t* bytes) {
+    cfwd_status s = cfwd_bottleneck_check(desc);
+    if (s != CFWD_OK) return s;
+    if (!bytes) return set_error(CFWD_ERR_INVALID_ARG, "bytes must not be NULL");
+    *bytes = bottleneck_filter_bytes();
+    return CFWD_OK;
+}
+
+cfwd_status cfwd_bottleneck_prepare(const cfwd_bottleneck_desc* desc, const void* w2, void* w2_prepared, size_t bytes,
+                                    void* stream) {
+    cfwd_status s = cfwd_bottleneck_check(desc);
+    if (s != CFWD_OK) return s;
+    if (!w2 || !w2_prepared) return set_error(CFWD_ERR_INVALID_ARG, "w2 and w2_prepared must not be NULL");
+    if (!aligned16(w2_prepared)) return set_error(CFWD_ERR_INVALID_ARG, "w2_prepared must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(w2) & 1u) != 0) return set_error(CFWD_ERR_INVALID_ARG, "w2 must be 2-byte aligned");
+    if (bytes < bottleneck_filter_bytes())
+        return set_error(CFWD_ERR_WORKSPACE,
+                         "prepared 3x3 weights need " + std::to_string(bottleneck_filter_bytes()) + " bytes");
+    return bottleneck_prepare(w2, w2_prepared, static_cast<hipStream_t>(stream));
+}
+
+cfwd_status cfwd_bottleneck_fwd(const cfwd_bottleneck_desc* desc, const void* x, const void* w1,
+                                const void* w2_prepared, const void* w3, const cfwd_bottleneck_epilogue* epilogue,
+                                void* y, void* stream) {
+    cfwd_status s = cfwd_bottleneck_check(desc);
+    if (s != CFWD_OK) return s;
+    if (!x || !w1 || !w2_prepared || !w3 || !y) return set_error(CFWD_ERR_INVALID_ARG, "NULL buffer");
+    if (!aligned16(x) || !aligned16(w1) || !aligned16(w2_prepared) || !aligned16(w3) || !aligned16(y))
+        return set_error(CFWD_ERR_INVALID_ARG, "device pointers must be 16-byte aligned");
+    const size_t xb = static_cast<size_t>(desc->n) * desc->c * desc->h * desc->w * 2;
+    const size_t yb = static_cast<size_t>(desc->n) * desc->k * desc->h * desc->w * 2;
+    auto overlaps = [](const void* p, size_t pb, const void* q, size_t qb) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+        return a < b + qb && b < a + pb;
+    };
+    if (overlaps(x, xb, y, yb)) return set_error(CFWD_ERR_INVALID_ARG, "y must not overlap x");
+    if (epilogue) {
+        for (const void* bptr : {epilogue->b1, epilogue->b2, epilogue->b3})
+            if (bptr && (reinterpret_cast<uintptr_t>(bptr) & 3u) != 0)
+                return set_error(CFWD_ERR_INVALID_ARG, "biases must be 4-byte aligned");
+        if (epilogue->residual) {
+            if (!aligned16(epilogue->residual))
+                return set_error(CFWD_ERR_INVALID_ARG, "residual must be 16-byte aligned");
+            if (overlaps(epilogue->residual, yb, y, yb))
+                return set_error(CFWD_ERR_INVALID_ARG, "residual must not overlap y");
+        }
+    }
+    return bottleneck_launch(desc, x, w1, w2_prepared, w3, epilogue, y, static_cast<hipStream_t>(stream));
+}
+
 cfwd_status cfwd_fastrun_allow_inexact_int8(int allow) {
     g_allow_inexact_i8.store(allow ? 1 : 0);
     return CFWD_OK;

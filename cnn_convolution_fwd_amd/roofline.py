@@ -69,6 +69,27 @@ def layer_algo_flops(L, n, algo_name: str) -> int:
     return layer_flops(L, n)
 
 
+def block_flops(n, c, h, w, mid, k) -> int:
+    """Direct FLOPs of a bottleneck block: 1x1 c->mid, 3x3 pad 1 mid->mid, 1x1 mid->k."""
+    px = n * h * w
+    return 2 * px * (c * mid + mid * mid * 9 + mid * k)
+
+
+def block_algo_flops(n, c, h, w, mid, k, rows_per_tile=4) -> int:
+    """FLOPs the fused block kernel performs: the first 1x1 also runs on the
+    two halo rows of every band of ``rows_per_tile`` output rows (Momenta
+    talk, section "Operator的粒度": the tiles' overlap is recomputed)."""
+    bands = -(-h // rows_per_tile)
+    rows1 = bands * (rows_per_tile + 2)
+    return 2 * n * w * (rows1 * c * mid + h * (mid * mid * 9 + mid * k))
+
+
+def block_bytes(n, c, h, w, mid, k, esize) -> int:
+    """Algorithmic bytes of the fused block: x read once, y written once, the
+    three weight tensors once (no intermediate tensor)."""
+    return esize * (n * c * h * w + n * k * h * w + mid * c + mid * mid * 9 + k * mid)
+
+
 def gemm_flops_bytes(m, n, k, esize=4):
     """C = A(m x k) B(k x n): 2mnk FLOPs; A, B and C each moved once."""
     return 2 * m * n * k, esize * (m * k + k * n + m * n)

@@ -207,6 +207,37 @@ def float_problem(config: int, layer_idx: int = 0, n: Optional[int] = None,
     return FloatProblem(L, n, dtype, x, w)
 
 
+@dataclass
+class BlockProblem:
+    """Inputs of a bottleneck block: x [N, C, H, W], w1 [M, C, 1, 1], w2 [M, M, 3, 3], w3 [K, M, 1, 1]."""
+    n: int
+    x: np.ndarray
+    w1: np.ndarray
+    w2: np.ndarray
+    w3: np.ndarray
+
+
+def bottleneck_block_problem(n: Optional[int] = None, dtype: str = "bf16") -> BlockProblem:
+    """The 56x56 bottleneck (1x1 256->64, 3x3 64->64, 1x1 64->256) as one block:
+    x and each weight drawn exactly as its layer's standalone problem."""
+    ps = [float_problem(4, i, n=n, dtype=dtype) for i in range(3)]
+    return BlockProblem(ps[0].n, ps[0].x, ps[0].w, ps[1].w, ps[2].w)
+
+
+def random_block_problem(n: int, c: int, h: int, w: int, mid: int, k: int, seed: int,
+                         dtype: str = "bf16") -> BlockProblem:
+    """Ad-hoc block shapes: x ~ N(0, 1), each weight ~ N(0, 2 / fan_in) (bf16-exact for bf16)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, c, h, w))
+    w1 = rng.standard_normal((mid, c, 1, 1)) * np.sqrt(2.0 / c)
+    w2 = rng.standard_normal((mid, mid, 3, 3)) * np.sqrt(2.0 / (mid * 9))
+    w3 = rng.standard_normal((k, mid, 1, 1)) * np.sqrt(2.0 / mid)
+    x, w1 = _finish_float(x, w1, dtype)
+    _, w2 = _finish_float(x, w2, dtype)
+    _, w3 = _finish_float(x, w3, dtype)
+    return BlockProblem(n, x, w1, w2, w3)
+
+
 def random_float_problem(layer: Layer, n: int, dtype: str, seed: int) -> FloatProblem:
     """Uniform[-1,1] input, Uniform[-1,1]/sqrt(fan_in) weights for ad-hoc shapes."""
     rng = np.random.default_rng(seed)

@@ -280,6 +280,58 @@ cfwd_status cfwd_fastrun_allow_inexact_int8(int allow);
 cfwd_status cfwd_fastrun_choose(const cfwd_algo *cands, const float *times, int n, int reps,
                                 const int *gate_ok, int *chosen);
 
+/* ---- Fused bottleneck block.
+ * The ResNet bottleneck (Momenta talk "Paper Reading | 讓深度學習更高效運行的兩個
+ * 視角", section "優化1：Bottleneck") as one operation, with the spatial tiling
+ * of its section "Operator的粒度": each workgroup computes a band of output
+ * rows and keeps the two 64-channel intermediates on chip, so x is read and y
+ * written once, with no intermediate tensor in memory.
+ *   t1 = act1(conv1x1(x, w1) + b1)            C -> mid
+ *   t2 = act2(conv3x3(t1, w2, pad 1) + b2)    mid -> mid
+ *   y  = act3(conv1x1(t2, w3) + b3 + residual) mid -> K
+ * all stride 1, cross-correlation as above, act = ReLU where asked.
+ * t1 and t2 are rounded to bf16 (what three separate bf16 layers store);
+ * each stage accumulates in fp32 and applies its epilogue in fp32 before its
+ * single rounding.  Supported: bf16, NCHW, mid = 64, C and K multiples of
+ * 32, W a multiple of 8 and at most 64, any N and H. */
+typedef struct {
+    int n, c, h, w; /* x: [N][C][H][W] */
+    int mid;        /* channels of the two inner convolutions */
+    int k;          /* channels of y: [N][K][H][W] */
+    cfwd_dtype dtype;
+} cfwd_bottleneck_desc;
+
+/* Per-stage epilogue: fp32 biases b1 [mid], b2 [mid], b3 [K] (NULL = none,
+ * 4-byte aligned); residual: bf16 of y's shape added before act3 (NULL =
+ * none, 16-byte aligned, must not overlap y); relu1..3 nonzero = ReLU. */
+typedef struct {
+    const void *b1, *b2, *b3;
+    const void *residual;
+    int relu1, relu2, relu3;
+} cfwd_bottleneck_epilogue;
+
+/* CFWD_OK when the fused kernel runs this block, UNSUPPORTED (reason in
+ * cfwd_last_error) when not, INVALID_ARG for a NULL descriptor. */
+cfwd_status cfwd_bottleneck_check(const cfwd_bottleneck_desc *desc);
+
+/* Bytes of the prepared 3x3 weights (9 x mid x mid bf16, tap-major). */
+cfwd_status cfwd_bottleneck_filter_size(const cfwd_bottleneck_desc *desc, size_t *bytes);
+
+/* Prepare w2 (KCRS [mid][mid][3][3], bf16, device) into w2_prepared
+ * (>= cfwd_bottleneck_filter_size bytes, 16-byte aligned).  Enqueued on
+ * `stream`. */
+cfwd_status cfwd_bottleneck_prepare(const cfwd_bottleneck_desc *desc, const void *w2, void *w2_prepared,
+                                    size_t bytes, void *stream);
+
+/* y = the block of x.  w1 KCRS [mid][C][1][1], w3 KCRS [K][mid][1][1] (bf16,
+ * device, as given), w2_prepared from cfwd_bottleneck_prepare; epilogue may
+ * be NULL (no bias, no residual, no ReLU).  x, w1, w2_prepared, w3, y
+ * 16-byte aligned; y must not overlap x or the residual.  Allocates
+ * nothing; enqueued on `stream`. */
+cfwd_status cfwd_bottleneck_fwd(const cfwd_bottleneck_desc *desc, const void *x, const void *w1,
+                                const void *w2_prepared, const void *w3,
+                                const cfwd_bottleneck_epilogue *epilogue, void *y, void *stream);
+
 /* Static description of a status code. */
 const char *cfwd_status_string(cfwd_status status);
 

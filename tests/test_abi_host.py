@@ -185,3 +185,31 @@ def test_fastrun_map_file_handling(tmp_path):
     # without a GPU there is no device to key the map by: lookups miss
     desc = B.make_desc(1, 8, 8, 8, 8, 3, 3, 1, 1, dtype="f32")
     assert B.fastrun_lookup(desc) is None
+
+
+def test_bottleneck_block_checks_on_the_host():
+    ok = B.bottleneck_desc(32, 256, 56, 56, 64, 256)
+    B.bottleneck_check(ok)
+    assert B.bottleneck_filter_size(ok) == 9 * 64 * 64 * 2
+    for bad in (B.bottleneck_desc(32, 256, 56, 56, 64, 256, "f32"),   # dtype
+                B.bottleneck_desc(32, 256, 56, 56, 128, 256),         # inner channels
+                B.bottleneck_desc(32, 250, 56, 56, 64, 256),          # C % 32
+                B.bottleneck_desc(32, 256, 56, 56, 64, 250),          # K % 32
+                B.bottleneck_desc(32, 256, 56, 60, 64, 256),          # W % 8
+                B.bottleneck_desc(32, 256, 56, 72, 64, 256)):         # W > 64
+        with pytest.raises(B.CfwdError) as e:
+            B.bottleneck_check(bad)
+        assert e.value.status == B.ERR_UNSUPPORTED
+    with pytest.raises(B.CfwdError) as e:
+        B.bottleneck_check(B.bottleneck_desc(0, 256, 56, 56, 64, 256))
+    assert e.value.status == B.ERR_UNSUPPORTED
+    # argument validation happens before anything is enqueued
+    d = B.bottleneck_desc(1, 32, 8, 8, 64, 32)
+    ep = B.BottleneckEpilogue()
+    assert B.bottleneck_fwd_raw(d, 0, 16, 16, 16, ep, 4096, None) == B.ERR_INVALID_ARG       # NULL x
+    assert B.bottleneck_fwd_raw(d, 8, 16, 16, 16, ep, 1 << 20, None) == B.ERR_INVALID_ARG   # misaligned x
+    assert B.bottleneck_fwd_raw(d, 4096, 16, 16, 16, ep, 4096 + 512, None) == B.ERR_INVALID_ARG  # y overlaps x
+    ep_bad = B.BottleneckEpilogue(2, None, None, None, 0, 0, 0)
+    assert B.bottleneck_fwd_raw(d, 4096, 16, 16, 16, ep_bad, 1 << 20, None) == B.ERR_INVALID_ARG  # bias alignment
+    ep_res = B.BottleneckEpilogue(None, None, None, (1 << 20) + 256, 0, 0, 0)
+    assert B.bottleneck_fwd_raw(d, 4096, 16, 16, 16, ep_res, 1 << 20, None) == B.ERR_INVALID_ARG  # residual overlaps y
