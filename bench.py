@@ -95,6 +95,8 @@ def parse():
     ap.add_argument("--fastrun-load", default="", help="Fast-Run map file to load before set-up (its problems are not "
                     "searched again)")
     ap.add_argument("--fastrun-save", default="", help="write the Fast-Run map to this file after set-up")
+    ap.add_argument("--layout", default="", choices=["", "nhwc"],
+                    help="float workloads: run the layers on NHWC activations (the NHWC implicit GEMM)")
     ap.add_argument("--block", default="layers", choices=["layers", "fused"],
                     help="bottleneck workload: its three layers one by one, or the fused block kernel")
     ap.add_argument("--allow-inexact-int8", action="store_true",
@@ -178,7 +180,7 @@ def main():
     from cnn_convolution_fwd_amd import telemetry
     from cnn_convolution_fwd_amd.roofline import (PEAK, block_algo_flops, block_bytes, block_flops, bound,
                                                    layer_algo_flops, layer_bytes, layer_flops)
-    from cnn_convolution_fwd_amd.workloads import (CONFIGS, bf16_bits, epilogue_inputs, float_problem, int8_problem,
+    from cnn_convolution_fwd_amd.workloads import (CONFIGS, bf16_bits, epilogue_inputs, float_problem, int8_problem, to_nhwc,
                                                     pack_nchwx)
 
     base = ALIASES.get(a.workload, a.workload)
@@ -209,6 +211,13 @@ def main():
     dev = torch.device("cuda:0")
     int8 = dtype == "i8"
     layout = "NCHWX" if int8 else "NCHW"
+    if a.layout == "nhwc":
+        if int8 or a.block == "fused":
+            print("--layout nhwc runs float layers (fp32 / bf16) one by one", file=sys.stderr)
+            sys.exit(2)
+        layout = "NHWC"
+        workload += "_nhwc"
+    act = to_nhwc if layout == "NHWC" else (lambda v: v)
 
     def to_dev(arr):
         if dtype == "bf16":
@@ -258,7 +267,7 @@ def main():
             scale = torch.from_numpy(pr.scale).to(dev)
         else:
             pr = float_problem(cfg_idx, li, n=N, dtype=dtype)
-            x0 = to_dev(pr.x)
+            x0 = to_dev(act(pr.x))
             scale = None
         w = to_dev(pr.w)
         # epilogue of this layer: bias, ReLU (not on downsample shortcuts), and
@@ -271,7 +280,7 @@ def main():
             bias = torch.from_numpy(epi.bias).to(dev)
             relu = "down" not in L.name
             if (cfg_idx, li) in RESIDUAL_LAYERS:
-                res0 = to_dev(pack_nchwx(epi.residual, cfg.x_block) if int8 else epi.residual)
+                res0 = to_dev(pack_nchwx(epi.residual, cfg.x_block) if int8 else act(epi.residual))
         fused = a.epilogue == "fused"
         plan = B.LayerPlan(x0, w, L.stride, L.pad, L.dil, L.groups, layout, channels=L.c, requant_scale=scale,
                            algo_spec=a.algo, bias=bias if fused else None, relu=relu and fused)
@@ -312,7 +321,7 @@ def main():
         if st != 0:
             raise RuntimeError(B.library().cfwd_last_error().decode())
         if a.epilogue == "unfused":  # the same epilogue as elementwise passes over y
-            y.add_(l["bias"].view(1, -1, 1, 1).to(y.dtype))
+            y.add_(l["bias"].view((1, 1, 1, -1) if layout == "NHWC" else (1, -1, 1, 1)).to(y.dtype))
             if res is not None:
                 y.add_(res)
             if l["relu"]:

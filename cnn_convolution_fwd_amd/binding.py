@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(HERE, "libcfwd.so")
 
 # enums (mirror include/cfwd.h)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_NO_CANDIDATE, ERR_HIP, ERR_CACHE_IO = range(7)
-LAYOUT_NCHW, LAYOUT_NCHWX = 0, 1
+LAYOUT_NCHW, LAYOUT_NCHWX, LAYOUT_NHWC = 0, 1, 2
+_LAYOUTS = {"NCHW": LAYOUT_NCHW, "NCHWX": LAYOUT_NCHWX, "NHWC": LAYOUT_NHWC}
 F32, BF16, I8 = 0, 1, 2
 ALGO_AUTO, ALGO_IMPLICIT_GEMM, ALGO_WINOGRAD_F2X2_3X3, ALGO_WINOGRAD_F6X6_3X3, ALGO_DIRECT, ALGO_POINTWISE = range(6)
 
@@ -32,6 +33,7 @@ EXPORTED = [
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
     "cfwd_conv2d_fwd_noalloc", "cfwd_conv2d_fwd_ex", "cfwd_fastrun_allow_inexact_int8",
     "cfwd_bottleneck_check", "cfwd_bottleneck_filter_size", "cfwd_bottleneck_prepare", "cfwd_bottleneck_fwd",
+    "cfwd_convert_layout",
 ]
 ACT_NONE, ACT_RELU = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CFWD_NOALLOC_SCRATCH_BYTES
@@ -113,6 +115,8 @@ def _lib():
             "cfwd_fastrun_clear": [],
             "cfwd_fastrun_allow_inexact_int8": [ctypes.c_int],
             "cfwd_bottleneck_check": [P(BottleneckDesc)],
+            "cfwd_convert_layout": [ctypes.c_int] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int,
+                                                         ctypes.c_int, vp, vp],
             "cfwd_bottleneck_filter_size": [P(BottleneckDesc), P(sz)],
             "cfwd_bottleneck_prepare": [P(BottleneckDesc), vp, vp, sz, vp],
             "cfwd_bottleneck_fwd": [P(BottleneckDesc), vp, vp, vp, vp, P(BottleneckEpilogue), vp, vp],
@@ -150,7 +154,7 @@ def make_desc(n, c, h, w, k, r, s, stride=1, padding=0, dilation=1, groups=1, la
     sh, sw = _pair(stride)
     ph, pw = _pair(padding)
     dh, dw = _pair(dilation)
-    lay = LAYOUT_NCHW if layout.upper() == "NCHW" else LAYOUT_NCHWX
+    lay = _LAYOUTS[layout.upper()]
     dt = {"f32": F32, "fp32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16, "i8": I8, "int8": I8}[dtype]
     return ConvDesc(n, c, h, w, k, r, s, sh, sw, ph, pw, dh, dw, groups, lay, int(x_block or 0), dt)
 
@@ -300,11 +304,16 @@ def _dtype_of(t) -> str:
 
 
 def desc_for(x, w, stride=1, padding=0, dilation=1, groups=1, layout="NCHW", channels=None) -> ConvDesc:
-    """Descriptor for activations ``x`` (NCHW [N,C,H,W] or NCHWX [N,CB,H,W,X]) and KCRS ``w``."""
+    """Descriptor for activations ``x`` (NCHW [N,C,H,W], NHWC [N,H,W,C] or NCHWX [N,CB,H,W,X]) and KCRS ``w``."""
     if layout.upper() == "NCHW":
         if x.dim() != 4:
             raise ValueError("NCHW activations must be 4-D")
         n, c, h, wd = x.shape
+        xb = 0
+    elif layout.upper() == "NHWC":
+        if x.dim() != 4:
+            raise ValueError("NHWC activations must be 4-D")
+        n, h, wd, c = x.shape
         xb = 0
     else:
         if x.dim() != 5:
@@ -323,6 +332,8 @@ def _out_shape(desc: ConvDesc):
     oh, ow = output_dims(desc)
     if desc.layout == LAYOUT_NCHW:
         return (desc.n, desc.k, oh, ow)
+    if desc.layout == LAYOUT_NHWC:
+        return (desc.n, oh, ow, desc.k)
     return (desc.n, -(-desc.k // desc.x), oh, ow, desc.x)
 
 
@@ -537,4 +548,28 @@ def bottleneck_fwd(x, w1, w2_prepared, w3, b1=None, b2=None, b3=None, residual=N
                             int(bool(relu[2])))
     _check(bottleneck_fwd_raw(desc, x.data_ptr(), w1.data_ptr(), w2_prepared.data_ptr(), w3.data_ptr(), ep,
                               out.data_ptr(), _stream()))
+    return out
+
+
+# ------------------------------------------------------- layout conversion
+
+def convert_layout(t, src_layout: str, dst_layout: str, dst_x: int = 0, channels: Optional[int] = None, out=None):
+    """Copy activations between NCHW [N,C,H,W], NHWC [N,H,W,C] and NCHWX [N,CB,H,W,X] (cfwd_convert_layout)."""
+    torch = _torch()
+    _check_dev(t, out)
+    sl, dl = src_layout.upper(), dst_layout.upper()
+    if sl == "NCHW":
+        n, c, h, w = t.shape
+        sx = 0
+    elif sl == "NHWC":
+        n, h, w, c = t.shape
+        sx = 0
+    else:
+        n, cb, h, w, sx = t.shape
+        c = channels if channels is not None else cb * sx
+    shape = {"NCHW": (n, c, h, w), "NHWC": (n, h, w, c)}.get(dl) or (n, -(-c // dst_x), h, w, dst_x)
+    if out is None:
+        out = torch.empty(shape, dtype=t.dtype, device=t.device)
+    _check(_lib().cfwd_convert_layout(n, c, h, w, _DTYPE_CODES[_dtype_of(t)], _LAYOUTS[sl], sx, t.data_ptr(),
+                                      _LAYOUTS[dl], int(dst_x), out.data_ptr(), _stream()))
     return out

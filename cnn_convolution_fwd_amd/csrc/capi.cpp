@@ -27,6 +27,7 @@
 #include "internal.h"
 #include "winograd_i8.h"
 #include "bottleneck.h"
+#include "nhwc.h"
 
 #define CFWD_VERSION "0.1.0"
 
@@ -92,8 +93,8 @@ cfwd_status make_prob(const cfwd_conv_desc* d, Prob* p, std::string* why) {
         return CFWD_ERR_INVALID_ARG;
     }
     int xb;
-    if (d->layout == CFWD_LAYOUT_NCHW) {
-        xb = 1;
+    if (d->layout == CFWD_LAYOUT_NCHW || d->layout == CFWD_LAYOUT_NHWC) {
+        xb = 1;  // element counts as NCHW; only the NHWC configs accept NHWC (supported())
     } else if (d->layout == CFWD_LAYOUT_NCHWX) {
         if (d->x != 4 && d->x != 8) {
             *why = "NCHWX block x must be 4 or 8";
@@ -146,9 +147,14 @@ int family_rank(cfwd_algo_kind k) {
     }
 }
 
+// Implicit GEMM configs 0 .. igemm_num_configs() - 1 are the NCHW / NCHWX
+// kernels; the next nhwc_num_configs() the NHWC kernel (k_nhwc.hip).
+int nhwc_first() { return igemm_num_configs(); }
+bool is_nhwc_cfg(cfwd_algo_kind k, int cfg) { return k == CFWD_ALGO_IMPLICIT_GEMM && cfg >= nhwc_first(); }
+
 int num_configs(cfwd_algo_kind k) {
     switch (k) {
-        case CFWD_ALGO_IMPLICIT_GEMM: return igemm_num_configs();
+        case CFWD_ALGO_IMPLICIT_GEMM: return igemm_num_configs() + nhwc_num_configs();
         case CFWD_ALGO_POINTWISE: return pointwise_num_configs();
         case CFWD_ALGO_DIRECT: return direct_num_configs();
         case CFWD_ALGO_WINOGRAD_F2X2_3X3: return winograd_num_configs(2);
@@ -162,6 +168,12 @@ bool supported(const Prob& p, cfwd_algo_kind k, int cfg, std::string* why) {
         if (why) *why = "no such config for this algorithm";
         return false;
     }
+    // NHWC problems run only on the NHWC configs, and those only on NHWC
+    if (p.layout == CFWD_LAYOUT_NHWC && !is_nhwc_cfg(k, cfg)) {
+        if (why) *why = "NHWC activations run on the NHWC implicit GEMM configs only";
+        return false;
+    }
+    if (is_nhwc_cfg(k, cfg)) return nhwc_supported(p, cfg - nhwc_first(), why);
     switch (k) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_supported(p, cfg, why);
         case CFWD_ALGO_POINTWISE: return pointwise_supported(p, cfg, why);
@@ -199,6 +211,7 @@ std::vector<cfwd_algo> candidates(const Prob& p) {
 }
 
 size_t filter_bytes(const Prob& p, const cfwd_algo& a) {
+    if (is_nhwc_cfg(a.kind, a.config_id)) return nhwc_filter_bytes(p, a.config_id - nhwc_first());
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_filter_bytes(p, a.config_id);
         case CFWD_ALGO_POINTWISE: return pointwise_filter_bytes(p, a.config_id);
@@ -212,6 +225,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Device scratch an algorithm needs besides its prepared filter.
 size_t scratch_bytes(const Prob& p, const cfwd_algo& a) {
+    if (is_nhwc_cfg(a.kind, a.config_id)) return 0;
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_scratch_bytes(p, a.config_id);
         case CFWD_ALGO_WINOGRAD_F2X2_3X3: return winograd_scratch_bytes(p, 2, a.config_id);
@@ -307,6 +321,9 @@ bool map_lookup(const Prob& p, cfwd_algo* out) {
 }
 
 cfwd_algo heuristic(const Prob& p) {
+    if (p.layout == CFWD_LAYOUT_NHWC)
+        for (int c = 0; c < nhwc_num_configs(); ++c)
+            if (nhwc_supported(p, c, nullptr)) return cfwd_algo{CFWD_ALGO_IMPLICIT_GEMM, nhwc_first() + c, 0.0f};
     // Stands in for the article's hand-written preference table (its figure is
     // not preserved): depthwise -> direct, 1x1 -> pointwise, else implicit GEMM.
     if (p.depthwise()) return cfwd_algo{CFWD_ALGO_DIRECT, direct_default_config(p), 0.0f};
@@ -321,6 +338,14 @@ cfwd_algo heuristic(const Prob& p) {
 // Default config of a family (config_id -1): the first supported one, except
 // implicit GEMM, which uses its own preference.
 bool family_default(const Prob& p, cfwd_algo_kind k, int* cfg) {
+    if (p.layout == CFWD_LAYOUT_NHWC) {
+        for (int c = 0; c < num_configs(k); ++c)
+            if (supported(p, k, c, nullptr)) {
+                *cfg = c;
+                return true;
+            }
+        return false;
+    }
     if (k == CFWD_ALGO_IMPLICIT_GEMM) {
         *cfg = igemm_default_config(p);
         return *cfg >= 0;
@@ -341,6 +366,10 @@ cfwd_status resolve(const Prob& p, cfwd_algo in, cfwd_algo* out) {
     if (in.kind == CFWD_ALGO_AUTO) {
         if (map_lookup(p, out)) return CFWD_OK;
         *out = heuristic(p);
+        std::string why;
+        // NHWC problems outside the NHWC kernel's scope have no algorithm
+        if (p.layout == CFWD_LAYOUT_NHWC && !supported(p, out->kind, out->config_id, &why))
+            return set_error(CFWD_ERR_UNSUPPORTED, why);
         return CFWD_OK;
     }
     if (family_rank(in.kind) > 4) return set_error(CFWD_ERR_INVALID_ARG, "unknown algorithm kind");
@@ -358,6 +387,7 @@ cfwd_status resolve(const Prob& p, cfwd_algo in, cfwd_algo* out) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
 cfwd_status prepare(const Prob& p, const cfwd_algo& a, const void* w, void* wp, hipStream_t st) {
+    if (is_nhwc_cfg(a.kind, a.config_id)) return nhwc_prepare(p, a.config_id - nhwc_first(), w, wp, st);
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_prepare(p, a.config_id, w, wp, st);
         case CFWD_ALGO_POINTWISE: return pointwise_prepare(p, a.config_id, w, wp, st);
@@ -370,6 +400,7 @@ cfwd_status prepare(const Prob& p, const cfwd_algo& a, const void* w, void* wp, 
 cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w, const void* wp,
                 const float* scale, void* y, void* scratch, const Epi& e, hipStream_t st) {
     cfwd_status s;
+    if (is_nhwc_cfg(a.kind, a.config_id)) return nhwc_launch(p, a.config_id - nhwc_first(), x, wp, y, e, st);
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, scratch, e, st); break;
         case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, e, st); break;
@@ -488,6 +519,7 @@ float gate_tolerance(const Prob& p, cfwd_algo_kind k) {
 
 struct FrLayout {
     size_t ref, den, xabs, wabs, stats, cand, evict, evict_bytes, total;
+    size_t xn, yn;  // NHWC problems: x and an output converted to NCHW for the reference
 };
 
 FrLayout fastrun_layout(const Prob& p, const std::vector<cfwd_algo>& cands) {
@@ -505,6 +537,11 @@ FrLayout fastrun_layout(const Prob& p, const std::vector<cfwd_algo>& cands) {
         L.den = off; off += ybytes;
         L.xabs = off; off += xbytes;
         L.wabs = off; off += wbytes;
+    }
+    L.xn = L.yn = 0;
+    if (p.layout == CFWD_LAYOUT_NHWC) {
+        L.xn = off; off += xbytes;
+        L.yn = off; off += ybytes;
     }
     L.stats = off; off += 256;
     L.cand = off; off += round_up(cand, 256);
@@ -712,17 +749,33 @@ cfwd_status cfwd_fastrun_select(const cfwd_conv_desc* desc, const void* x, const
 
     // Reference output: the generic direct kernel (exact integer arithmetic
     // for int8; fp32 accumulation for float).  For float dtypes the error
-    // normaliser den = conv(|x|, |w|) is computed the same way.
-    s = direct_launch(p, 0, x, w_kcrs, requant_scale, ref, Epi{}, st);
+    // normaliser den = conv(|x|, |w|) is computed the same way.  NHWC
+    // problems run it on x converted to NCHW and convert its outputs back.
+    const bool nhwc = p.layout == CFWD_LAYOUT_NHWC;
+    Prob pr = p;
+    pr.layout = CFWD_LAYOUT_NCHW;
+    const void* xr = x;
+    if (nhwc) {
+        s = layout_convert(p.n, p.c, p.h, p.w, p.esize, CFWD_LAYOUT_NHWC, 0, x, CFWD_LAYOUT_NCHW, 0, ws + L.xn, st);
+        if (s != CFWD_OK) return s;
+        xr = ws + L.xn;
+    }
+    auto to_layout = [&](void* out) -> cfwd_status {  // NHWC: out <- the NCHW result in yn
+        return layout_convert(p.n, p.k, p.oh, p.ow, p.esize, CFWD_LAYOUT_NCHW, 0, ws + L.yn, CFWD_LAYOUT_NHWC, 0, out,
+                              st);
+    };
+    s = direct_launch(pr, 0, xr, w_kcrs, requant_scale, nhwc ? ws + L.yn : ref, Epi{}, st);
+    if (s == CFWD_OK && nhwc) s = to_layout(ref);
     if (s != CFWD_OK) return s;
     s = zero_output_channel_padding(p, ref, st);
     if (s != CFWD_OK) return s;
     if (p.dtype != CFWD_I8) {
-        s = abs_copy(p, x, ws + L.xabs, p.x_img * p.n, st);
+        s = abs_copy(p, xr, ws + L.xabs, p.x_img * p.n, st);
         if (s != CFWD_OK) return s;
         s = abs_copy(p, w_kcrs, ws + L.wabs, static_cast<long long>(p.k) * p.cg * p.r * p.s, st);
         if (s != CFWD_OK) return s;
-        s = direct_launch(p, 0, ws + L.xabs, ws + L.wabs, nullptr, ws + L.den, Epi{}, st);
+        s = direct_launch(pr, 0, ws + L.xabs, ws + L.wabs, nullptr, nhwc ? ws + L.yn : ws + L.den, Epi{}, st);
+        if (s == CFWD_OK && nhwc) s = to_layout(ws + L.den);
         if (s != CFWD_OK) return s;
         // NCHWX channels past K: the direct kernel does not write them; den
         // there must be 0 like the candidate's and the reference's outputs
@@ -995,6 +1048,31 @@ cfwd_status cfwd_bottleneck_fwd(const cfwd_bottleneck_desc* desc, const void* x,
         }
     }
     return bottleneck_launch(desc, x, w1, w2_prepared, w3, epilogue, y, static_cast<hipStream_t>(stream));
+}
+
+cfwd_status cfwd_convert_layout(int n, int c, int h, int w, cfwd_dtype dtype, cfwd_layout src_layout, int src_x,
+                                const void* src, cfwd_layout dst_layout, int dst_x, void* dst, void* stream) {
+    if (n < 1 || c < 1 || h < 1 || w < 1) return set_error(CFWD_ERR_INVALID_ARG, "n, c, h, w must be >= 1");
+    int es;
+    if (!esize_of(dtype, &es)) return set_error(CFWD_ERR_INVALID_ARG, "unknown dtype");
+    auto lay_ok = [](cfwd_layout l, int xb) {
+        return l == CFWD_LAYOUT_NCHW || l == CFWD_LAYOUT_NHWC || (l == CFWD_LAYOUT_NCHWX && (xb == 4 || xb == 8));
+    };
+    if (!lay_ok(src_layout, src_x) || !lay_ok(dst_layout, dst_x))
+        return set_error(CFWD_ERR_INVALID_ARG, "layouts must be NCHW, NHWC or NCHWX with x = 4 or 8");
+    if (!src || !dst) return set_error(CFWD_ERR_INVALID_ARG, "src and dst must not be NULL");
+    if ((reinterpret_cast<uintptr_t>(src) % es) != 0 || (reinterpret_cast<uintptr_t>(dst) % es) != 0)
+        return set_error(CFWD_ERR_INVALID_ARG, "src and dst must be aligned to the element size");
+    auto bytes = [&](cfwd_layout l, int xb) {
+        const long long cp = (l == CFWD_LAYOUT_NCHWX) ? (c + xb - 1) / xb * xb : c;
+        return static_cast<size_t>(n) * cp * h * w * es;
+    };
+    const size_t sb = bytes(src_layout, src_x), db = bytes(dst_layout, dst_x);
+    if (sb / es / n >= (1ULL << 31) || db / es / n >= (1ULL << 31))
+        return set_error(CFWD_ERR_UNSUPPORTED, "each image must hold fewer than 2^31 elements");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+    if (a < b + db && b < a + sb) return set_error(CFWD_ERR_INVALID_ARG, "src and dst must not overlap");
+    return layout_convert(n, c, h, w, es, src_layout, src_x, src, dst_layout, dst_x, dst, static_cast<hipStream_t>(stream));
 }
 
 cfwd_status cfwd_fastrun_allow_inexact_int8(int allow) {

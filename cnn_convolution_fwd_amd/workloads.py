@@ -147,6 +147,15 @@ def unpack_nchwx(xp: np.ndarray, c: int) -> np.ndarray:
     full = xp.transpose(0, 1, 4, 2, 3).reshape(N, CB * xb, H, W)
     return np.ascontiguousarray(full[:, :c])
 
+def to_nhwc(x: np.ndarray) -> np.ndarray:
+    """[N, C, H, W] -> [N, H, W, C]: element (n, c, h, w) goes to [n][h][w][c]."""
+    return np.ascontiguousarray(x.transpose(0, 2, 3, 1))
+
+
+def from_nhwc(x: np.ndarray) -> np.ndarray:
+    """[N, H, W, C] -> [N, C, H, W]."""
+    return np.ascontiguousarray(x.transpose(0, 3, 1, 2))
+
 # --------------------------------------------------------------- generators
 
 

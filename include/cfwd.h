@@ -15,7 +15,11 @@
  * "Winograd" and "Fast-Run"; Momenta talk "Paper Reading | 讓深度學習更高效運行
  * 的兩個視角", section "優化2：Depthwise卷積" for the depthwise / 1x1 layers):
  *   IMPLICIT_GEMM   im2col x matmul without materialising im2col: input patches
- *                   are staged in LDS and multiplied on the matrix cores.
+ *                   are staged in LDS and multiplied on the matrix cores.  Its
+ *                   last config(s) are the NHWC kernel, the only ones that take
+ *                   NHWC problems (and they take nothing else): both operands
+ *                   are staged by plain 16-byte copies, the channels of a
+ *                   pixel being contiguous.
  *   WINOGRAD_F2X2_3X3 / WINOGRAD_F6X6_3X3
  *                   F(m x m, 3 x 3) minimal filtering for 3x3, stride 1,
  *                   dilation 1, groups 1; float dtypes, and int8 for
@@ -53,6 +57,9 @@
  *                   NCHWX [N][ceil(C/x)][H][W][x], x = 4 or 8 (MegEngine
  *                   inference article, section "NCHWX"); channels past C are
  *                   ignored on input.
+ *                   NHWC  [N][H][W][C] (channels contiguous; fp32 / bf16, groups
+ *                   1, C a multiple of 4 (fp32) or 8 (bf16); runs on the NHWC
+ *                   implicit GEMM configs, see IMPLICIT_GEMM).
  *   w  weights      KCRS  [K][C/G][R][S] in every layout, activation dtype.
  *   y  output       same layout and dtype as x, with K channels; in NCHWX the
  *                   channels past K are written as 0.
@@ -89,7 +96,7 @@ typedef enum {
     CFWD_ERR_CACHE_IO = 6      /* Fast-Run map file could not be written    */
 } cfwd_status;
 
-typedef enum { CFWD_LAYOUT_NCHW = 0, CFWD_LAYOUT_NCHWX = 1 } cfwd_layout;
+typedef enum { CFWD_LAYOUT_NCHW = 0, CFWD_LAYOUT_NCHWX = 1, CFWD_LAYOUT_NHWC = 2 } cfwd_layout;
 
 typedef enum { CFWD_F32 = 0, CFWD_BF16 = 1, CFWD_I8 = 2 } cfwd_dtype;
 
@@ -239,7 +246,8 @@ cfwd_status cfwd_conv2d_fwd_noalloc(const cfwd_conv_desc *desc, cfwd_algo algo, 
  * Cache and L2 are flushed by overwriting a 512 MiB region of the workspace
  * unless x and y together already exceed that, so candidates are timed from
  * HBM), reject any whose output fails the accuracy gate against the generic
- * DIRECT kernel's result on the same data (bit-identical for int8, except
+ * DIRECT kernel's result on the same data (for NHWC, run on x converted to
+ * NCHW and converted back; bit-identical for int8, except
  * int8 Winograd F(2x2): no output more than 1 away;
  * normalised error <= 1e-5 fp32 except Winograd F(6x6), 1e-3 fp32 F(6x6),
  * 1e-2 bf16; NaN or infinity fails), keep the fastest (times within 1% count
@@ -263,6 +271,17 @@ cfwd_status cfwd_fastrun_lookup(const cfwd_conv_desc *desc, cfwd_algo *algo);
 cfwd_status cfwd_fastrun_load(const char *path);
 cfwd_status cfwd_fastrun_save(const char *path);
 cfwd_status cfwd_fastrun_clear(void);
+
+/* Copy an activation tensor of n x c x h x w elements of `dtype` from one
+ * layout to another (NCHW, NHWC, NCHWX with x = src_x / dst_x = 4 or 8; the
+ * x arguments are ignored for the others).  NCHWX destinations get their
+ * channels past c written as 0; NCHWX sources' are not read.  For networks
+ * whose layers prefer different layouts (MegEngine CPU-inference article,
+ * section "结论": a network-wide mixed choice of layouts).  src and dst
+ * (device, element-aligned) must not overlap.  Enqueued on `stream`. */
+cfwd_status cfwd_convert_layout(int n, int c, int h, int w, cfwd_dtype dtype, cfwd_layout src_layout,
+                                int src_x, const void *src, cfwd_layout dst_layout, int dst_x, void *dst,
+                                void *stream);
 
 /* Whether int8 candidates whose results are not always bit-identical to the
  * integer ones (int8 Winograd F(2x2), see WINOGRAD_F2X2_3X3 above) take part

@@ -213,3 +213,44 @@ def test_bottleneck_block_checks_on_the_host():
     assert B.bottleneck_fwd_raw(d, 4096, 16, 16, 16, ep_bad, 1 << 20, None) == B.ERR_INVALID_ARG  # bias alignment
     ep_res = B.BottleneckEpilogue(None, None, None, (1 << 20) + 256, 0, 0, 0)
     assert B.bottleneck_fwd_raw(d, 4096, 16, 16, 16, ep_res, 1 << 20, None) == B.ERR_INVALID_ARG  # residual overlaps y
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_nhwc_routes_to_its_own_configs(dtype):
+    desc = B.make_desc(32, 256, 56, 56, 256, 3, 3, 1, 1, 1, 1, "NHWC", None, dtype)
+    cands = B.list_candidates(desc)
+    assert len(cands) == 1 and cands[0].kind == B.ALGO_IMPLICIT_GEMM
+    nhwc_cfg = cands[0].config_id
+    assert B.resolve_algo(desc, B.algo()).key() == cands[0].key()
+    assert B.resolve_algo(desc, B.algo("implicit_gemm")).key() == cands[0].key()
+    # weights [K][R][S][C] (C already a whole chunk)
+    assert B.filter_size(desc, cands[0]) == 256 * 9 * 256 * (4 if dtype == "f32" else 2)
+    for kind in ("direct", "pointwise", "winograd_f2x2_3x3", "winograd_f6x6_3x3"):
+        with pytest.raises(B.CfwdError):
+            B.resolve_algo(desc, B.algo(kind))
+    with pytest.raises(B.CfwdError):
+        B.resolve_algo(desc, B.algo("implicit_gemm", 0))
+    # the NHWC config does not take NCHW problems
+    nchw = B.make_desc(32, 256, 56, 56, 256, 3, 3, 1, 1, 1, 1, "NCHW", None, dtype)
+    with pytest.raises(B.CfwdError):
+        B.resolve_algo(nchw, B.algo("implicit_gemm", nhwc_cfg))
+    # outside the NHWC kernel's scope there is no algorithm, AUTO included
+    for bad in (B.make_desc(1, 6, 8, 8, 8, 3, 3, 1, 1, 1, 1, "NHWC", None, dtype),       # C % 8 (bf16), C % 4 (fp32)
+                B.make_desc(1, 16, 8, 8, 16, 3, 3, 1, 1, 1, 2, "NHWC", None, dtype),     # groups
+                B.make_desc(1, 16, 8, 8, 16, 3, 3, 1, 1, 1, 1, "NHWC", None, "i8")):     # int8
+        assert B.list_candidates(bad) == []
+        with pytest.raises(B.CfwdError) as e:
+            B.resolve_algo(bad, B.algo())
+        assert e.value.status == B.ERR_UNSUPPORTED
+
+
+def test_convert_layout_validation_on_the_host():
+    lib = B.library()
+    args = (2, 8, 4, 4, B.BF16)
+    assert lib.cfwd_convert_layout(*args, 7, 0, 4096, B.LAYOUT_NHWC, 0, 1 << 20, None) == B.ERR_INVALID_ARG  # layout
+    assert lib.cfwd_convert_layout(*args, B.LAYOUT_NCHWX, 3, 4096, B.LAYOUT_NHWC, 0, 1 << 20, None) == B.ERR_INVALID_ARG
+    assert lib.cfwd_convert_layout(*args, B.LAYOUT_NCHW, 0, None, B.LAYOUT_NHWC, 0, 1 << 20, None) == B.ERR_INVALID_ARG
+    assert lib.cfwd_convert_layout(*args, B.LAYOUT_NCHW, 0, 4096, B.LAYOUT_NHWC, 0, 4096 + 64, None) == B.ERR_INVALID_ARG
+    assert lib.cfwd_convert_layout(*args, B.LAYOUT_NCHW, 0, 4097, B.LAYOUT_NHWC, 0, 1 << 20, None) == B.ERR_INVALID_ARG
+    assert lib.cfwd_convert_layout(0, 8, 4, 4, B.BF16, B.LAYOUT_NCHW, 0, 4096, B.LAYOUT_NHWC, 0, 1 << 20,
+                                   None) == B.ERR_INVALID_ARG

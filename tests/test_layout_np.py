@@ -7,8 +7,8 @@ lives at [n][c // X][h][w][c % X]; channels past C are zero.
 import numpy as np
 import pytest
 
-from cnn_convolution_fwd_amd.workloads import (bf16_bits, bf16_to_f32, pack_nchwx, round_to_bf16,
-                                                unpack_nchwx)
+from cnn_convolution_fwd_amd.workloads import (bf16_bits, bf16_to_f32, from_nhwc, pack_nchwx, round_to_bf16,
+                                                to_nhwc, unpack_nchwx)
 
 
 @pytest.mark.parametrize("C,xb", [(3, 4), (4, 4), (16, 4), (5, 8), (32, 8)])
@@ -34,3 +34,19 @@ def test_bf16_rounding_is_rne():
     bits = bf16_bits(np.array([1.0, -2.0], dtype=np.float32))
     assert bits.tolist() == [0x3F80, 0xC000]
     np.testing.assert_array_equal(bf16_to_f32(bits), [1.0, -2.0])
+
+
+def test_nhwc_index_formula_and_roundtrip():
+    """NHWC keeps a pixel's channels contiguous: (n, c, h, w) at [n][h][w][c],
+    flat offset ((n * H + h) * W + w) * C + c."""
+    rng = np.random.default_rng(7)
+    N, C, H, W = 2, 5, 3, 4
+    x = rng.standard_normal((N, C, H, W)).astype(np.float32)
+    t = to_nhwc(x)
+    flat = t.reshape(-1)
+    for n in range(N):
+        for c in range(C):
+            for h in range(H):
+                for w in range(W):
+                    assert flat[((n * H + h) * W + w) * C + c] == x[n, c, h, w]
+    np.testing.assert_array_equal(from_nhwc(t), x)
