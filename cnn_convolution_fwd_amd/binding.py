@@ -33,7 +33,7 @@ EXPORTED = [
     "cfwd_fastrun_clear", "cfwd_fastrun_choose", "cfwd_status_string", "cfwd_last_error", "cfwd_algo_name",
     "cfwd_conv2d_fwd_noalloc", "cfwd_conv2d_fwd_ex", "cfwd_fastrun_allow_inexact_int8",
     "cfwd_bottleneck_check", "cfwd_bottleneck_filter_size", "cfwd_bottleneck_prepare", "cfwd_bottleneck_fwd",
-    "cfwd_convert_layout",
+    "cfwd_convert_layout", "cfwd_unpack_int4",
 ]
 ACT_NONE, ACT_RELU = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # CFWD_NOALLOC_SCRATCH_BYTES
@@ -115,6 +115,7 @@ def _lib():
             "cfwd_fastrun_clear": [],
             "cfwd_fastrun_allow_inexact_int8": [ctypes.c_int],
             "cfwd_bottleneck_check": [P(BottleneckDesc)],
+            "cfwd_unpack_int4": [vp, vp, ctypes.c_longlong, vp],
             "cfwd_convert_layout": [ctypes.c_int] * 4 + [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int,
                                                          ctypes.c_int, vp, vp],
             "cfwd_bottleneck_filter_size": [P(BottleneckDesc), P(sz)],
@@ -572,4 +573,16 @@ def convert_layout(t, src_layout: str, dst_layout: str, dst_x: int = 0, channels
         out = torch.empty(shape, dtype=t.dtype, device=t.device)
     _check(_lib().cfwd_convert_layout(n, c, h, w, _DTYPE_CODES[_dtype_of(t)], _LAYOUTS[sl], sx, t.data_ptr(),
                                       _LAYOUTS[dl], int(dst_x), out.data_ptr(), _stream()))
+    return out
+
+
+# ------------------------------------------------------- 4-bit weights
+
+def unpack_int4(packed, count: int, out=None):
+    """int8 tensor of ``count`` signed 4-bit values packed two per byte, low nibble first (cfwd_unpack_int4)."""
+    torch = _torch()
+    _check_dev(packed, out)
+    if out is None:
+        out = torch.empty(count, dtype=torch.int8, device=packed.device)
+    _check(_lib().cfwd_unpack_int4(packed.data_ptr(), out.data_ptr(), int(count), _stream()))
     return out

@@ -28,6 +28,7 @@
 #include "winograd_i8.h"
 #include "bottleneck.h"
 #include "nhwc.h"
+#include "lowbit.h"
 
 #define CFWD_VERSION "0.1.0"
 
@@ -1073,6 +1074,17 @@ cfwd_status cfwd_convert_layout(int n, int c, int h, int w, cfwd_dtype dtype, cf
     const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
     if (a < b + db && b < a + sb) return set_error(CFWD_ERR_INVALID_ARG, "src and dst must not overlap");
     return layout_convert(n, c, h, w, es, src_layout, src_x, src, dst_layout, dst_x, dst, static_cast<hipStream_t>(stream));
+}
+
+cfwd_status cfwd_unpack_int4(const void* packed, void* out_int8, long long count, void* stream) {
+    if (count < 1) return set_error(CFWD_ERR_INVALID_ARG, "count must be >= 1");
+    if (!packed || !out_int8) return set_error(CFWD_ERR_INVALID_ARG, "packed and out_int8 must not be NULL");
+    if (!aligned16(packed) || !aligned16(out_int8))
+        return set_error(CFWD_ERR_INVALID_ARG, "packed and out_int8 must be 16-byte aligned");
+    const uintptr_t a = reinterpret_cast<uintptr_t>(packed), b = reinterpret_cast<uintptr_t>(out_int8);
+    const uintptr_t pb = static_cast<uintptr_t>((count + 1) / 2), ob = static_cast<uintptr_t>(count);
+    if (a < b + ob && b < a + pb) return set_error(CFWD_ERR_INVALID_ARG, "packed and out_int8 must not overlap");
+    return unpack_int4(packed, out_int8, count, static_cast<hipStream_t>(stream));
 }
 
 cfwd_status cfwd_fastrun_allow_inexact_int8(int allow) {

@@ -156,6 +156,28 @@ def from_nhwc(x: np.ndarray) -> np.ndarray:
     """[N, H, W, C] -> [N, C, H, W]."""
     return np.ascontiguousarray(x.transpose(0, 3, 1, 2))
 
+def pack_int4(v: np.ndarray) -> np.ndarray:
+    """Signed 4-bit values (-8 .. 7), flattened, two per byte: value i in byte
+    i // 2, low nibble for even i, high nibble for odd i (uint8 array)."""
+    v = np.asarray(v).reshape(-1).astype(np.int16)
+    if v.size and (v.min() < -8 or v.max() > 7):
+        raise ValueError("4-bit values must lie in -8 .. 7")
+    u = (v & 0xF).astype(np.uint8)
+    if u.size % 2:
+        u = np.concatenate([u, np.zeros(1, np.uint8)])
+    return (u[0::2] | (u[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(p: np.ndarray, count: int) -> np.ndarray:
+    """Inverse of pack_int4: int8 array of the first ``count`` values."""
+    p = np.asarray(p, dtype=np.uint8)
+    lo = (p & 0xF).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    v = np.empty(p.size * 2, np.int16)
+    v[0::2], v[1::2] = lo, hi
+    v = np.where(v >= 8, v - 16, v)
+    return v[:count].astype(np.int8)
+
 # --------------------------------------------------------------- generators
 
 

@@ -283,6 +283,16 @@ cfwd_status cfwd_convert_layout(int n, int c, int h, int w, cfwd_dtype dtype, cf
                                 int src_x, const void *src, cfwd_layout dst_layout, int dst_x, void *dst,
                                 void *stream);
 
+/* 4-bit weights (MegEngine CPU-inference article, section "结论": lower-bit
+ * quantisation after int8).  gfx950's matrix cores have no int4 operands, so
+ * 4-bit weights are stored packed and widened once, when loaded, to the int8
+ * KCRS tensor every int8 call takes; results are then the int8 path's, bit
+ * for bit.  out_int8[i] = signed value i of `packed`: byte i / 2, low nibble
+ * for even i, high nibble for odd i, two's complement (-8 .. 7).  packed
+ * holds (count + 1) / 2 bytes and must be 16-byte aligned, out_int8 count
+ * bytes, 16-byte aligned, not overlapping packed.  Enqueued on `stream`. */
+cfwd_status cfwd_unpack_int4(const void *packed, void *out_int8, long long count, void *stream);
+
 /* Whether int8 candidates whose results are not always bit-identical to the
  * integer ones (int8 Winograd F(2x2), see WINOGRAD_F2X2_3X3 above) take part
  * in cfwd_list_candidates and cfwd_fastrun_select: 0 (the default) = no,

@@ -254,3 +254,11 @@ def test_convert_layout_validation_on_the_host():
     assert lib.cfwd_convert_layout(*args, B.LAYOUT_NCHW, 0, 4097, B.LAYOUT_NHWC, 0, 1 << 20, None) == B.ERR_INVALID_ARG
     assert lib.cfwd_convert_layout(0, 8, 4, 4, B.BF16, B.LAYOUT_NCHW, 0, 4096, B.LAYOUT_NHWC, 0, 1 << 20,
                                    None) == B.ERR_INVALID_ARG
+
+
+def test_unpack_int4_validation_on_the_host():
+    lib = B.library()
+    assert lib.cfwd_unpack_int4(None, 4096, 10, None) == B.ERR_INVALID_ARG                # NULL
+    assert lib.cfwd_unpack_int4(4096, 8192, 0, None) == B.ERR_INVALID_ARG                 # count
+    assert lib.cfwd_unpack_int4(4104, 8192, 10, None) == B.ERR_INVALID_ARG                # misaligned
+    assert lib.cfwd_unpack_int4(4096, 4096 + 16, 64, None) == B.ERR_INVALID_ARG           # overlap

@@ -50,3 +50,16 @@ def test_nhwc_index_formula_and_roundtrip():
                 for w in range(W):
                     assert flat[((n * H + h) * W + w) * C + c] == x[n, c, h, w]
     np.testing.assert_array_equal(from_nhwc(t), x)
+
+
+def test_int4_packing_worked_example():
+    """Two values per byte, low nibble first, two's complement: [1, -1, 7, -8, 3]
+    packs to 0xF1 (1 low, -1 = 0xF high), 0x87 (7 low, -8 = 0x8 high), 0x03."""
+    from cnn_convolution_fwd_amd.workloads import pack_int4, unpack_int4
+    p = pack_int4(np.array([1, -1, 7, -8, 3]))
+    assert list(p) == [0xF1, 0x87, 0x03]
+    np.testing.assert_array_equal(unpack_int4(p, 5), np.array([1, -1, 7, -8, 3], np.int8))
+    v = np.random.default_rng(4).integers(-8, 8, 1001)
+    np.testing.assert_array_equal(unpack_int4(pack_int4(v), v.size), v.astype(np.int8))
+    with pytest.raises(ValueError):
+        pack_int4(np.array([8]))
