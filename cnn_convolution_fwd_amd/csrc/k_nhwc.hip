@@ -14,9 +14,11 @@
 // pixel's channels are contiguous, so both operands are staged into LDS by
 // plain 16-byte copies -- the pack the article fuses into im2col costs
 // nothing here -- and each K step is one tap of one 64-byte channel chunk.
-// Workgroup: 128 channels x 128 pixels, 4 waves of 64 x 64 (16 fragments of
-// 16 x 16), LDS double-buffered with one barrier per K step; the next step's
-// pieces are loaded into registers while the current step multiplies.
+// Workgroup: 128 channels x TP = 128 pixels, 4 waves of 64 x 64 (16 x 16
+// fragments), LDS double-buffered with one barrier per K step; the next
+// step's pieces are loaded into registers while the current step
+// multiplies.  (A 256-pixel tile measured slower: its 128 accumulators per
+// lane leave one wave per SIMD.)
 // The weights are prepared once as [k][r][s][C rounded up to the chunk].
 #include "internal.h"
 #include "nhwc.h"
@@ -25,9 +27,8 @@ namespace cfwd {
 namespace nh {
 
 constexpr int TK = 128;   // output channels per workgroup
-constexpr int TP = 128;   // output pixels per workgroup
 constexpr int NTHR = 256;
-constexpr int BUF = (TK + TP) * 64;  // one LDS buffer: A rows then B rows, 64 bytes each
+constexpr int kTP[1] = {128};  // output pixels per workgroup, per config
 
 template <typename T> struct Op;
 template <> struct Op<bf16_t> {
@@ -66,10 +67,13 @@ __device__ __forceinline__ int slot_off(int r, int j) { return r * 64 + ((j ^ ((
 __device__ __forceinline__ uint4 ld16(const void* p) { return __builtin_bit_cast(uint4, *reinterpret_cast<const i32x4*>(p)); }
 __device__ __forceinline__ void st16(void* p, const uint4& v) { *reinterpret_cast<i32x4*>(p) = __builtin_bit_cast(i32x4, v); }
 
-template <typename T, bool EPI>
+template <typename T, bool EPI, int TP>
 __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
     using O = Op<T>;
     constexpr int E16 = O::E16, CK = O::CK;
+    constexpr int BUF = (TK + TP) * 64;  // one LDS buffer: A rows then B rows, 64 bytes each
+    constexpr int NB = TP / 64;          // pixel pieces per thread per step
+    constexpr int NT = TP / 32;          // pixel fragments per wave
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, i = lane & 15;
@@ -81,11 +85,11 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
     const T* __restrict__ x = static_cast<const T*>(a.x);
     const T* __restrict__ wp = static_cast<const T*>(a.wp);
 
-    // staging pieces: u = 0, 1 weights (row k, slot j), u = 2, 3 pixels
-    long long wsrc[2];   // element offset of the piece for tap 0, chunk 0 (-1: zero)
-    int ih0[2], iw0[2];  // pixel pieces: input origin of the output pixel
-    long long xbase[2];  // element offset of the image (-1: no pixel)
-    int lofs[4];
+    // staging pieces: u = 0, 1 weights (row k, slot j), then NB pixel pieces
+    long long wsrc[2];     // element offset of the piece for tap 0, chunk 0 (-1: zero)
+    int ih0[NB], iw0[NB];  // pixel pieces: input origin of the output pixel
+    long long xbase[NB];   // element offset of the image (-1: no pixel)
+    int lofs[2 + NB];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int q = tid + NTHR * u;
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
         lofs[u] = slot_off(row, j);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < NB; ++u) {
         const int q = tid + NTHR * u;
         const int px = q >> 2, j = q & 3;
         const int P = m0 + px;
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
         lofs[2 + u] = TK * 64 + slot_off(px, j);
     }
     const int steps = a.nch * RS;
-    uint4 stg[4];
+    uint4 stg[2 + NB];
     auto load = [&](int st) __attribute__((always_inline)) {
         const int chunk = st / RS, tap = st - chunk * RS;
         const int r = tap / a.S, s = tap - r * a.S;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
         for (int u = 0; u < 2; ++u)
             stg[u] = (wsrc[u] >= 0) ? ld16(wp + wsrc[u] + static_cast<long long>(tap) * a.Cp + c0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int ih = ih0[u] + r * a.dh, iw = iw0[u] + s * a.dw;
             const int c = c0 + (((tid + NTHR * u) & 3) * E16);
             const bool ok = xbase[u] >= 0 && static_cast<unsigned>(ih) < static_cast<unsigned>(a.H) &&
@@ -133,21 +137,20 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
     };
     auto store = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) st16(lds + buf * BUF + lofs[u], stg[u]);
+        for (int u = 0; u < 2 + NB; ++u) st16(lds + buf * BUF + lofs[u], stg[u]);
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[4][NT];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    // this lane's operand rows: weights 64 wk + 16 mt + i, pixels 64 wq + 16 nt + i
-    int aoff[4], boff[4];
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    // this lane's operand rows: weights 64 wk + 16 mt + i, pixels (TP / 2) wq + 16 nt + i
+    int aoff[4], boff[NT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        aoff[t] = slot_off(64 * wk + 16 * t + i, g);
-        boff[t] = TK * 64 + slot_off(64 * wq + 16 * t + i, g);
-    }
+    for (int t = 0; t < 4; ++t) aoff[t] = slot_off(64 * wk + 16 * t + i, g);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) boff[t] = TK * 64 + slot_off((TP / 2) * wq + 16 * t + i, g);
 
     load(0);
     store(0);
@@ -155,27 +158,26 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
     __syncthreads();
     for (int st = 0; st < steps; ++st) {
         const uint8_t* buf = lds + (st & 1) * BUF;
-        uint4 af[4], bf[4];
+        uint4 af[4], bf[NT];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            af[t] = ld16(buf + aoff[t]);
-            bf[t] = ld16(buf + boff[t]);
-        }
+        for (int t = 0; t < 4; ++t) af[t] = ld16(buf + aoff[t]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) bf[t] = ld16(buf + boff[t]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt) O::mma(acc[mt][nt], af[mt], bf[nt]);
+            for (int nt = 0; nt < NT; ++nt) O::mma(acc[mt][nt], af[mt], bf[nt]);
         if (st + 1 < steps) store((st + 1) & 1);  // that buffer was last read before the previous barrier
         if (st + 2 < steps) load(st + 2);
         __syncthreads();
     }
 
-    // D[channel][pixel]: lane holds pixel 64 wq + 16 nt + i, channels
+    // D[channel][pixel]: lane holds pixel (TP / 2) wq + 16 nt + i, channels
     // 64 wk + 16 mt + 4g .. + 3, which are consecutive in NHWC
     T* __restrict__ y = static_cast<T*>(a.y);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-        const int P = m0 + 64 * wq + 16 * nt + i;
+    for (int nt = 0; nt < NT; ++nt) {
+        const int P = m0 + (TP / 2) * wq + 16 * nt + i;
         if (P >= a.npix) continue;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
@@ -268,7 +270,7 @@ struct Plan {
     int Cp, nch, ntk, npix;
 };
 
-bool plan(const Prob& p, Plan* pl, std::string* why) {
+bool plan(const Prob& p, int cfg, Plan* pl, std::string* why) {
     auto no = [&](const char* m) {
         if (why) *why = m;
         return false;
@@ -279,7 +281,8 @@ bool plan(const Prob& p, Plan* pl, std::string* why) {
     const int e16 = 16 / p.esize, ck = 64 / p.esize;
     if (p.c % e16 != 0) return no("implicit GEMM (NHWC): C must be a multiple of 8 (bf16) or 4 (fp32)");
     const long long npix = static_cast<long long>(p.n) * p.oh * p.ow;
-    if (npix >= (1LL << 31) - TP) return no("implicit GEMM (NHWC): too many output pixels");
+    if (cfg != 0) return no("implicit GEMM (NHWC): no such config");
+    if (npix >= (1LL << 31) - kTP[cfg]) return no("implicit GEMM (NHWC): too many output pixels");
     pl->Cp = (p.c + ck - 1) / ck * ck;
     pl->nch = pl->Cp / ck;
     pl->ntk = (p.k + TK - 1) / TK;
@@ -294,24 +297,20 @@ bool plan(const Prob& p, Plan* pl, std::string* why) {
 int nhwc_num_configs() { return 1; }
 
 bool nhwc_supported(const Prob& p, int cfg, std::string* why) {
-    if (cfg != 0) {
-        if (why) *why = "implicit GEMM (NHWC): no such config";
-        return false;
-    }
     nh::Plan pl;
-    return nh::plan(p, &pl, why);
+    return nh::plan(p, cfg, &pl, why);
 }
 
 size_t nhwc_filter_bytes(const Prob& p, int cfg) {
     nh::Plan pl;
-    if (cfg != 0 || !nh::plan(p, &pl, nullptr)) return 0;
+    if (!nh::plan(p, cfg, &pl, nullptr)) return 0;
     return static_cast<size_t>(p.k) * p.r * p.s * pl.Cp * p.esize;
 }
 
 cfwd_status nhwc_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStream_t st) {
     nh::Plan pl;
     std::string why;
-    if (cfg != 0 || !nh::plan(p, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    if (!nh::plan(p, cfg, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     const long long total = static_cast<long long>(p.k) * p.r * p.s * pl.Cp;
     const unsigned blocks = static_cast<unsigned>(std::min<long long>((total + 255) / 256, 65536));
     if (p.dtype == CFWD_BF16)
@@ -326,7 +325,7 @@ cfwd_status nhwc_prepare(const Prob& p, int cfg, const void* w, void* wp, hipStr
 cfwd_status nhwc_launch(const Prob& p, int cfg, const void* x, const void* wp, void* y, const Epi& e, hipStream_t st) {
     nh::Plan pl;
     std::string why;
-    if (cfg != 0 || !nh::plan(p, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
+    if (!nh::plan(p, cfg, &pl, &why)) return set_error(CFWD_ERR_UNSUPPORTED, why);
     if (wp == nullptr) return set_error(CFWD_ERR_WORKSPACE, "implicit GEMM (NHWC): the prepared filter is required");
     nh::Args a;
     a.x = x;
@@ -336,17 +335,16 @@ cfwd_status nhwc_launch(const Prob& p, int cfg, const void* x, const void* wp, v
     a.sh = p.sh; a.sw = p.sw; a.ph = p.ph; a.pw = p.pw; a.dh = p.dh; a.dw = p.dw; a.OH = p.oh; a.OW = p.ow;
     a.Cp = pl.Cp; a.nch = pl.nch; a.ntk = pl.ntk; a.npix = pl.npix;
     a.e = e;
-    const long long blocks = static_cast<long long>((pl.npix + nh::TP - 1) / nh::TP) * pl.ntk;
+    const int tp = nh::kTP[cfg];
+    const long long blocks = static_cast<long long>((pl.npix + tp - 1) / tp) * pl.ntk;
     if (blocks > 0x7fffffffLL) return set_error(CFWD_ERR_UNSUPPORTED, "implicit GEMM (NHWC): too many tiles");
     const bool epi = e.bias || e.res || e.relu;
     const unsigned nb = static_cast<unsigned>(blocks);
-    if (p.dtype == CFWD_BF16) {
-        if (epi) nh::nhwc_kernel<bf16_t, true><<<nb, nh::NTHR, 0, st>>>(a);
-        else nh::nhwc_kernel<bf16_t, false><<<nb, nh::NTHR, 0, st>>>(a);
-    } else {
-        if (epi) nh::nhwc_kernel<float, true><<<nb, nh::NTHR, 0, st>>>(a);
-        else nh::nhwc_kernel<float, false><<<nb, nh::NTHR, 0, st>>>(a);
-    }
+    auto go = [&](auto kern) { kern<<<nb, nh::NTHR, 0, st>>>(a); };
+    if (p.dtype == CFWD_BF16)
+        epi ? go(nh::nhwc_kernel<bf16_t, true, 128>) : go(nh::nhwc_kernel<bf16_t, false, 128>);
+    else
+        epi ? go(nh::nhwc_kernel<float, true, 128>) : go(nh::nhwc_kernel<float, false, 128>);
     return check_hip(hipGetLastError(), "NHWC implicit GEMM launch");
 }
 

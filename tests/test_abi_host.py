@@ -219,7 +219,7 @@ def test_bottleneck_block_checks_on_the_host():
 def test_nhwc_routes_to_its_own_configs(dtype):
     desc = B.make_desc(32, 256, 56, 56, 256, 3, 3, 1, 1, 1, 1, "NHWC", None, dtype)
     cands = B.list_candidates(desc)
-    assert len(cands) == 1 and cands[0].kind == B.ALGO_IMPLICIT_GEMM
+    assert len(cands) == 1 and all(a.kind == B.ALGO_IMPLICIT_GEMM for a in cands)
     nhwc_cfg = cands[0].config_id
     assert B.resolve_algo(desc, B.algo()).key() == cands[0].key()
     assert B.resolve_algo(desc, B.algo("implicit_gemm")).key() == cands[0].key()

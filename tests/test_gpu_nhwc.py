@@ -39,13 +39,14 @@ SHAPES = [
 ]
 
 
-def run_nhwc(x, w, dtype, st, pd, dl, bias=None, res=None, relu=False):
+def run_nhwc(x, w, dtype, st, pd, dl, bias=None, res=None, relu=False, cfg=-1):
     torch = torch_cuda()
     xd = to_device(to_nhwc(x), dtype)
     wd = to_device(w, dtype)
     bd = torch.from_numpy(bias).cuda() if bias is not None else None
     rd = to_device(to_nhwc(res), dtype) if res is not None else None
-    y = B.conv2d_fwd(xd, wd, st, pd, dl, 1, "NHWC", bias=bd, residual=rd, relu=relu)
+    y = B.conv2d_fwd(xd, wd, st, pd, dl, 1, "NHWC", algo_kind="implicit_gemm" if cfg >= 0 else "auto", config_id=cfg,
+                     bias=bd, residual=rd, relu=relu)
     return from_nhwc(from_device(y, dtype))
 
 
@@ -58,13 +59,14 @@ def test_nhwc_conv(case, dtype):
     x_nhwc = to_device(to_nhwc(pr.x), dtype)
     desc = B.desc_for(x_nhwc, to_device(pr.w, dtype), st, pd, dl, 1, "NHWC")
     cands = [(a.kind, a.config_id) for a in B.list_candidates(desc)]
-    assert len(cands) == 1 and cands[0][0] == B.ALGO_IMPLICIT_GEMM, cands
+    assert cands and all(k == B.ALGO_IMPLICIT_GEMM for k, _ in cands), cands
     ref, den = oracle.conv2d(pr.x, pr.w, st, pd, dl, 1)
-    say("nhwc", name, dtype)
-    y = run_nhwc(pr.x, pr.w, dtype, st, pd, dl)
-    err = oracle.normalised_error(y, ref, den)
-    say("  normalised error %.3g" % err)
-    assert err <= TOL[dtype], "%s %s: %.3g" % (name, dtype, err)
+    for _, cfg in cands:
+        say("nhwc", name, dtype, "config", cfg)
+        y = run_nhwc(pr.x, pr.w, dtype, st, pd, dl, cfg=cfg)
+        err = oracle.normalised_error(y, ref, den)
+        say("  normalised error %.3g" % err)
+        assert err <= TOL[dtype], "%s %s config %d: %.3g" % (name, dtype, cfg, err)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -74,10 +76,12 @@ def test_nhwc_epilogue(dtype):
     pr = random_float_problem(L, N, dtype, 91)
     epi = epilogue_inputs((N, K, H, W), dtype, 92)
     ref, den = oracle.conv2d_fused(pr.x, pr.w, epi.bias, epi.residual, True, 1, 1)
-    y = run_nhwc(pr.x, pr.w, dtype, 1, 1, 1, epi.bias, epi.residual, True)
-    err = oracle.normalised_error(y, ref, den)
-    say("nhwc epilogue", dtype, "%.3g" % err)
-    assert err <= TOL[dtype]
+    xd = to_device(to_nhwc(pr.x), dtype)
+    for a in B.list_candidates(B.desc_for(xd, to_device(pr.w, dtype), 1, 1, 1, 1, "NHWC")):
+        y = run_nhwc(pr.x, pr.w, dtype, 1, 1, 1, epi.bias, epi.residual, True, cfg=a.config_id)
+        err = oracle.normalised_error(y, ref, den)
+        say("nhwc epilogue", dtype, a.config_id, "%.3g" % err)
+        assert err <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -85,11 +89,13 @@ def test_nhwc_resnet3x3_full_size(dtype):
     """The ResNet 3x3 256-channel layer (N=32, 56x56) in NHWC, whole tensor."""
     pr = float_problem(3, 0, dtype=dtype)
     ref, den = oracle.conv2d(pr.x, pr.w, 1, 1)
-    say("nhwc resnet3x3 full", dtype)
-    y = run_nhwc(pr.x, pr.w, dtype, 1, 1, 1)
-    err = oracle.normalised_error(y, ref, den)
-    say("  normalised error %.3g" % err)
-    assert err <= TOL[dtype]
+    xd = to_device(to_nhwc(pr.x), dtype)
+    for a in B.list_candidates(B.desc_for(xd, to_device(pr.w, dtype), 1, 1, 1, 1, "NHWC")):
+        say("nhwc resnet3x3 full", dtype, "config", a.config_id)
+        y = run_nhwc(pr.x, pr.w, dtype, 1, 1, 1, cfg=a.config_id)
+        err = oracle.normalised_error(y, ref, den)
+        say("  normalised error %.3g" % err)
+        assert err <= TOL[dtype]
 
 
 def test_nhwc_fastrun_gate_uses_converted_reference():
