@@ -38,8 +38,34 @@ namespace {
 thread_local std::string g_last_error;
 }
 
+// Environment, read once: CFWD_LOG (0 silent, 1 failures, 2 + AUTO choices,
+// 3 + every call's resolved algorithm), CFWD_FASTRUN_MODE (off: AUTO ignores
+// the map; readonly, the default: map, else the fixed preference; search: a
+// map miss with a large enough workspace runs the selection),
+// CFWD_FASTRUN_CACHE (a map file loaded at the first AUTO call and, in search
+// mode, rewritten after each selection).
+struct Env {
+    int log = 0;
+    enum { OFF, READONLY, SEARCH } mode = READONLY;
+    std::string cache;
+};
+const Env& env() {
+    static const Env e = [] {
+        Env v;
+        if (const char* l = std::getenv("CFWD_LOG")) v.log = std::atoi(l);
+        if (const char* m = std::getenv("CFWD_FASTRUN_MODE")) {
+            if (std::strcmp(m, "off") == 0) v.mode = Env::OFF;
+            else if (std::strcmp(m, "search") == 0) v.mode = Env::SEARCH;
+        }
+        if (const char* c = std::getenv("CFWD_FASTRUN_CACHE")) v.cache = c;
+        return v;
+    }();
+    return e;
+}
+
 cfwd_status set_error(cfwd_status st, const std::string& msg) {
     g_last_error = msg;
+    if (st != CFWD_OK && env().log >= 1) std::fprintf(stderr, "cfwd: %s\n", msg.c_str());
     return st;
 }
 
@@ -321,6 +347,13 @@ bool map_lookup(const Prob& p, cfwd_algo* out) {
     return true;
 }
 
+// CFWD_FASTRUN_CACHE: merged into the map once, before the first AUTO lookup
+std::once_flag g_cache_once;
+void load_cache_once() {
+    if (env().cache.empty()) return;
+    std::call_once(g_cache_once, [] { (void)cfwd_fastrun_load(env().cache.c_str()); });
+}
+
 cfwd_algo heuristic(const Prob& p) {
     if (p.layout == CFWD_LAYOUT_NHWC)
         for (int c = 0; c < nhwc_num_configs(); ++c)
@@ -365,7 +398,8 @@ bool family_default(const Prob& p, cfwd_algo_kind k, int* cfg) {
 
 cfwd_status resolve(const Prob& p, cfwd_algo in, cfwd_algo* out) {
     if (in.kind == CFWD_ALGO_AUTO) {
-        if (map_lookup(p, out)) return CFWD_OK;
+        load_cache_once();
+        if (env().mode != Env::OFF && map_lookup(p, out)) return CFWD_OK;
         *out = heuristic(p);
         std::string why;
         // NHWC problems outside the NHWC kernel's scope have no algorithm
@@ -878,20 +912,34 @@ cfwd_status cfwd_conv2d_fwd_ex(const cfwd_conv_desc* desc, cfwd_algo algo, const
     const bool has_epi = e.bias || e.res || e.relu;
     hipStream_t st = static_cast<hipStream_t>(stream);
     cfwd_algo a;
+    const Env& ev = env();
     if (algo.kind == CFWD_ALGO_AUTO) {
-        if (!map_lookup(p, &a)) {
-            const char* mode = std::getenv("CFWD_FASTRUN_MODE");
-            if (mode && std::strcmp(mode, "search") == 0 && workspace && !has_epi) {
+        load_cache_once();
+        const char* how = "map";
+        if (ev.mode == Env::OFF || !map_lookup(p, &a)) {
+            if (ev.mode == Env::SEARCH && workspace && !has_epi) {
                 size_t need = fastrun_layout(p, candidates(p)).total;
-                if (ws_bytes >= need)
-                    return cfwd_fastrun_select(desc, x, w_kcrs, requant_scale, y, workspace, ws_bytes, stream, &a);
+                if (ws_bytes >= need) {
+                    s = cfwd_fastrun_select(desc, x, w_kcrs, requant_scale, y, workspace, ws_bytes, stream, &a);
+                    if (s == CFWD_OK && !ev.cache.empty()) s = cfwd_fastrun_save(ev.cache.c_str());
+                    if (ev.log >= 2)
+                        std::fprintf(stderr, "cfwd: AUTO %s -> %s (search)\n", problem_key(p).c_str(),
+                                     cfwd_algo_name(a));
+                    return s;
+                }
             }
             a = heuristic(p);
+            how = "fixed preference";
+            // NHWC problems outside the NHWC kernel's scope have no algorithm
+            if (p.layout == CFWD_LAYOUT_NHWC && !supported(p, a.kind, a.config_id, &why))
+                return set_error(CFWD_ERR_UNSUPPORTED, why);
         }
+        if (ev.log >= 2) std::fprintf(stderr, "cfwd: AUTO %s -> %s (%s)\n", problem_key(p).c_str(), cfwd_algo_name(a), how);
     } else {
         s = resolve(p, algo, &a);
         if (s != CFWD_OK) return s;
     }
+    if (ev.log >= 3) std::fprintf(stderr, "cfwd: conv %s with %s\n", problem_key(p).c_str(), cfwd_algo_name(a));
     return conv_impl(p, a, x, w_kcrs, w_prepared, requant_scale, y, workspace, ws_bytes, st, e);
 }
 

@@ -72,6 +72,18 @@
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the default
  * stream).  Calls that only enqueue work return without waiting.
  *
+ * Environment (read once per process):
+ *   CFWD_FASTRUN_MODE  readonly (default): AUTO takes the Fast-Run map entry,
+ *                      else the fixed preference; off: AUTO ignores the map;
+ *                      search: a map miss of cfwd_conv2d_fwd with a workspace
+ *                      of cfwd_fastrun_workspace_size bytes runs the selection.
+ *   CFWD_FASTRUN_CACHE a map file merged into the map before the first AUTO
+ *                      resolution; in search mode rewritten after each
+ *                      selection.
+ *   CFWD_LOG           0 silent (default); 1 every failure's reason on stderr;
+ *                      2 also each AUTO resolution and how it was made; 3 also
+ *                      the algorithm of every convolution call.
+ *
  * Errors: every call returns a cfwd_status; on failure nothing has been
  * enqueued and cfwd_last_error() (per thread) describes why.  Validation
  * failures never touch y.  No call allocates device memory.

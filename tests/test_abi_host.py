@@ -262,3 +262,19 @@ def test_unpack_int4_validation_on_the_host():
     assert lib.cfwd_unpack_int4(4096, 8192, 0, None) == B.ERR_INVALID_ARG                 # count
     assert lib.cfwd_unpack_int4(4104, 8192, 10, None) == B.ERR_INVALID_ARG                # misaligned
     assert lib.cfwd_unpack_int4(4096, 4096 + 16, 64, None) == B.ERR_INVALID_ARG           # overlap
+
+
+def test_cfwd_log_reports_failures(tmp_path):
+    """CFWD_LOG=1 prints each failure's reason to stderr (environment read once per process)."""
+    import subprocess
+    import sys as _sys
+    code = ("from cnn_convolution_fwd_amd import binding as B\n"
+            "d = B.make_desc(1, 8, 8, 8, 8, 3, 3, 2, 1, dtype='f32')\n"
+            "try:\n    B.resolve_algo(d, B.algo('winograd_f2x2_3x3'))\nexcept B.CfwdError:\n    pass\n")
+    env = dict(os.environ, CFWD_LOG="1")
+    r = subprocess.run([_sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert "cfwd: winograd" in r.stderr
+    env["CFWD_LOG"] = "0"
+    r = subprocess.run([_sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert "cfwd:" not in r.stderr
