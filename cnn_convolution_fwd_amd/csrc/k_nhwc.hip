@@ -117,8 +117,10 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
         lofs[2 + u] = TK * 64 + slot_off(px, j);
     }
     const int steps = a.nch * RS;
-    uint4 stg[2 + NB];
-    auto load = [&](int st) __attribute__((always_inline)) {
+    // two register sets: the pieces of steps st + 1 and st + 2 are in
+    // flight while step st multiplies
+    uint4 sa[2 + NB], sb[2 + NB];
+    auto load = [&](uint4 (&stg)[2 + NB], int st) __attribute__((always_inline)) {
         const int chunk = st / RS, tap = st - chunk * RS;
         const int r = tap / a.S, s = tap - r * a.S;
         const int c0 = chunk * CK;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
                             : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store = [&](int buf) __attribute__((always_inline)) {
+    auto store = [&](const uint4 (&stg)[2 + NB], int buf) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < 2 + NB; ++u) st16(lds + buf * BUF + lofs[u], stg[u]);
     };
@@ -152,11 +154,7 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) boff[t] = TK * 64 + slot_off((TP / 2) * wq + 16 * t + i, g);
 
-    load(0);
-    store(0);
-    if (steps > 1) load(1);
-    __syncthreads();
-    for (int st = 0; st < steps; ++st) {
+    auto step_mma = [&](int st) __attribute__((always_inline)) {
         const uint8_t* buf = lds + (st & 1) * BUF;
         uint4 af[4], bf[NT];
 #pragma unroll
@@ -167,9 +165,26 @@ __global__ __launch_bounds__(NTHR) void nhwc_kernel(Args a) {
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) O::mma(acc[mt][nt], af[mt], bf[nt]);
-        if (st + 1 < steps) store((st + 1) & 1);  // that buffer was last read before the previous barrier
-        if (st + 2 < steps) load(st + 2);
+    };
+    // at the top of step st: LDS buffer st & 1 holds step st; the set for
+    // step st + 1 (sb when st is even) and the other (step st + 2) are in
+    // flight; the loop takes two steps so each set is fixed
+    load(sa, 0);
+    store(sa, 0);
+    if (steps > 1) load(sb, 1);
+    if (steps > 2) load(sa, 2);
+    __syncthreads();
+    for (int st = 0; st < steps; st += 2) {
+        step_mma(st);
+        if (st + 1 < steps) store(sb, 1);  // buffer 1 was last read before the previous barrier
+        if (st + 3 < steps) load(sb, st + 3);
         __syncthreads();
+        if (st + 1 < steps) {
+            step_mma(st + 1);
+            if (st + 2 < steps) store(sa, 0);
+            if (st + 4 < steps) load(sa, st + 4);
+            __syncthreads();
+        }
     }
 
     // D[channel][pixel]: lane holds pixel (TP / 2) wq + 16 nt + i, channels
