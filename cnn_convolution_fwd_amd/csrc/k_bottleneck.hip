@@ -10,7 +10,8 @@
 // the tiles' overlap.  Here the hand-over is in LDS and covers all three
 // convolutions: only x is read from HBM and only y is written.
 //
-// Workgroup = TH = 4 output rows (all W columns) of one image, 4 waves:
+// Workgroup = TH = 4 output rows (all W columns) of one image, 8 waves (two
+// workgroups per CU: four waves per SIMD to cover each stage's latencies):
 //   A  t1 = act1(w1 . x + b1) on the TH + 2 rows the 3x3 needs (its halo is
 //      recomputed by the neighbouring workgroups: 1.5x the first 1x1's
 //      work).  x arrives in chunks of 32 channels, copied from NCHW rows as
@@ -40,13 +41,15 @@ namespace bn {
 
 constexpr int TH = 4;      // output rows per workgroup
 constexpr int MID = 64;    // inner channels
-constexpr int NTHR = 256;  // 4 waves
+constexpr int NW = 8;      // waves per workgroup (four per SIMD with two workgroups per CU)
+constexpr int NTHR = 64 * NW;
 constexpr int KC = 32;     // input channels per staged chunk
 constexpr int MAXW = 64;
-constexpr int TA = 6;      // stage-A pixel tiles per wave: ceil(3W/8 / 4) for W <= 64
-constexpr int TBW = 4;     // stage-B/C pixel tiles per wave: ceil(W/4 / 4)
+constexpr int TA = 24 / NW;   // stage-A pixel tiles per wave: ceil(3W/8 / NW) for W <= 64
+constexpr int TBW = 16 / NW;  // stage-B pixel tiles per wave: ceil(W/4 / NW)
+constexpr int TCW = 4;        // stage-C pixel tiles per wave (64 pixels: one 128-byte run per channel)
 constexpr int KP = 32;     // output channels per stage-C pass
-constexpr int XP = 6;      // staged 16-byte pieces per thread per chunk: 32 * 6W/8 / 256
+constexpr int XP = 1536 / NTHR;  // staged 16-byte pieces per thread per chunk: 32 * 6W/8 / NTHR
 constexpr int SPITCH = 68; // floats per channel row of a wave's output slice (64 pixels + 4: rows 16 bytes apart in the banks)
 constexpr int TG = 3;      // 3x3 taps per staged w2 group
 constexpr int W2G = TG * 2 * 4 * 1024;  // bytes of one staged w2 group: [tap][half][mt][lane][16 B]
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
     int troff[TA];
 #pragma unroll
     for (int u = 0; u < TA; ++u) {
-        const int jt = min(wave + 4 * u, ntA - 1);
+        const int jt = min(wave + NW * u, ntA - 1);
         troff[u] = ((4 * g + (i >> 2)) * a.pitch_x + 16 * jt + 4 * (i & 3)) * 2;
     }
     const int tr2 = 16 * a.pitch_x * 2;
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
             for (int v = 0; v < 4; ++v) bias[mt][v] = a.b1 ? a.b1[16 * mt + 4 * g + v] : 0.0f;
 #pragma unroll
         for (int u = 0; u < TA; ++u) {
-            const int jt = wave + 4 * u;
+            const int jt = wave + NW * u;
             if (jt >= ntA) continue;
             const int p = 16 * jt + i;
             const int row = p / W, col = p - row * W;
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
     int rp0[TBW];
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
-        const int jt = min(wave + 4 * u, ntB - 1);
+        const int jt = min(wave + NW * u, ntB - 1);
         const int p = 16 * jt + i;
         const int orow = p / W, ocol = p - orow * W;
         rp0[u] = (orow + 1) * W2 + ocol + 1;
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
             for (int v = 0; v < 4; ++v) bias[mt][v] = a.b2 ? a.b2[16 * mt + 4 * g + v] : 0.0f;
 #pragma unroll
         for (int u = 0; u < TBW; ++u) {
-            const int jt = wave + 4 * u;
+            const int jt = wave + NW * u;
             if (jt >= ntB) continue;
             const int p = 16 * jt + i;
 #pragma unroll
@@ -328,36 +331,37 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
 
     // ------------------------------------------------------------ stage C
     // (R1 is free: every wave passed the barrier above after its last read
-    // of t1.)  Wave w owns the band's output pixels [64 w, 64 w + 64) (pixel tiles
-    // 4w .. 4w + 3; tiles past the band repeat the last one, unstored).  Per
-    // pass of 32 channels its fragments go through a private LDS slice
-    // [32 channels][68-float pitch] and come back as 8 consecutive pixels of
-    // one channel per lane: 16-byte streaming stores, 8 lanes per channel.
-    uint4 ta[TBW][2];
+    // of t1.)  Wave w owns the band's output pixels [64 pg, 64 pg + 64),
+    // pg = w % 4 (pixel tiles 4 pg .. 4 pg + 3; tiles past the band repeat
+    // the last one, unstored), and channels 16 kh .. 16 kh + 15 of each pass
+    // of 32, kh = w / 4.  Per pass its fragments go through a private LDS
+    // slice [16 channels][68-float pitch] and come back as 8 consecutive
+    // pixels of one channel per lane: 16-byte streaming stores, 8 lanes per
+    // channel (128 contiguous bytes).
+    const int pg = wave & 3, kh = wave >> 2;
+    uint4 ta[TCW][2];
 #pragma unroll
-    for (int u = 0; u < TBW; ++u) {
-        const int jt = min(4 * wave + u, ntB - 1);
+    for (int u = 0; u < TCW; ++u) {
+        const int jt = min(4 * pg + u, ntB - 1);
         const int p = 16 * jt + i;
 #pragma unroll
         for (int s = 0; s < 2; ++s) ta[u][s] = ld16(R0 + rec_off(p, 4 * s + g));
     }
-    uint4 wc[2][2], wn[2][2];
-    auto load_w3 = [&](uint4 (&w)[2][2], int k0) __attribute__((always_inline)) {
+    uint4 wc[2], wn[2];
+    auto load_w3 = [&](uint4 (&w)[2], int k0) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) w[kt][s] = ld16(a.w3 + (k0 + 16 * kt + i) * MID + 32 * s + 8 * g);
+        for (int s = 0; s < 2; ++s) w[s] = ld16(a.w3 + (k0 + 16 * kh + i) * MID + 32 * s + 8 * g);
     };
-    float* ST = reinterpret_cast<float*>(R1) + wave * (KP * SPITCH);
+    float* ST = reinterpret_cast<float*>(R1) + wave * (16 * SPITCH);
     const uint16_t* resn = a.res ? a.res + static_cast<long long>(n) * K * H * W : nullptr;
     uint16_t* yn = a.y + static_cast<long long>(n) * K * H * W;
     const long long plane = static_cast<long long>(H) * W;
-    // store pieces q = lane + 64 r: channel q / 8 of the pass, pixels 8 (q % 8) ..
-    int pofs[4];  // offset in a channel plane; < 0: nothing to store
+    // store pieces q = lane + 64 r: channel 16 kh + q / 8 of the pass, pixels 8 (q % 8) ..
+    int pofs[2];  // offset in a channel plane; < 0: nothing to store
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < 2; ++r) {
         const int q = lane + 64 * r;
-        const int px = 64 * wave + 8 * (q & 7);
+        const int px = 64 * pg + 8 * (q & 7);
         const int orow = px / W, col = px - orow * W;
         const int oh = oh0 + orow;
         pofs[r] = (px < a.px_b && oh < H) ? oh * W + col : -1;
@@ -366,28 +370,26 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
     load_w3(wc, 0);
     for (int kp = 0; kp < npass; ++kp) {
         if (kp + 1 < npass) load_w3(wn, (kp + 1) * KP);
-        const int k0 = kp * KP;
+        const int k0 = kp * KP + 16 * kh;
         // the epilogue operands of this pass, requested before its products
-        float bk[4];
-        uint4 rv[4];
+        float bk[2];
+        uint4 rv[2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 2; ++r) {
             const int k = k0 + ((lane + 64 * r) >> 3);
             bk[r] = a.b3 ? a.b3[k] : 0.0f;
             rv[r] = (resn && pofs[r] >= 0) ? ld16(resn + k * plane + pofs[r]) : make_uint4(0, 0, 0, 0);
         }
-        // D[pixel][channel]: lane holds channel 16 kt + i, pixels 16 u + 4g .. + 3
+        // D[pixel][channel]: lane holds channel i (of this wave's 16), pixels 16 u + 4g .. + 3
 #pragma unroll
-        for (int u = 0; u < TBW; ++u)
+        for (int u = 0; u < TCW; ++u) {
+            f32x4 c4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                f32x4 c4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int s = 0; s < 2; ++s) c4 = mma(ta[u][s], wc[s], c4);
+            *reinterpret_cast<f32x4*>(ST + i * SPITCH + 16 * u + 4 * g) = c4;
+        }
 #pragma unroll
-                for (int s = 0; s < 2; ++s) c4 = mma(ta[u][s], wc[kt][s], c4);
-                *reinterpret_cast<f32x4*>(ST + (16 * kt + i) * SPITCH + 16 * u + 4 * g) = c4;
-            }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 2; ++r) {
             const int q = lane + 64 * r;
             const float* src = ST + (q >> 3) * SPITCH + 8 * (q & 7);
             const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
@@ -407,9 +409,7 @@ __global__ __launch_bounds__(NTHR, 2) void bottleneck_kernel(Args a) {
                                             reinterpret_cast<i32x4*>(yn + (k0 + (q >> 3)) * plane + pofs[r]));
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int s = 0; s < 2; ++s) wc[kt][s] = wn[kt][s];
+        for (int s = 0; s < 2; ++s) wc[s] = wn[s];
     }
 }
 
@@ -455,7 +455,7 @@ bool plan(const cfwd_bottleneck_desc* d, Plan* pl, std::string* why) {
     const int r0 = std::max(std::max(KC * pl->pitch_x * 2, pl->px_b * 128), W2G);
     pl->r1 = (r0 + 255) / 256 * 256;
     // t1; w1 in operand order during the first 1x1; the waves' output slices
-    const int r1b = std::max(std::max((TH + 2) * (d->w + 2) * 128, d->c * 128), 4 * KP * SPITCH * 4);
+    const int r1b = std::max(std::max((TH + 2) * (d->w + 2) * 128, d->c * 128), NW * 16 * SPITCH * 4);
     pl->lds = pl->r1 + r1b;
     if (pl->lds > 160 * 1024) return no("bottleneck block: too many input channels for LDS (w1 is staged whole)");
     return true;
