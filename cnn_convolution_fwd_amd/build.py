@@ -38,12 +38,14 @@ COMMON = [
 ]
 
 
-# Per-source extra flags.  The gather-form stem kernels are bound by vector
-# ALU issue; keeping MFMA results in ordinary VGPRs instead of accumulation
-# registers removes the register moves around their epilogues (about a tenth
-# of their vector instructions) without raising register use.
+# Per-source extra flags.  The stem kernels (gather form and the int8 NCHW4
+# stem) are bound by vector ALU issue; keeping MFMA results in ordinary VGPRs
+# instead of accumulation registers removes the register moves around their
+# epilogues (about a tenth of their vector instructions) without raising
+# register use.
 EXTRA = {
     "k_lowc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_stem_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

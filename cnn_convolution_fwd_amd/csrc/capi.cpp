@@ -29,6 +29,7 @@
 #include "bottleneck.h"
 #include "nhwc.h"
 #include "lowbit.h"
+#include "stem_i8.h"
 
 #define CFWD_VERSION "0.1.0"
 
@@ -175,13 +176,18 @@ int family_rank(cfwd_algo_kind k) {
 }
 
 // Implicit GEMM configs 0 .. igemm_num_configs() - 1 are the NCHW / NCHWX
-// kernels; the next nhwc_num_configs() the NHWC kernel (k_nhwc.hip).
+// kernels; the next nhwc_num_configs() the NHWC kernel (k_nhwc.hip); the
+// next stem_i8_num_configs() the int8 NCHW4 stem kernel (k_stem_i8.hip).
 int nhwc_first() { return igemm_num_configs(); }
-bool is_nhwc_cfg(cfwd_algo_kind k, int cfg) { return k == CFWD_ALGO_IMPLICIT_GEMM && cfg >= nhwc_first(); }
+int stem_first() { return nhwc_first() + nhwc_num_configs(); }
+bool is_nhwc_cfg(cfwd_algo_kind k, int cfg) {
+    return k == CFWD_ALGO_IMPLICIT_GEMM && cfg >= nhwc_first() && cfg < stem_first();
+}
+bool is_stem_cfg(cfwd_algo_kind k, int cfg) { return k == CFWD_ALGO_IMPLICIT_GEMM && cfg >= stem_first(); }
 
 int num_configs(cfwd_algo_kind k) {
     switch (k) {
-        case CFWD_ALGO_IMPLICIT_GEMM: return igemm_num_configs() + nhwc_num_configs();
+        case CFWD_ALGO_IMPLICIT_GEMM: return igemm_num_configs() + nhwc_num_configs() + stem_i8_num_configs();
         case CFWD_ALGO_POINTWISE: return pointwise_num_configs();
         case CFWD_ALGO_DIRECT: return direct_num_configs();
         case CFWD_ALGO_WINOGRAD_F2X2_3X3: return winograd_num_configs(2);
@@ -201,6 +207,7 @@ bool supported(const Prob& p, cfwd_algo_kind k, int cfg, std::string* why) {
         return false;
     }
     if (is_nhwc_cfg(k, cfg)) return nhwc_supported(p, cfg - nhwc_first(), why);
+    if (is_stem_cfg(k, cfg)) return stem_i8_supported(p, cfg - stem_first(), why);
     switch (k) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_supported(p, cfg, why);
         case CFWD_ALGO_POINTWISE: return pointwise_supported(p, cfg, why);
@@ -239,6 +246,7 @@ std::vector<cfwd_algo> candidates(const Prob& p) {
 
 size_t filter_bytes(const Prob& p, const cfwd_algo& a) {
     if (is_nhwc_cfg(a.kind, a.config_id)) return nhwc_filter_bytes(p, a.config_id - nhwc_first());
+    if (is_stem_cfg(a.kind, a.config_id)) return stem_i8_filter_bytes(p, a.config_id - stem_first());
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_filter_bytes(p, a.config_id);
         case CFWD_ALGO_POINTWISE: return pointwise_filter_bytes(p, a.config_id);
@@ -252,7 +260,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Device scratch an algorithm needs besides its prepared filter.
 size_t scratch_bytes(const Prob& p, const cfwd_algo& a) {
-    if (is_nhwc_cfg(a.kind, a.config_id)) return 0;
+    if (is_nhwc_cfg(a.kind, a.config_id) || is_stem_cfg(a.kind, a.config_id)) return 0;
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_scratch_bytes(p, a.config_id);
         case CFWD_ALGO_WINOGRAD_F2X2_3X3: return winograd_scratch_bytes(p, 2, a.config_id);
@@ -423,6 +431,7 @@ bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u
 
 cfwd_status prepare(const Prob& p, const cfwd_algo& a, const void* w, void* wp, hipStream_t st) {
     if (is_nhwc_cfg(a.kind, a.config_id)) return nhwc_prepare(p, a.config_id - nhwc_first(), w, wp, st);
+    if (is_stem_cfg(a.kind, a.config_id)) return stem_i8_prepare(p, a.config_id - stem_first(), w, wp, st);
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: return igemm_prepare(p, a.config_id, w, wp, st);
         case CFWD_ALGO_POINTWISE: return pointwise_prepare(p, a.config_id, w, wp, st);
@@ -436,6 +445,11 @@ cfwd_status run(const Prob& p, const cfwd_algo& a, const void* x, const void* w,
                 const float* scale, void* y, void* scratch, const Epi& e, hipStream_t st) {
     cfwd_status s;
     if (is_nhwc_cfg(a.kind, a.config_id)) return nhwc_launch(p, a.config_id - nhwc_first(), x, wp, y, e, st);
+    if (is_stem_cfg(a.kind, a.config_id)) {
+        s = stem_i8_launch(p, a.config_id - stem_first(), x, wp, scale, y, e, st);
+        if (s != CFWD_OK) return s;
+        return zero_output_channel_padding(p, y, st);
+    }
     switch (a.kind) {
         case CFWD_ALGO_IMPLICIT_GEMM: s = igemm_launch(p, a.config_id, x, wp, scale, y, scratch, e, st); break;
         case CFWD_ALGO_POINTWISE: s = pointwise_launch(p, a.config_id, x, wp, scale, y, e, st); break;
