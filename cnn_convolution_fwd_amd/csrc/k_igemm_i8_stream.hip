@@ -70,6 +70,13 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
     constexpr int NTHR = WM * WN * 64;
     constexpr int NT = WN * FN * 32;
     constexpr int D = (RS == 9) ? 3 : 2;  // weight ring (taps ahead + 1)
+    // 3x3 layers: every load and store of a tile is issued unconditionally
+    // (buffer accesses whose padding ones fall past the range), so that the
+    // compiler's waits count them exactly and leave the next tile's input
+    // rows and the previous tile's stores in flight.  1x1 layers (one tap,
+    // nothing to overlap the rows with) keep the plain form, measured
+    // faster there.
+    constexpr bool PIPE = RS > 1;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -103,7 +110,10 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
     };
     auto stage_load = [&](int n, int th) {
         const int ih0 = th * a.TH * a.sh - a.ph;
+        // the image, also as a buffer: loads past its range return zeros
         const int8_t* xn = a.x + static_cast<long long>(n) * a.x_img;
+        const __amdgpu_buffer_rsrc_t xr =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(xn), 0, static_cast<int>(a.x_img), 0x00020000);
 #pragma unroll
         for (int m = 0; m < SMAXU; ++m) {
             const int u = tid + m * NTHR;
@@ -116,9 +126,20 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
             for (int b = 0; b < 4; ++b) {
                 const int cbi = 4 * j + b;  // input channel block
                 const bool ok = rowok && cbi < a.cb_in;
-                const int8_t* src = xn + (ok ? static_cast<long long>(cbi) * HW4 + (ih * a.W + iwb) * 4 : 0);
-                const uint4 v = *reinterpret_cast<const uint4*>(src);
-                stg[m][b] = ok ? v : make_uint4(0, 0, 0, 0);
+                if constexpr (PIPE) {
+                    // every load is issued, the padding ones past the
+                    // buffer's range (zeros from the hardware): with a select
+                    // or branch here the compiler makes the loads conditional
+                    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(
+                        xr,
+                        ok ? static_cast<unsigned>(cbi) * HW4 + static_cast<unsigned>((ih * a.W + iwb) * 4) : 0x80000000u,
+                        0, 0);
+                    stg[m][b] = make_uint4(v[0], v[1], v[2], v[3]);
+                } else {
+                    const int8_t* src = xn + (ok ? static_cast<long long>(cbi) * HW4 + (ih * a.W + iwb) * 4 : 0);
+                    const uint4 v = *reinterpret_cast<const uint4*>(src);
+                    stg[m][b] = ok ? v : make_uint4(0, 0, 0, 0);
+                }
             }
         }
     };
@@ -174,6 +195,17 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
     uint4 wr[D][FN][2];
     load_b(wr[0], kt, 0);
     if constexpr (RS == 9) load_b(wr[1], kt, 1);
+    if constexpr (PIPE) {
+        // On the loop's back edge the carried weights are followed by the
+        // tile's FM * FN stores; on entry the same number of stores follow
+        // them, all past a zero-sized buffer (dropped by the hardware), so
+        // that the waits at the first taps, which must hold on both paths,
+        // leave the real stores in flight.
+        const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.y, 0, 0, 0x00020000);
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int it = 0; it < FM * FN; ++it) __builtin_amdgcn_raw_buffer_store_b128(z, none, 0x80000000u, 0, 2);
+    }
     __syncthreads();
 
     int buf = 0;
@@ -182,7 +214,9 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
         const bool more = kn < tcount;
         int nn = n, thn = th, ktn = kt;
         if (more) tile_of(kn, nn, thn, ktn);
-        if (more) stage_load(nn, thn);
+        if constexpr (!PIPE) {
+            if (more) stage_load(nn, thn);
+        }
         const uint8_t* pb = lds + buf * patch_bytes;
 
         i32x16 acc[FM][FN];
@@ -198,12 +232,16 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
         }
 #pragma unroll
         for (int t = 0; t < RS; ++t) {
-            // weights: tap t + D - 1 of this tile, or the first taps of the next
+            // weights: tap t + D - 1 of this tile, or the first taps of the
+            // next (of this tile's block again after the last tile: a valid
+            // load that is never used).  No branch around the loads, so
+            // the waits for them count exactly the operations issued after
+            // them and leave the previous tile's stores in flight.
             {
                 const int tt = t + D - 1;
                 if (tt < RS)
                     load_b(wr[tt % D], kt, tt);
-                else if (more)
+                else if (PIPE || more)
                     load_b(wr[tt % D], ktn, tt - RS);
             }
             if (t + 1 < RS) {
@@ -223,6 +261,21 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
 #pragma unroll
                     for (int nf = 0; nf < FN; ++nf)
                         ig::Mma32<int8_t>::piece(acc[f][nf], ra[t & 1][f][i], wr[t % D][nf][i], i);
+            if constexpr (PIPE) {
+                // The next tile's input rows (on the last tile its own rows
+                // again, never written to LDS), issued once the first two
+                // taps have waited for the weights carried over from the
+                // previous tile: issued before those waits, these loads
+                // (which the compiler places in branches) would be drained
+                // by them, together with the previous tile's stores.  The
+                // scheduler barriers keep them here: left alone, the
+                // compiler moves them to the end of the taps.
+                if (t == 1) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    stage_load(nn, thn);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
 
         // ---- epilogue: requantise into ebuf as [channel block][tile pixel][4 channels]
@@ -280,14 +333,35 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
             const int rows = min(a.TH, a.OH - oh0);
             const int npx = rows * a.OW;
             const int nkb = min(NT, a.K - kt0) / 4;
-            int8_t* yb = a.y + static_cast<long long>(n) * a.y_img + static_cast<long long>(oh0) * a.OW * 4;
             const long long plane = static_cast<long long>(a.OH) * a.OW * 4;
             const int pieces = npx / 4;  // 16-byte pieces (4 pixels) per channel block; OW % 4 == 0
-            for (int q = tid; q < nkb * pieces; q += NTHR) {
-                const int kb = q / pieces, jj = q - (q / pieces) * pieces;
-                const uint4 v = *reinterpret_cast<const uint4*>(ebuf + kb * pitch + jj * 16);
-                const u32x4_t w = {v.x, v.y, v.z, v.w};
-                __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(yb + (kt0 / 4 + kb) * plane + jj * 16));
+            // At most FM * FN pieces per thread (NT / 4 channel blocks x the
+            // tile's pixels / 4 pieces over NTHR threads), all issued, the
+            // absent ones past the buffer's range (dropped by the hardware),
+            // so that later waits count them exactly.  Streaming stores.
+            if constexpr (PIPE) {
+                const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+                    a.y + static_cast<long long>(n) * a.y_img, 0, static_cast<int>(a.y_img), 0x00020000);
+                const unsigned ybase = static_cast<unsigned>(oh0 * a.OW * 4);
+#pragma unroll
+                for (int it = 0; it < FM * FN; ++it) {
+                    const int q0 = tid + it * NTHR;
+                    const bool okq = q0 < nkb * pieces;
+                    const int q = okq ? q0 : 0;
+                    const int kb = q / pieces, jj = q - (q / pieces) * pieces;
+                    const uint4 v = *reinterpret_cast<const uint4*>(ebuf + kb * pitch + jj * 16);
+                    const u32x4_t w = {v.x, v.y, v.z, v.w};
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        w, yr, okq ? ybase + static_cast<unsigned>((kt0 / 4 + kb) * plane + jj * 16) : 0x80000000u, 0, 2);
+                }
+            } else {
+                int8_t* yb = a.y + static_cast<long long>(n) * a.y_img + static_cast<long long>(oh0) * a.OW * 4;
+                for (int q = tid; q < nkb * pieces; q += NTHR) {
+                    const int kb = q / pieces, jj = q - (q / pieces) * pieces;
+                    const uint4 v = *reinterpret_cast<const uint4*>(ebuf + kb * pitch + jj * 16);
+                    const u32x4_t w = {v.x, v.y, v.z, v.w};
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(yb + (kt0 / 4 + kb) * plane + jj * 16));
+                }
             }
         }
         if (more) stage_store(lds + (buf ^ 1) * patch_bytes);
