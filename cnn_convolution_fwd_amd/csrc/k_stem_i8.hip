@@ -7,16 +7,16 @@
 // 4-byte word, so the S taps of one filter row for one output pixel are S
 // consecutive words of one input row.  K is laid out as 8 filter rows x 8
 // taps x 4 channels (256 bytes, zero past R, S, C): each 16-byte matrix-core
-// operand piece is then 4 consecutive input words, loaded as is -- no gather,
-// no LDS staging, no per-element selects except at the image's left and
-// right edges (MegEngine inference article, section "NCHWX": the blocked
-// layout that makes the channel vector one aligned word).
+// operand piece is then 4 consecutive input words, loaded with one 16-byte
+// load -- no gather, no LDS staging; only fragments at the image's edges
+// shift or zero the words (MegEngine inference article, section "NCHWX": the
+// blocked layout that makes the channel vector one aligned word).
 //
 // Matrix product per 16-pixel fragment (16 consecutive output columns of one
 // output row) and 64 output channels: v_mfma_i32_16x16x64_i8 with the
 // weights as A (rows = channels) and the pixels as B, so each lane ends with
 // 4 consecutive channels of one pixel: one requantised NCHW4 word per store,
-// 16 lanes = 64 contiguous bytes.  Persistent waves take 4 fragments at a
+// 16 lanes = 64 contiguous bytes.  Persistent waves take FPW fragments at a
 // time; the weights of a 64-channel group (4 K steps x 4 tiles x 16 bytes)
 // stay in registers, and the next fragments' pixels load during the
 // current ones' products and stores.
@@ -94,9 +94,9 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
     // words are consumed, so the loads stay in flight: lanes whose window
     // leaves the row shift the words by iw0 - b (-3 .. 3, the same for
     // every filter row) and zero what lies outside; rows outside the image
-    // are zeroed (rlo: the fragment's first input row).  Filter rows and taps past R, S
-    // and channels past C have zero weights, so what is loaded there does
-    // not matter.
+    // are zeroed (rlo: the fragment's first input row).  Filter rows and
+    // taps past R, S and channels past C have zero weights, so what is
+    // loaded there does not matter.
     auto load_x = [&](uint4 (&b)[4][FPW], int (&shf)[FPW], int (&rlo)[FPW], const int (&n)[FPW], const int (&oh)[FPW],
                       const int (&ow)[FPW]) __attribute__((always_inline)) {
 #pragma unroll
