@@ -92,8 +92,8 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
     // Every load is issued from an address clamped into the image (W >= 4):
     // the 4 words at b = clamp(iw0, 0, W - 4).  The fix-up waits until the
     // words are consumed, so the loads stay in flight: lanes whose window
-    // leaves the row shift the words by iw0 - b (-3 .. 3, the same for
-    // every filter row) and zero what lies outside; rows outside the image
+    // leaves the row shift the words by iw0 - b (the same for every filter
+    // row) and zero what lies outside; rows outside the image
     // are zeroed (rlo: the fragment's first input row).  Filter rows and
     // taps past R, S and channels past C have zero weights, so what is
     // loaded there does not matter.
@@ -117,7 +117,10 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
         }
     };
     // word e of the result is word e + sh of v, zero outside 0 .. 3; a
-    // two-stage barrel shift of selects, zero when the row is outside
+    // two-stage barrel shift of selects for |sh| <= 3, all zero when the
+    // row is outside the image or |sh| >= 4 (the whole window lies past one
+    // end of the row: wide padding, or a late tap of a stride-1 filter at
+    // the last output columns)
     auto fix = [](uint4 v, int sh, bool in) __attribute__((always_inline)) -> i32x4 {
         uint32_t x0 = v.x, x1 = v.y, x2 = v.z, x3 = v.w;
         const bool up = sh > 0;
@@ -130,7 +133,7 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
             const uint32_t y0 = up ? x1 : 0u, y1 = up ? x2 : x0, y2 = up ? x3 : x1, y3 = up ? 0u : x2;
             x0 = y0; x1 = y1; x2 = y2; x3 = y3;
         }
-        const uint32_t k = in ? 0xffffffffu : 0u;
+        const uint32_t k = (in && m < 4) ? 0xffffffffu : 0u;
         return i32x4{static_cast<int>(x0 & k), static_cast<int>(x1 & k), static_cast<int>(x2 & k),
                      static_cast<int>(x3 & k)};
     };

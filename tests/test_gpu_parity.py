@@ -55,6 +55,15 @@ SMALL = [
     ("stem3x3s2_32", 2, 3, 32, 32, 32, 3, 3, 2, 1, 1, 1),
     ("stem7x7s2_32", 2, 3, 32, 32, 64, 7, 7, 2, 3, 1, 1),
     ("c4_k40_s1", 1, 4, 16, 24, 40, 3, 3, 1, 1, 1, 1),
+    # int8 NCHW4 stem kernel: two 64-channel groups (the second half full),
+    # five filter rows (three K steps), a ragged 16-pixel fragment; and the
+    # narrowest rows it takes (W = 4: every load window clamped at both ends)
+    ("stem_k96_5x5", 1, 3, 9, 21, 96, 5, 5, 1, 2, 1, 1),
+    ("stem_w4", 2, 4, 6, 4, 16, 3, 3, 1, 1, 1, 1),
+    # operand windows wholly past a row's end or start (taps 4..7 at the
+    # last columns of a stride-1 7x7; an 8x8 filter with padding 7)
+    ("stem7x7s1_p3", 1, 3, 12, 13, 16, 7, 7, 1, 3, 1, 1),
+    ("stem8x8_p7", 1, 4, 10, 9, 8, 8, 8, 1, 7, 1, 1),
     # fused Winograd F(2x2) tile blocks: 8 x 8 tiles with pad 0 and an output
     # width that is not a multiple of 8; two 32-tile column blocks with a
     # ragged channel chunk and output-channel block
