@@ -36,6 +36,8 @@ struct Args {
     const float* scale;
     int8_t* y;
     int H, W, K, OH, OW, sh, sw, ph, pw, R;
+    int W2, lastrow;     // 2 W; (H - 1) W: word offsets of a row step and of the last row
+    unsigned plane4;     // bytes per output channel block (OH OW 4)
     int nsteps;          // ceil(R / 2)
     int ngroups;         // ceil(K / 64)
     int fw;              // fragments per output row: ceil(OW / 16)
@@ -107,11 +109,15 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
             rlo[f] = oh[f] * a.sh - a.ph;  // the fragment's first input row (uniform)
             // the fragment's image (n is uniform): 32-bit byte offsets from it
             const char* img = reinterpret_cast<const char*>(a.x + static_cast<long long>(n[f]) * a.H * a.W);
+            // word offset of this lane's first row; K step t is 2 t rows
+            // further, clamped into the image on the product (W > 0), so one
+            // multiply per fragment instead of one per load
+            const int row0 = (rlo[f] + (g >> 1)) * a.W;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                const int ihc = min(max(rlo[f] + 2 * t + (g >> 1), 0), a.H - 1);
+                const int rw = min(max(row0 + t * a.W2, 0), a.lastrow);
                 uint32_t v[4];
-                __builtin_memcpy(v, img + static_cast<unsigned>((ihc * a.W + bw) * 4), 16);
+                __builtin_memcpy(v, img + static_cast<unsigned>((rw + bw) * 4), 16);
                 b[t][f] = make_uint4(v[0], v[1], v[2], v[3]);
             }
         }
@@ -142,6 +148,10 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
     uint4 w[4][4];
     float sc[4][4];
     int bi[4][4];
+    // byte offset of the lane's channel block 16 kg + 4 mt + g in an image of y
+    unsigned cofs[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) cofs[mt] = static_cast<unsigned>(kg * (KG / 4) + 4 * mt + g) * a.plane4;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -211,6 +221,7 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
         // 64 kg + 16 mt + 4g .. + 3: one NCHW4 word
 #pragma unroll
         for (int f = 0; f < FPW; ++f) {
+            const unsigned pofs = static_cast<unsigned>(soh[f] * a.OW + sow[f]) * 4u;  // the lane's pixel in a plane
             // the fragment's image of y as a buffer (n is uniform across the
             // wave): offsets at or past y_img are dropped
             const __amdgpu_buffer_rsrc_t ybuf = __builtin_amdgcn_make_buffer_rsrc(
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(NTHR) void stem_kernel(Args a) {
             for (int mt = 0; mt < 4; ++mt) {
                 const int k0 = kg * KG + 16 * mt + 4 * g;
                 const bool ok = slive[f] && k0 < a.K;
-                const unsigned off = static_cast<unsigned>(((k0 >> 2) * a.OH + soh[f]) * a.OW + sow[f]) * 4u;
+                const unsigned off = cofs[mt] + pofs;
                 uint32_t word = 0;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
@@ -315,6 +326,8 @@ cfwd_status stem_i8_launch(const Prob& p, int cfg, const void* x, const void* wp
     a.scale = scale;
     a.y = static_cast<int8_t*>(y);
     a.H = p.h; a.W = p.w; a.K = p.k; a.OH = p.oh; a.OW = p.ow;
+    a.W2 = 2 * p.w; a.lastrow = (p.h - 1) * p.w;
+    a.plane4 = static_cast<unsigned>(p.oh) * static_cast<unsigned>(p.ow) * 4u;
     a.sh = p.sh; a.sw = p.sw; a.ph = p.ph; a.pw = p.pw; a.R = p.r;
     a.nsteps = (p.r + 1) / 2;
     a.ngroups = (p.k + st8::KG - 1) / st8::KG;
