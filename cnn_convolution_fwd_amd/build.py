@@ -39,13 +39,16 @@ COMMON = [
 
 
 # Per-source extra flags.  The stem kernels (gather form and the int8 NCHW4
-# stem) are bound by vector ALU issue; keeping MFMA results in ordinary VGPRs
-# instead of accumulation registers removes the register moves around their
-# epilogues (about a tenth of their vector instructions) without raising
-# register use.
+# stem) and the persistent int8 kernel are bound by vector ALU issue; keeping
+# MFMA results in ordinary VGPRs instead of accumulation registers removes the
+# register moves around their epilogues (about a tenth of their vector
+# instructions) without raising register use (in the persistent kernel it
+# lowers it: two of its 3x3 variants fall under 256 registers, and the
+# epilogue variants of its widest tile spill less).
 EXTRA = {
     "k_lowc.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "k_stem_i8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "k_igemm_i8_stream.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
