@@ -260,7 +260,7 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
                 for (int f = 0; f < FM; ++f)
 #pragma unroll
                     for (int nf = 0; nf < FN; ++nf)
-                        ig::Mma32<int8_t>::piece(acc[f][nf], ra[t & 1][f][i], wr[t % D][nf][i], i);
+                        ig::Mma32<int8_t>::piece(acc[f][nf], wr[t % D][nf][i], ra[t & 1][f][i], i);
             if constexpr (PIPE) {
                 // The next tile's input rows (on the last tile its own rows
                 // again, never written to LDS), issued once the first two
@@ -278,50 +278,53 @@ __global__ __launch_bounds__(WM* WN * 64) void stream_kernel(Args a) {
             }
         }
 
-        // ---- epilogue: requantise into ebuf as [channel block][tile pixel][4 channels]
+        // ---- epilogue: requantise into ebuf as [channel block][tile pixel][4 channels].
+        // The weights are the products' A operand, so D is [channel][pixel]:
+        // a lane holds pixel (wm FM + f) 32 + lrow and, for each j, the 4
+        // consecutive channels (wn FN + nf) 32 + 8 j + 4 h + v of one NCHW4
+        // block -- one requantised dword, no transpose across lanes.
         const int oh0 = th * a.TH;
         const int kt0 = kt * NT;
 #pragma unroll
         for (int nf = 0; nf < FN; ++nf) {
-            const int kk = (wn * FN + nf) * 32 + lrow;
-            const int kc = kt0 + kk;
-            const bool kval = kc < a.K;
-            const float sc0 = a.scale[kval ? kc : 0];
-            const float sc = kval ? sc0 : 0.0f;
-            uint8_t* cbrow = ebuf + (kk >> 2) * pitch;  // this lane's channel block
-            const int ke = EPI ? min(kc, a.K - 1) : 0;
-            const int ebias = (EPI && a.e.bias) ? static_cast<const int32_t*>(a.e.bias)[ke] : 0;
-            const float elo = (EPI && a.e.relu) ? 0.0f : -127.0f;
-            const long long kofs = EPI ? static_cast<long long>(n) * a.y_img + static_cast<long long>(ke >> 2) * a.OH * a.OW * 4 +
-                                             (ke & 3) + static_cast<long long>(oh0) * a.OW * 4
-                                       : 0;
 #pragma unroll
-            for (int f = 0; f < FM; ++f) {
+            for (int j = 0; j < 4; ++j) {
+                const int kb = (wn * FN + nf) * 32 + 8 * j + 4 * h;  // the block's first channel in the tile
+                const int kc0 = kt0 + kb;
+                const bool kval = kc0 < a.K;  // K % 4 == 0: the whole block is real or padding
+                float sc[4];
+                int eb[4];
 #pragma unroll
-                for (int grp = 0; grp < 4; ++grp) {
-                    const int p0 = (wm * FM + f) * 32 + 8 * grp + 4 * h;
+                for (int v = 0; v < 4; ++v) {
+                    const float s0 = a.scale[kval ? kc0 + v : 0];
+                    sc[v] = kval ? s0 : 0.0f;
+                    eb[v] = (EPI && a.e.bias && kval) ? static_cast<const int32_t*>(a.e.bias)[kc0 + v] : 0;
+                }
+                const float elo = (EPI && a.e.relu) ? 0.0f : -127.0f;
+                uint8_t* cbrow = ebuf + (kb >> 2) * pitch;  // this block's row of ebuf
+#pragma unroll
+                for (int f = 0; f < FM; ++f) {
+                    const int p = (wm * FM + f) * 32 + lrow;
                     float eres[4] = {0.0f, 0.0f, 0.0f, 0.0f};
                     if constexpr (EPI) {
-                        if (a.e.res) {
+                        if (a.e.res && kval && p < tile_pix && oh0 * a.OW + p < a.OH * a.OW) {
+                            const uint32_t rw = *reinterpret_cast<const uint32_t*>(
+                                static_cast<const int8_t*>(a.e.res) + static_cast<long long>(n) * a.y_img +
+                                (static_cast<long long>(kc0 >> 2) * a.OH * a.OW + static_cast<long long>(oh0) * a.OW + p) * 4);
 #pragma unroll
                             for (int v = 0; v < 4; ++v)
-                                if (p0 + v < tile_pix && oh0 * a.OW + p0 + v < a.OH * a.OW)
-                                    eres[v] = static_cast<float>(
-                                        static_cast<const int8_t*>(a.e.res)[kofs + static_cast<long long>(p0 + v) * 4]);
+                                eres[v] = static_cast<float>(static_cast<int8_t>((rw >> (8 * v)) & 0xffu));
                         }
                     }
                     uint32_t q[4];
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         if constexpr (EPI)
-                            q[v] = requant_i8_fused(acc[f][nf][grp * 4 + v], ebias, sc, eres[v], elo);
+                            q[v] = requant_i8_fused(acc[f][nf][j * 4 + v], eb[v], sc[v], eres[v], elo);
                         else
-                            q[v] = requant_i8_bits(acc[f][nf][grp * 4 + v], sc);
+                            q[v] = requant_i8_bits(acc[f][nf][j * 4 + v], sc[v]);
                     }
-                    // lanes 4m .. 4m + 3 hold the 4 channels of one block:
-                    // transposed, each writes one pixel's dword
-                    const uint32_t dq = quad_transpose_bytes(pack_low_bytes(q[0], q[1], q[2], q[3]), lane);
-                    if (p0 < tile_pix) *reinterpret_cast<uint32_t*>(cbrow + (p0 + (lane & 3)) * 4) = dq;
+                    if (p < tile_pix) *reinterpret_cast<uint32_t*>(cbrow + p * 4) = pack_low_bytes(q[0], q[1], q[2], q[3]);
                 }
             }
         }
